@@ -1,0 +1,125 @@
+"""CPU oracle for the 2:4 sparse + rank-r linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg may import this
+package. It wraps `splr_oracle.c` (plain C, float64 sums in index order, OpenMP over independent
+outputs) through ctypes. It shares no code with the GPU library and never loads it.
+
+Conventions: "bf16" arrays are numpy uint16 bit patterns, "fp32" arrays numpy float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "splr_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_DT = {"fp32": 0, "bf16": 1}
+_NP = {"fp32": np.float32, "bf16": np.uint16}
+_lib = None
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fused multiply-add, so every sum is the written one)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
+                               "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.splr_ref_prune24_pack.argtypes = [P, I64, I64, ctypes.c_int, P, P]
+        lib.splr_ref_linear.argtypes = [P, I64, I64, P, P, I64, P, P, I64, ctypes.c_int, P, I64, P]
+        lib.splr_ref_dense_reconstruct.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P]
+        for f in (lib.splr_ref_prune24_pack, lib.splr_ref_linear, lib.splr_ref_dense_reconstruct):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(a: np.ndarray, dtype: str, ndim: int, name: str) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != _NP[dtype] or a.ndim != ndim:
+        raise TypeError(f"{name}: expected {ndim}-D {_NP[dtype].__name__} for {dtype}, got {a.dtype} {a.shape}")
+    return a
+
+
+def prune24_pack(R: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """2:4 projection of R [n_out x n_in] -> (values [n_out x n_in/2], meta uint32 [n_out x n_in/32])."""
+    R = _check(R, dtype, 2, "R")
+    n_out, n_in = R.shape
+    values = np.empty((n_out, n_in // 2), dtype=_NP[dtype])
+    meta = np.empty((n_out, n_in // 32), dtype=np.uint32)
+    rc = _load().splr_ref_prune24_pack(_ptr(R), n_out, n_in, _DT[dtype], _ptr(values), _ptr(meta))
+    if rc:
+        raise ValueError(f"splr_ref_prune24_pack failed ({rc}) for shape {R.shape}")
+    return values, meta
+
+
+def linear(X: np.ndarray, values: np.ndarray, meta: np.ndarray, U: Optional[np.ndarray],
+           V: Optional[np.ndarray], dtype: str, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """float64 Y = X S^T + (X V^T) U^T for all token rows, or only for `rows` (in that order)."""
+    X = _check(X, dtype, 2, "X")
+    values = _check(values, dtype, 2, "values")
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    M, n_in = X.shape
+    n_out = values.shape[0]
+    if values.shape[1] * 2 != n_in or meta.shape != (n_out, n_in // 32):
+        raise ValueError("values/meta do not match X")
+    r = 0 if U is None else U.shape[1]
+    if r:
+        U = _check(U, dtype, 2, "U")
+        V = _check(V, dtype, 2, "V")
+        if U.shape != (n_out, r) or V.shape != (r, n_in):
+            raise ValueError("U/V shapes")
+    else:
+        U = V = None
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n_rows = M if rows is None else rows.shape[0]
+    Y = np.empty((n_rows, n_out), dtype=np.float64)
+    rc = _load().splr_ref_linear(_ptr(X), M, n_in, _ptr(values), _ptr(meta), n_out, _ptr(U), _ptr(V), r,
+                                 _DT[dtype], _ptr(rows), n_rows, _ptr(Y))
+    if rc:
+        raise ValueError(f"splr_ref_linear failed ({rc})")
+    return Y
+
+
+def dense_reconstruct(values: np.ndarray, meta: np.ndarray, U: Optional[np.ndarray],
+                      V: Optional[np.ndarray], dtype: str) -> np.ndarray:
+    """float64 W_hat = S + U V, S scattered from (values, meta)."""
+    values = _check(values, dtype, 2, "values")
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    n_out, n_in = values.shape[0], values.shape[1] * 2
+    if meta.shape != (n_out, n_in // 32):
+        raise ValueError("meta shape")
+    r = 0 if U is None else U.shape[1]
+    if r:
+        U = _check(U, dtype, 2, "U")
+        V = _check(V, dtype, 2, "V")
+    else:
+        U = V = None
+    W = np.empty((n_out, n_in), dtype=np.float64)
+    rc = _load().splr_ref_dense_reconstruct(_ptr(values), _ptr(meta), _ptr(U), _ptr(V), n_out, n_in, r,
+                                            _DT[dtype], _ptr(W))
+    if rc:
+        raise ValueError(f"splr_ref_dense_reconstruct failed ({rc})")
+    return W

@@ -1,0 +1,211 @@
+/*
+ * CPU oracle for the 2:4 sparse + rank-r linear layer.  TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, obviously-correct definition that the GPU library is checked
+ * against.  Only the tests, the package's smoke check and the benchmark's CPU-baseline leg load
+ * it; the GPU library never links, includes or calls it, and it includes nothing from the GPU
+ * library.  Every sum is a sequential float64 loop in index order; OpenMP only splits independent
+ * outputs between threads, so the result does not depend on the thread count.
+ *
+ * Layouts (row-major, contiguous):
+ *   R, W_hat : [n_out][n_in]
+ *   values   : [n_out][n_in/2]   the two kept entries of every group of 4, ascending index
+ *   meta     : [n_out][n_in/32]  uint32; group g of a row has the nibble (a | b << 2) at bits
+ *                                4*(g % 8) of word g / 8, a < b being the kept positions (0..3)
+ *   X        : [M][n_in]   U : [n_out][r]   V : [r][n_in]   Y : [rows][n_out] (float64)
+ * dtype 0 = float32 storage, 1 = bfloat16 storage (uint16 bit patterns).
+ *
+ * Functions and the passages they follow:
+ *   splr_ref_prune24_pack     -- the sparse subproblem with identity Hessian is solved exactly by
+ *                                hard thresholding (HASSLE-free page, §4.1.1); under the 2:4
+ *                                constraint, at most two of every four consecutive weights may be
+ *                                nonzero (3BASiL article, "A three-block ADMM replaces alternating
+ *                                minimization").  Hard thresholding per group = keep the two
+ *                                largest magnitudes unchanged, zero the rest.
+ *   splr_ref_linear           -- the compressed forward pass sums the sparse product and the
+ *                                low-rank product, computed side by side (LoSparse page, §3 and
+ *                                §3.2), here as Y = X S^T + (X V^T) U^T.
+ *   splr_ref_dense_reconstruct-- the weight is approximated by the sum S + U V (LoSparse §3).
+ *
+ * Readings where the pages are silent (ties, special values, layout) are the ones listed at the
+ * top of each function.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define SPLR_REF_FP32 0
+#define SPLR_REF_BF16 1
+
+#define SPLR_REF_OK 0
+#define SPLR_REF_EINVAL 1
+#define SPLR_REF_ENOMEM 2
+
+static double load_f64(const void *base, int dtype, size_t i) {
+  if (dtype == SPLR_REF_BF16) {
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+  }
+  return (double)((const float *)base)[i];
+}
+
+/* Unsigned magnitude key: the IEEE bit pattern with the sign cleared.  For finite values it orders
+   by |x| exactly (subnormals included, +0 and -0 equal); infinities sort above every finite value
+   and NaNs above infinities (by payload). */
+static uint32_t magnitude_key(const void *base, int dtype, size_t i) {
+  if (dtype == SPLR_REF_BF16) return (uint32_t)(((const uint16_t *)base)[i] & 0x7FFFu);
+  return ((const uint32_t *)base)[i] & 0x7FFFFFFFu;
+}
+
+static void copy_elem(void *dst, size_t di, const void *src, size_t si, int dtype) {
+  if (dtype == SPLR_REF_BF16)
+    ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
+  else
+    ((uint32_t *)dst)[di] = ((const uint32_t *)src)[si];
+}
+
+/* Position i of a group outranks position j when its magnitude is larger, or equal with i < j. */
+static int outranks(const uint32_t key[4], int i, int j) {
+  return key[i] > key[j] || (key[i] == key[j] && i < j);
+}
+
+/*
+ * 2:4 projection and pack.  For every row and every group of four consecutive input columns:
+ * keep the entry that outranks the other three and the entry that outranks the remaining two,
+ * unchanged (bit copies); store them in ascending position order and record their positions.
+ * Readings: ties go to the lower position; groups with fewer than two nonzeros still store two
+ * slots (zeros included), so the output layout is fixed.
+ */
+int splr_ref_prune24_pack(const void *R, int64_t n_out, int64_t n_in, int dtype, void *values,
+                          uint32_t *meta) {
+  if (!R || !values || !meta) return SPLR_REF_EINVAL;
+  if (n_out < 0 || n_in < 0 || n_in % 32 != 0) return SPLR_REF_EINVAL;
+  if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
+  const int64_t groups = n_in / 4, words = n_in / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < n_out; ++n) {
+    for (int64_t w = 0; w < words; ++w) meta[n * words + w] = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+      const size_t base = (size_t)n * (size_t)n_in + 4 * (size_t)g;
+      uint32_t key[4];
+      for (int i = 0; i < 4; ++i) key[i] = magnitude_key(R, dtype, base + i);
+      int first = 0;
+      for (int i = 1; i < 4; ++i)
+        if (outranks(key, i, first)) first = i;
+      int second = -1;
+      for (int i = 0; i < 4; ++i) {
+        if (i == first) continue;
+        if (second < 0 || outranks(key, i, second)) second = i;
+      }
+      const int a = first < second ? first : second;
+      const int b = first < second ? second : first;
+      const size_t vi = (size_t)n * (size_t)(n_in / 2) + 2 * (size_t)g;
+      copy_elem(values, vi, R, base + a, dtype);
+      copy_elem(values, vi + 1, R, base + b, dtype);
+      meta[n * words + g / 8] |= (uint32_t)(a | (b << 2)) << (4 * (g % 8));
+    }
+  }
+  return SPLR_REF_OK;
+}
+
+static void decode_nibble(const uint32_t *meta_row, int64_t g, int *a, int *b) {
+  const uint32_t nib = (meta_row[g / 8] >> (4 * (g % 8))) & 0xFu;
+  *a = (int)(nib & 3u);
+  *b = (int)(nib >> 2);
+}
+
+/*
+ * Y[i][n] = sum_g ( X[m][4g+a] * values[n][2g] + X[m][4g+b] * values[n][2g+1] )
+ *         + sum_j T[i][j] * U[n][j],      T[i][j] = sum_k X[m][k] * V[j][k],
+ * for m = rows[i] (every m in 0..M-1 in order when rows is NULL), all in float64.
+ * U and V may be NULL when r == 0.
+ */
+int splr_ref_linear(const void *X, int64_t M, int64_t n_in, const void *values,
+                    const uint32_t *meta, int64_t n_out, const void *U, const void *V, int64_t r,
+                    int dtype, const int64_t *rows, int64_t n_rows, double *Y) {
+  if (!X || !values || !meta || !Y) return SPLR_REF_EINVAL;
+  if (r > 0 && (!U || !V)) return SPLR_REF_EINVAL;
+  if (M < 0 || n_in < 0 || n_in % 32 != 0 || n_out < 0 || r < 0) return SPLR_REF_EINVAL;
+  if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
+  if (!rows) n_rows = M;
+  for (int64_t i = 0; i < (rows ? n_rows : 0); ++i)
+    if (rows[i] < 0 || rows[i] >= M) return SPLR_REF_EINVAL;
+  const int64_t groups = n_in / 4, words = n_in / 32;
+
+  double *xrows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * (size_t)(n_in > 0 ? n_in : 1));
+  double *T = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * (size_t)(r > 0 ? r : 1));
+  if (!xrows || !T) {
+    free(xrows);
+    free(T);
+    return SPLR_REF_ENOMEM;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t m = rows ? rows[i] : i;
+    for (int64_t k = 0; k < n_in; ++k) xrows[i * n_in + k] = load_f64(X, dtype, (size_t)m * (size_t)n_in + k);
+  }
+  /* first low-rank stage: T = X V^T */
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t i = 0; i < n_rows; ++i)
+    for (int64_t j = 0; j < r; ++j) {
+      double t = 0.0;
+      for (int64_t k = 0; k < n_in; ++k) t += xrows[i * n_in + k] * load_f64(V, dtype, (size_t)j * (size_t)n_in + k);
+      T[i * r + j] = t;
+    }
+  /* sparse product plus second low-rank stage */
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t i = 0; i < n_rows; ++i)
+    for (int64_t n = 0; n < n_out; ++n) {
+      const double *x = xrows + i * n_in;
+      const uint32_t *mrow = meta + n * words;
+      const size_t vrow = (size_t)n * (size_t)(n_in / 2);
+      double sparse = 0.0;
+      for (int64_t g = 0; g < groups; ++g) {
+        int a, b;
+        decode_nibble(mrow, g, &a, &b);
+        sparse += x[4 * g + a] * load_f64(values, dtype, vrow + 2 * (size_t)g);
+        sparse += x[4 * g + b] * load_f64(values, dtype, vrow + 2 * (size_t)g + 1);
+      }
+      double lowrank = 0.0;
+      for (int64_t j = 0; j < r; ++j) lowrank += T[i * r + j] * load_f64(U, dtype, (size_t)n * (size_t)r + j);
+      Y[i * n_out + n] = sparse + lowrank;
+    }
+  free(xrows);
+  free(T);
+  return SPLR_REF_OK;
+}
+
+/*
+ * W_hat[n][k] = S[n][k] + sum_j U[n][j] * V[j][k] in float64, where S is the dense matrix
+ * scattered from (values, meta): the two stored entries at their positions, +0 elsewhere.
+ */
+int splr_ref_dense_reconstruct(const void *values, const uint32_t *meta, const void *U,
+                               const void *V, int64_t n_out, int64_t n_in, int64_t r, int dtype,
+                               double *W_hat) {
+  if (!values || !meta || !W_hat) return SPLR_REF_EINVAL;
+  if (r > 0 && (!U || !V)) return SPLR_REF_EINVAL;
+  if (n_out < 0 || n_in < 0 || n_in % 32 != 0 || r < 0) return SPLR_REF_EINVAL;
+  if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
+  const int64_t groups = n_in / 4, words = n_in / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < n_out; ++n) {
+    double *w = W_hat + n * n_in;
+    for (int64_t k = 0; k < n_in; ++k) w[k] = 0.0;
+    for (int64_t g = 0; g < groups; ++g) {
+      int a, b;
+      decode_nibble(meta + n * words, g, &a, &b);
+      const size_t vi = (size_t)n * (size_t)(n_in / 2) + 2 * (size_t)g;
+      w[4 * g + a] = load_f64(values, dtype, vi);
+      w[4 * g + b] = load_f64(values, dtype, vi + 1);
+    }
+    for (int64_t k = 0; k < n_in; ++k) {
+      double lowrank = 0.0;
+      for (int64_t j = 0; j < r; ++j)
+        lowrank += load_f64(U, dtype, (size_t)n * (size_t)r + j) * load_f64(V, dtype, (size_t)j * (size_t)n_in + k);
+      w[k] += lowrank;
+    }
+  }
+  return SPLR_REF_OK;
+}

@@ -1,0 +1,134 @@
+"""Pins of the oracle's layer product and dense reconstruction.
+
+The compressed forward pass is the sum of the sparse product and the low-rank product (LoSparse
+page, §3 and §3.2); the weight it stands for is S + U V (LoSparse §3). In this orientation:
+Y = X S^T + (X V^T) U^T = X (S + U V)^T. Pins:
+  * a library routine: numpy float64 X @ (S_dense + U @ V).T with S built densely by the test;
+  * special cases: U = 0, S = 0, r = 0, X = I;
+  * integer-exact inputs, where every sum is exact and the result must match integer arithmetic;
+  * linearity in X, and row sampling returning exactly the full result's rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_rank_linear_prune24_amd import inputs
+
+PATTERNS = [(a, b) for a in range(4) for b in range(a + 1, 4)]
+NP = {"fp32": np.float32, "bf16": np.uint16}
+
+
+def random_24_dense(n_out, n_in, dtype, seed, int_range=None):
+    """A dense matrix with exactly the 2:4 structure, built directly (not through the projection)."""
+    g = np.random.default_rng(seed)
+    pat = g.integers(0, 6, size=(n_out, n_in // 4))
+    if int_range is None:
+        vals = g.standard_normal((n_out, n_in // 4, 2)) * 0.02
+    else:
+        vals = g.integers(int_range[0], int_range[1] + 1, size=(n_out, n_in // 4, 2)).astype(np.float64)
+    dense = np.zeros((n_out, n_in // 4, 4))
+    a = np.array([p[0] for p in PATTERNS])[pat]
+    b = np.array([p[1] for p in PATTERNS])[pat]
+    np.put_along_axis(dense, a[..., None], vals[..., :1], axis=2)
+    np.put_along_axis(dense, b[..., None], vals[..., 1:], axis=2)
+    return inputs.from_f64(dense.reshape(n_out, n_in), dtype)
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("M,n_in,n_out,r", [(37, 256, 96, 16), (5, 64, 33, 32), (64, 512, 128, 0)])
+def test_linear_matches_dense_matmul(dtype, M, n_in, n_out, r):
+    L = inputs.random_case(M, n_in, n_out, r, dtype, seed=5, n_outliers=2)
+    S = random_24_dense(n_out, n_in, dtype, seed=9)
+    values, meta = oracle.prune24_pack(S, dtype)           # lossless on a 2:4 matrix
+    S_back = inputs.from_f64(oracle.dense_reconstruct(values, meta, None, None, dtype), dtype)
+    assert np.array_equal(S_back, S)
+    U, V = (L.U, L.V) if r else (None, None)
+    Y = oracle.linear(L.X, values, meta, U, V, dtype)
+    Xf, Sf = inputs.to_f64(L.X, dtype), inputs.to_f64(S, dtype)
+    Wf = Sf + (inputs.to_f64(L.U, dtype) @ inputs.to_f64(L.V, dtype) if r else 0.0)
+    Y_np = Xf @ Wf.T
+    assert np.max(np.abs(Y - Y_np)) <= 1e-12 * rms(Y_np)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_special_cases(dtype):
+    M, n_in, n_out, r = 24, 128, 64, 16
+    L = inputs.random_case(M, n_in, n_out, r, dtype, seed=21)
+    S = random_24_dense(n_out, n_in, dtype, seed=22)
+    values, meta = oracle.prune24_pack(S, dtype)
+    Xf, Sf = inputs.to_f64(L.X, dtype), inputs.to_f64(S, dtype)
+    Uf, Vf = inputs.to_f64(L.U, dtype), inputs.to_f64(L.V, dtype)
+    scale = rms(Xf @ Sf.T)
+
+    # U = 0: only the sparse product remains
+    zU = np.zeros_like(L.U)
+    Y = oracle.linear(L.X, values, meta, zU, L.V, dtype)
+    assert np.max(np.abs(Y - Xf @ Sf.T)) <= 1e-13 * scale
+    # r = 0 gives the same
+    Y0 = oracle.linear(L.X, values, meta, None, None, dtype)
+    assert np.array_equal(Y0, Y)
+    # S = 0: only the low-rank product (X V^T) U^T remains
+    zv = np.zeros_like(values)
+    Y = oracle.linear(L.X, zv, meta, L.U, L.V, dtype)
+    lr = (Xf @ Vf.T) @ Uf.T
+    assert np.max(np.abs(Y - lr)) <= 1e-13 * rms(lr)
+    # X = I (M = n_in): Y = (S + U V)^T, i.e. the transposed reconstruction
+    eye = inputs.from_f64(np.eye(n_in), dtype)
+    Y = oracle.linear(eye, values, meta, L.U, L.V, dtype)
+    W = oracle.dense_reconstruct(values, meta, L.U, L.V, dtype)
+    assert np.array_equal(Y, W.T)
+    assert np.max(np.abs(W - (Sf + Uf @ Vf))) <= 1e-15 * rms(W) * 10
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_integer_exact(dtype):
+    M, n_in, n_out, r = 16, 512, 48, 16
+    X = inputs.small_integers((M, n_in), -4, 4, dtype, seed=1, tensor_id=0)
+    U = inputs.small_integers((n_out, r), -2, 2, dtype, seed=1, tensor_id=2)
+    V = inputs.small_integers((r, n_in), -2, 2, dtype, seed=1, tensor_id=3)
+    S = random_24_dense(n_out, n_in, dtype, seed=2, int_range=(-4, 4))
+    values, meta = oracle.prune24_pack(S, dtype)
+    Y = oracle.linear(X, values, meta, U, V, dtype)
+    Xi = inputs.to_f64(X, dtype).astype(np.int64)
+    Si = inputs.to_f64(S, dtype).astype(np.int64)
+    Ui = inputs.to_f64(U, dtype).astype(np.int64)
+    Vi = inputs.to_f64(V, dtype).astype(np.int64)
+    Yi = Xi @ Si.T + (Xi @ Vi.T) @ Ui.T
+    assert np.array_equal(Y, Yi.astype(np.float64))
+
+
+def test_linearity_and_rows():
+    dtype = "fp32"
+    L = inputs.random_case(20, 256, 40, 16, dtype, seed=31)
+    values, meta = oracle.prune24_pack(L.R, dtype)
+    Y1 = oracle.linear(L.X, values, meta, L.U, L.V, dtype)
+    # scaling by a power of two is exact on both sides
+    Y2x = oracle.linear(L.X * np.float32(2.0), values, meta, L.U, L.V, dtype)
+    assert np.array_equal(Y2x, 2.0 * Y1)
+    # additivity over inputs with disjoint column supports (their sum is exact)
+    Xa = L.X.copy(); Xa[:, 1::2] = 0
+    Xb = L.X.copy(); Xb[:, 0::2] = 0
+    Ya = oracle.linear(Xa, values, meta, L.U, L.V, dtype)
+    Yb = oracle.linear(Xb, values, meta, L.U, L.V, dtype)
+    assert np.max(np.abs(Y1 - (Ya + Yb))) <= 1e-13 * rms(Y1)
+    rows = np.array([19, 0, 7, 7, 3])
+    Yr = oracle.linear(L.X, values, meta, L.U, L.V, dtype, rows=rows)
+    assert np.array_equal(Yr, Y1[rows])
+
+
+def test_named_workload_small():
+    """C1 end to end: pack the residual, then the product equals X (S + U V)^T in numpy."""
+    L = inputs.make_layer("C1", 0)
+    values, meta = oracle.prune24_pack(L.R, "fp32")
+    Y = oracle.linear(L.X, values, meta, L.U, L.V, "fp32")
+    S = oracle.dense_reconstruct(values, meta, None, None, "fp32")
+    W = S + L.U.astype(np.float64) @ L.V.astype(np.float64)
+    Y_np = L.X.astype(np.float64) @ W.T
+    assert np.max(np.abs(Y - Y_np)) <= 1e-12 * rms(Y_np)
+    # the sparse part keeps more than half of the residual's energy
+    R = L.R.astype(np.float64)
+    assert (S ** 2).sum() > 0.5 * (R ** 2).sum()

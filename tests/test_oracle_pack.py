@@ -1,0 +1,201 @@
+"""Pins of the oracle's 2:4 projection + pack against what the pages and the mathematics fix.
+
+The projection is the sparse step with identity Hessian, solved exactly by hard thresholding
+(HASSLE-free page, §4.1.1), under the constraint that at most two of every four consecutive
+weights are nonzero (3BASiL article, "A three-block ADMM replaces alternating minimization").
+So it must return the Euclidean-nearest 2:4 matrix. The pins:
+  * brute force over all six keep patterns per group, minimising the discarded energy in exact
+    rational arithmetic, ties to the lexicographically smallest pattern;
+  * hand-written outcomes for ties and special values (tests/golden/pack_special_groups.txt);
+  * invariants: <= 2 nonzeros per group, idempotence, sign and power-of-two equivariance,
+    equivariance under permutations of whole groups, kept energy >= half the group's energy.
+"""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_rank_linear_prune24_amd import inputs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PATTERNS = [(a, b) for a in range(4) for b in range(a + 1, 4)]      # the six ways to keep two of four
+VALID_NIBBLES = {a | (b << 2) for a, b in PATTERNS}
+NP = {"fp32": np.float32, "bf16": np.uint16}
+
+
+def exact(x_bits, dtype):
+    """Exact rational value of a stored (finite) element."""
+    return Fraction(float(inputs.to_f64(np.array([x_bits], dtype=NP[dtype]), dtype)[0]))
+
+
+def brute_force_group(group_bits, dtype):
+    """Pattern (a, b) minimising the discarded energy, exactly; ties -> lexicographically smallest."""
+    vals = [exact(x, dtype) for x in group_bits]
+    best = None
+    for a, b in PATTERNS:           # PATTERNS is in lexicographic order, so `<` keeps the smallest
+        discarded = sum(v * v for i, v in enumerate(vals) if i not in (a, b))
+        if best is None or discarded < best[0]:
+            best = (discarded, a, b)
+    return best[1], best[2]
+
+
+def nibbles(meta):
+    meta = np.asarray(meta, dtype=np.uint32)
+    n_out, words = meta.shape
+    out = np.empty((n_out, words * 8), dtype=np.uint32)
+    for g in range(8):
+        out[:, g::8] = (meta >> (4 * g)) & 0xF
+    return out
+
+
+def groups_to_matrix(groups, dtype):
+    """Lay out 4-element groups (a storage-dtype array) as rows of 32 columns, zero padded."""
+    g = np.asarray(groups).reshape(-1, 4)
+    assert g.dtype == NP[dtype]
+    pad = (-len(g)) % 8
+    if pad:
+        g = np.concatenate([g, np.zeros((pad, 4), dtype=NP[dtype])])
+    return g.reshape(-1, 32), len(groups)
+
+
+def check_against_brute_force(R, dtype):
+    values, meta = oracle.prune24_pack(R, dtype)
+    nib = nibbles(meta)
+    n_out, n_in = R.shape
+    for n in range(n_out):
+        for g in range(n_in // 4):
+            grp = R[n, 4 * g:4 * g + 4]
+            a, b = brute_force_group(grp, dtype)
+            assert nib[n, g] == (a | (b << 2)), (n, g, grp, nib[n, g], (a, b))
+            assert values[n, 2 * g] == grp[a] and values[n, 2 * g + 1] == grp[b]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_exhaustive_small_integer_groups(dtype):
+    # every 4-tuple over {-2..2}: all tie shapes, zeros of both signs excluded (no -0 integers)
+    groups = list(itertools.product(range(-2, 3), repeat=4))
+    f = np.array(groups, dtype=np.float64)
+    R, _ = groups_to_matrix(inputs.from_f64(f, dtype), dtype)
+    check_against_brute_force(R, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_random_groups_brute_force(dtype):
+    g = np.random.default_rng(7)
+    f = g.standard_normal((40, 64)) * 0.02
+    # sprinkle exact ties, zeros and sign flips
+    f[:, 5] = f[:, 6]
+    f[:, 9] = -f[:, 10]
+    f[::3, 20:24] = 0.0
+    f[1::4, 33] = f[1::4, 35]
+    R = inputs.from_f64(f, dtype)
+    check_against_brute_force(R, dtype)
+
+
+def test_special_value_fixture():
+    rows = {"fp32": [], "bf16": []}
+    with open(os.path.join(HERE, "golden", "pack_special_groups.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            dtype = parts[0]
+            xs = [int(t, 16) for t in parts[1:5]]
+            rows[dtype].append((xs, int(parts[5], 16), int(parts[6], 16), int(parts[7], 16)))
+    assert len(rows["fp32"]) >= 15 and len(rows["bf16"]) >= 10
+    for dtype, cases in rows.items():
+        # place the cases at every group slot of a 32-wide row, twice over with an offset, so the
+        # nibble position inside the metadata word is exercised
+        for shift in range(2):
+            groups = [[0, 0, 0, 0]] * shift + [c[0] for c in cases]
+            bits = np.array(groups, dtype=np.uint32 if dtype == "fp32" else np.uint16)
+            R, ng = groups_to_matrix(bits.view(NP[dtype]), dtype)
+            values, meta = oracle.prune24_pack(R, dtype)
+            nib = nibbles(meta).reshape(-1)
+            vals = values.reshape(-1, 2)
+            for i, (xs, want_nib, v0, v1) in enumerate(cases):
+                k = i + shift
+                assert nib[k] == want_nib, (dtype, [hex(x) for x in xs], hex(nib[k]), hex(want_nib))
+                got = vals[k].view(np.uint32 if dtype == "fp32" else np.uint16)
+                assert int(got[0]) == v0 and int(got[1]) == v1, (dtype, [hex(x) for x in xs])
+
+
+def _dense_of(values, meta, dtype):
+    """The packed matrix scattered back to storage dtype (exact: S entries are stored values)."""
+    return inputs.from_f64(oracle.dense_reconstruct(values, meta, None, None, dtype), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_invariants_gaussian(dtype):
+    g = np.random.default_rng(11)
+    R = inputs.from_f64(g.standard_normal((96, 256)) * 0.02, dtype)
+    values, meta = oracle.prune24_pack(R, dtype)
+    nib = nibbles(meta)
+    assert set(np.unique(nib).tolist()) <= VALID_NIBBLES
+
+    S = _dense_of(values, meta, dtype)
+    Sf = inputs.to_f64(S, dtype)
+    nz = (Sf.reshape(96, -1, 4) != 0).sum(axis=2)
+    assert nz.max() <= 2
+    # kept entries are bit copies of R
+    kept = Sf != 0
+    assert np.array_equal(S[kept], R[kept])
+
+    # idempotence: projecting an already-2:4 matrix changes nothing
+    v2, m2 = oracle.prune24_pack(S, dtype)
+    assert np.array_equal(v2, values) and np.array_equal(m2, meta)
+
+    # sign equivariance: same positions, negated values (sign bit flipped)
+    sign = np.uint32(0x80000000) if dtype == "fp32" else np.uint16(0x8000)
+    Rb = R.view(np.uint32) if dtype == "fp32" else R
+    Rneg = (Rb ^ sign).view(R.dtype) if dtype == "fp32" else Rb ^ sign
+    vn, mn = oracle.prune24_pack(Rneg, dtype)
+    assert np.array_equal(mn, meta)
+    vb = values.view(np.uint32) if dtype == "fp32" else values
+    vnb = vn.view(np.uint32) if dtype == "fp32" else vn
+    assert np.array_equal(vnb, vb ^ sign)
+
+    # power-of-two scaling changes no decision (no overflow / underflow at these magnitudes)
+    for e in (-6, 3):
+        Rs = inputs.from_f64(inputs.to_f64(R, dtype) * 2.0 ** e, dtype)
+        vs, ms = oracle.prune24_pack(Rs, dtype)
+        assert np.array_equal(ms, meta)
+        assert np.array_equal(inputs.to_f64(vs, dtype), inputs.to_f64(values, dtype) * 2.0 ** e)
+
+    # permuting whole groups permutes the nibbles and value pairs the same way
+    perm = g.permutation(256 // 4)
+    Rp = R.reshape(96, -1, 4)[:, perm, :].reshape(96, 256)
+    vp, mp = oracle.prune24_pack(Rp, dtype)
+    assert np.array_equal(nibbles(mp), nib[:, perm])
+    assert np.array_equal(vp.reshape(96, -1, 2), values.reshape(96, -1, 2)[:, perm, :])
+
+    # kept energy is at least half of every group's energy (top two of four squares)
+    Rf = inputs.to_f64(R, dtype).reshape(96, -1, 4)
+    kept_e = (Sf.reshape(96, -1, 4) ** 2).sum(axis=2)
+    assert np.all(kept_e >= 0.5 * (Rf ** 2).sum(axis=2))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_optimal_against_every_pattern_vectorised(dtype):
+    """Large-scale brute force: the kept pattern discards no more energy than any of the six."""
+    g = np.random.default_rng(3)
+    R = inputs.from_f64(g.standard_normal((128, 512)) * 0.02, dtype)
+    values, meta = oracle.prune24_pack(R, dtype)
+    nib = nibbles(meta)
+    x2 = inputs.to_f64(R, dtype).reshape(128, -1, 4) ** 2
+    a = nib & 3
+    b = nib >> 2
+    total = x2.sum(axis=2)
+    chosen = total - np.take_along_axis(x2, a[..., None], 2)[..., 0] - np.take_along_axis(x2, b[..., None], 2)[..., 0]
+    for pa, pb in PATTERNS:
+        other = total - x2[..., pa] - x2[..., pb]
+        assert np.all(chosen <= other)
+
+
+def test_shape_errors():
+    with pytest.raises(ValueError):
+        oracle.prune24_pack(np.zeros((4, 48), dtype=np.float32), "fp32")   # 48 % 32 != 0
