@@ -1,0 +1,135 @@
+/*
+ * splr.h -- C ABI of libsplr.so: the 2:4 sparse + rank-r linear layer on AMD MI355X (gfx950).
+ *
+ * The layer approximates a weight W [n_out x n_in] by S + U V, where S keeps at most two of every
+ * four consecutive weights along the input dimension and U [n_out x r], V [r x n_in] are thin
+ * factors (LoSparse page, §3; 3BASiL article, "Splitting each weight matrix into two parts" and
+ * "A three-block ADMM replaces alternating minimization").  The forward pass evaluates the sparse
+ * product and the low-rank product side by side and adds them (LoSparse §3.2); in the orientation
+ * used here that is  Y = X S^T + (X V^T) U^T.
+ *
+ * General rules for every entry point
+ * -----------------------------------
+ *  - Array arguments are DEVICE pointers (hipMalloc / torch CUDA tensors), row-major, contiguous,
+ *    16-byte aligned.  The caller owns every buffer; the library never allocates or frees device
+ *    memory.  Outputs must not alias inputs.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns without waiting.
+ *  - Arguments are validated before any HIP call: on a validation error nothing is enqueued and
+ *    the error code is returned.  A failed launch returns SPLR_ERR_HIP.  No C++ exception crosses
+ *    the boundary.
+ *  - Storage types: SPLR_FP32 = IEEE binary32, SPLR_BF16 = bfloat16 (upper half of a binary32).
+ *    The same dtype applies to every floating-point input of one call; Y and W_hat are float32.
+ *  - n_in must be a positive multiple of 32 (a metadata word covers 32 input columns).
+ *
+ * Packed 2:4 layout (shared by every entry point)
+ * -----------------------------------------------
+ *  values [n_out][n_in/2] dtype  : the two kept entries of each group of four consecutive input
+ *                                  columns, in ascending column order.
+ *  meta   [n_out][n_in/32] uint32: group g of a row (columns 4g..4g+3) is described by the nibble
+ *                                  (a | b << 2) stored at bits 4*(g % 8) of word g / 8, where
+ *                                  a < b in {0,1,2,3} are the kept positions.  Valid nibbles:
+ *                                  0x4 0x8 0xC 0x9 0xD 0xE.  Metadata not produced by
+ *                                  splr_prune24_pack gives unspecified results (not checked).
+ */
+#ifndef SPLR_H_
+#define SPLR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SPLR_FP32 = 0, SPLR_BF16 = 1 } splr_dtype_t;
+
+typedef enum {
+  SPLR_OK = 0,
+  SPLR_ERR_NULL = 1,      /* a required pointer is NULL                                         */
+  SPLR_ERR_SHAPE = 2,     /* a size is out of range (see each entry point)                      */
+  SPLR_ERR_DTYPE = 3,     /* unknown splr_dtype_t                                               */
+  SPLR_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                                   */
+  SPLR_ERR_HIP = 5,       /* the HIP runtime reported an error while enqueueing                 */
+  SPLR_ERR_WORKSPACE = 6  /* workspace NULL or smaller than splr_linear_workspace_bytes()      */
+} splr_status_t;
+
+/*
+ * splr_prune24_pack -- Euclidean projection of a dense matrix onto the 2:4 set, then packing.
+ *
+ * This is the sparse step of the alternating-minimisation / ADMM decompositions: with an identity
+ * Hessian, hard thresholding solves it exactly (HASSLE-free page, §4.1.1); the constraint allows at
+ * most two nonzeros in every four consecutive weights (3BASiL article, "A three-block ADMM replaces
+ * alternating minimization").  R is typically the residual W - U V.
+ *
+ * For each row and each group of four consecutive columns the two entries of largest magnitude
+ * are kept as bit copies.  Magnitude is compared as the bit pattern with the sign cleared: +0 and
+ * -0 tie, subnormals are ordered exactly, infinities outrank finite values, NaNs outrank
+ * infinities (by payload).  Equal magnitudes go to the lower column.  The result is bit-exact and
+ * deterministic.
+ *
+ *   R      [n_out][n_in] dtype   input
+ *   values [n_out][n_in/2] dtype output
+ *   meta   [n_out][n_in/32] u32  output
+ * Errors: NULL pointer -> SPLR_ERR_NULL; n_out < 1, n_in < 32 or n_in % 32 != 0 -> SPLR_ERR_SHAPE;
+ *         bad dtype -> SPLR_ERR_DTYPE; misaligned pointer -> SPLR_ERR_ALIGN.
+ */
+splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr_dtype_t dtype,
+                                void* values, uint32_t* meta, hipStream_t stream);
+
+/*
+ * splr_linear_workspace_bytes -- device workspace that splr_linear needs for these sizes
+ * (0 when none).  It holds the first low-rank stage T = X V^T.
+ */
+size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64_t r,
+                                   splr_dtype_t dtype);
+
+/*
+ * splr_linear -- Y = X S^T + (X V^T) U^T  (LoSparse §3.2: both products, summed).
+ *
+ *   X      [M][n_in] dtype                       activations
+ *   values [n_out][n_in/2] dtype, meta [n_out][n_in/32] u32   packed S (layout above)
+ *   U      [n_out][r] dtype, V [r][n_in] dtype   thin factors; both may be NULL iff r == 0
+ *   Y      [M][n_out] float32                    output, written once
+ *   workspace / workspace_bytes                  device scratch of at least
+ *                                                splr_linear_workspace_bytes(...) bytes (may be
+ *                                                NULL when that is 0); contents need not be
+ *                                                initialised and are clobbered.
+ * Arithmetic: products of dtype operands accumulated in float32.  With SPLR_BF16 the first
+ * low-rank stage T is kept to about 16 significant bits (a bfloat16 high part plus a bfloat16
+ * correction), never rounded to a single bfloat16.  Results are bitwise reproducible run to run
+ * (fixed reduction order, no floating-point atomics).
+ * Errors: NULL pointer -> SPLR_ERR_NULL; M < 1, n_out < 1, n_in < 32, n_in % 32 != 0, r < 0,
+ *         r > 1024 or r % 16 != 0 -> SPLR_ERR_SHAPE; bad dtype -> SPLR_ERR_DTYPE; misaligned
+ *         pointer -> SPLR_ERR_ALIGN; workspace too small -> SPLR_ERR_WORKSPACE.
+ */
+splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* values,
+                          const uint32_t* meta, int64_t n_out, const void* U, const void* V,
+                          int64_t r, splr_dtype_t dtype, float* Y, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * splr_dense_reconstruct -- W_hat = S + U V as a dense float32 matrix (LoSparse §3: the weight is
+ * approximated by the sum of the sparse and the low-rank part).  A verification aid.
+ *
+ *   values, meta : packed S [n_out x n_in];  U [n_out][r], V [r][n_in] (NULL iff r == 0)
+ *   W_hat [n_out][n_in] float32 output: stored entries widened exactly at their columns, +0
+ *         elsewhere, plus the rank-r product accumulated in float32.
+ * Errors: as splr_linear (no workspace).
+ */
+splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, const void* U,
+                                     const void* V, int64_t n_out, int64_t n_in, int64_t r,
+                                     splr_dtype_t dtype, float* W_hat, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* splr_status_string(splr_status_t status);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* splr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLR_H_ */

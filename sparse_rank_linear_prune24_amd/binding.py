@@ -1,0 +1,139 @@
+"""Thin ctypes binding of libsplr.so (C ABI in include/splr.h).
+
+Argument marshalling only: tensors are passed as device pointers together with torch's current
+HIP stream; every step of the computation runs in the library's kernels. There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+
+Conventions: bf16 tensors are torch.bfloat16, fp32 tensors torch.float32; metadata is int32
+(the bits of the library's uint32 words).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsplr.so")
+
+SPLR_FP32, SPLR_BF16 = 0, 1
+STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
+          5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
+EXPORTS = ("splr_prune24_pack", "splr_linear_workspace_bytes", "splr_linear", "splr_dense_reconstruct",
+           "splr_status_string", "splr_version")
+
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_lib = None
+
+
+class SplrError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types declared (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_rank_linear_prune24_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.splr_prune24_pack.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P]
+        L.splr_prune24_pack.restype = _I32
+        L.splr_linear_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32]
+        L.splr_linear_workspace_bytes.restype = _SZ
+        L.splr_linear.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P, _SZ, _P]
+        L.splr_linear.restype = _I32
+        L.splr_dense_reconstruct.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]
+        L.splr_dense_reconstruct.restype = _I32
+        L.splr_status_string.argtypes = [_I32]
+        L.splr_status_string.restype = ctypes.c_char_p
+        L.splr_version.argtypes = []
+        L.splr_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPLR_BF16
+    if t.dtype == torch.float32:
+        return SPLR_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (use torch.bfloat16 or torch.float32)")
+
+
+def _dev(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SplrError(fn, status)
+
+
+def prune24_pack(R: torch.Tensor, values: Optional[torch.Tensor] = None, meta: Optional[torch.Tensor] = None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """2:4 projection + pack of R [n_out, n_in] -> (values [n_out, n_in/2], meta int32 [n_out, n_in/32])."""
+    n_out, n_in = R.shape
+    if values is None:
+        values = torch.empty((n_out, n_in // 2), dtype=R.dtype, device=R.device)
+    if meta is None:
+        meta = torch.empty((n_out, max(n_in // 32, 0)), dtype=torch.int32, device=R.device)
+    _check("splr_prune24_pack", lib().splr_prune24_pack(_dev(R, "R"), n_out, n_in, _dtype_code(R),
+                                                        _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
+    return values, meta
+
+
+def workspace_bytes(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype) -> int:
+    code = SPLR_BF16 if dtype == torch.bfloat16 else SPLR_FP32
+    return int(lib().splr_linear_workspace_bytes(M, n_out, n_in, r, code))
+
+
+def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
+           V: Optional[torch.Tensor], out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y [M, n_out] float32 = X S^T + (X V^T) U^T."""
+    M, n_in = X.shape
+    n_out = values.shape[0]
+    r = 0 if U is None else U.shape[1]
+    if out is None:
+        out = torch.empty((M, n_out), dtype=torch.float32, device=X.device)
+    need = workspace_bytes(M, n_out, n_in, r, X.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("splr_linear", lib().splr_linear(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
+                                            _dev(U, "U"), _dev(V, "V"), r, _dtype_code(X), _dev(out, "out"),
+                                            _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return out
+
+
+def dense_reconstruct(values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
+                      V: Optional[torch.Tensor], out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """W_hat [n_out, n_in] float32 = S + U V."""
+    n_out, n_in = values.shape[0], values.shape[1] * 2
+    r = 0 if U is None else U.shape[1]
+    if out is None:
+        out = torch.empty((n_out, n_in), dtype=torch.float32, device=values.device)
+    _check("splr_dense_reconstruct",
+           lib().splr_dense_reconstruct(_dev(values, "values"), _dev(meta, "meta"), _dev(U, "U"), _dev(V, "V"),
+                                        n_out, n_in, r, _dtype_code(values), _dev(out, "out"), _stream(stream)))
+    return out
+
+
+def version() -> str:
+    return lib().splr_version().decode()

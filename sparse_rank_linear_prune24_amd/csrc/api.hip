@@ -1,0 +1,126 @@
+// C ABI of libsplr (declared in include/splr.h): argument validation, workspace sizing and
+// kernel dispatch.  Every check runs before the first HIP call, so a rejected call enqueues
+// nothing; the library holds no mutable state and never allocates device memory.
+#include "splr.h"
+
+#include "kernels.hpp"
+
+namespace {
+
+// Size limits keep every index the kernels form inside their integer types.
+constexpr int64_t kMaxRows = int64_t(1) << 24;      // n_out and M
+constexpr int64_t kMaxCols = int64_t(1) << 20;      // n_in
+constexpr int64_t kMaxElems = int64_t(1) << 36;     // n_out * n_in, M * n_in, M * n_out
+constexpr int64_t kMaxRank = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(splr_dtype_t d) { return d == SPLR_FP32 || d == SPLR_BF16; }
+
+splr_status_t check_in(int64_t n_in) {
+  return (n_in >= 32 && n_in <= kMaxCols && n_in % 32 == 0) ? SPLR_OK : SPLR_ERR_SHAPE;
+}
+
+splr_status_t check_rows(int64_t rows, int64_t n_in) {
+  if (rows < 1 || rows > kMaxRows) return SPLR_ERR_SHAPE;
+  if (rows * n_in > kMaxElems) return SPLR_ERR_SHAPE;
+  return SPLR_OK;
+}
+
+splr_status_t check_rank(int64_t r) {
+  return (r >= 0 && r <= kMaxRank && r % 16 == 0) ? SPLR_OK : SPLR_ERR_SHAPE;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t workspace_bytes(int64_t M, int64_t n_in, int64_t r, splr_dtype_t dtype) {
+  if (r == 0) return 0;
+  const int ks = splr::lowrank_ksplit(M, n_in, r, dtype == SPLR_BF16);
+  return round_up((size_t)ks * (size_t)M * (size_t)r * sizeof(float), 256);
+}
+
+splr_status_t from_hip(hipError_t e) { return e == hipSuccess ? SPLR_OK : SPLR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr_dtype_t dtype, void* values,
+                                uint32_t* meta, hipStream_t stream) {
+  if (!R || !values || !meta) return SPLR_ERR_NULL;
+  splr_status_t s = check_in(n_in);
+  if (s == SPLR_OK) s = check_rows(n_out, n_in);
+  if (s != SPLR_OK) return s;
+  if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!aligned16(R) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
+  return from_hip(splr::launch_prune24_pack(R, n_out, n_in, dtype == SPLR_BF16, values, meta, stream));
+}
+
+size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64_t r, splr_dtype_t dtype) {
+  (void)n_out;
+  if (M < 1 || check_in(n_in) != SPLR_OK || check_rank(r) != SPLR_OK || !dtype_ok(dtype)) return 0;
+  return workspace_bytes(M, n_in, r, dtype);
+}
+
+splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                          int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, float* Y,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!X || !values || !meta || !Y) return SPLR_ERR_NULL;
+  if (r > 0 && (!U || !V)) return SPLR_ERR_NULL;
+  splr_status_t s = check_in(n_in);
+  if (s == SPLR_OK) s = check_rows(M, n_in);
+  if (s == SPLR_OK) s = check_rows(n_out, n_in);
+  if (s == SPLR_OK) s = check_rank(r);
+  if (s == SPLR_OK && M * n_out > kMaxElems) s = SPLR_ERR_SHAPE;
+  if (s != SPLR_OK) return s;
+  if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(Y)) return SPLR_ERR_ALIGN;
+  if (r > 0 && (!aligned16(U) || !aligned16(V))) return SPLR_ERR_ALIGN;
+  const size_t need = workspace_bytes(M, n_in, r, dtype);
+  if (need > 0 && (!workspace || ws_bytes < need)) return SPLR_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return SPLR_ERR_ALIGN;
+
+  const bool bf16 = dtype == SPLR_BF16;
+  float* T = static_cast<float*>(workspace);
+  const int ks = splr::lowrank_ksplit(M, n_in, r, bf16);
+  hipError_t e = splr::launch_lowrank(X, V, M, n_in, r, bf16, ks, T, stream);
+  if (e != hipSuccess) return SPLR_ERR_HIP;
+  if (bf16)
+    e = splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, T, ks, Y, stream);
+  else
+    e = splr::launch_linear_f32((const float*)X, M, n_in, (const float*)values, meta, n_out, (const float*)U, r, T,
+                                Y, stream);
+  return from_hip(e);
+}
+
+splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, const void* U, const void* V,
+                                     int64_t n_out, int64_t n_in, int64_t r, splr_dtype_t dtype, float* W_hat,
+                                     hipStream_t stream) {
+  if (!values || !meta || !W_hat) return SPLR_ERR_NULL;
+  if (r > 0 && (!U || !V)) return SPLR_ERR_NULL;
+  splr_status_t s = check_in(n_in);
+  if (s == SPLR_OK) s = check_rows(n_out, n_in);
+  if (s == SPLR_OK) s = check_rank(r);
+  if (s != SPLR_OK) return s;
+  if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!aligned16(values) || !aligned16(meta) || !aligned16(W_hat)) return SPLR_ERR_ALIGN;
+  if (r > 0 && (!aligned16(U) || !aligned16(V))) return SPLR_ERR_ALIGN;
+  return from_hip(splr::launch_dense_reconstruct(values, meta, U, V, n_out, n_in, r, dtype == SPLR_BF16, W_hat,
+                                                 stream));
+}
+
+const char* splr_status_string(splr_status_t status) {
+  switch (status) {
+    case SPLR_OK: return "SPLR_OK";
+    case SPLR_ERR_NULL: return "SPLR_ERR_NULL: a required pointer is NULL";
+    case SPLR_ERR_SHAPE: return "SPLR_ERR_SHAPE: a size is out of range";
+    case SPLR_ERR_DTYPE: return "SPLR_ERR_DTYPE: unknown dtype";
+    case SPLR_ERR_ALIGN: return "SPLR_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case SPLR_ERR_HIP: return "SPLR_ERR_HIP: the HIP runtime reported an error";
+    case SPLR_ERR_WORKSPACE: return "SPLR_ERR_WORKSPACE: workspace missing or too small";
+  }
+  return "SPLR_ERR_UNKNOWN";
+}
+
+const char* splr_version(void) { return "0.1.0"; }
+
+}  // extern "C"

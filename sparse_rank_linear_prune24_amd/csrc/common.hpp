@@ -1,0 +1,62 @@
+// Internal helpers shared by the gfx950 kernels of libsplr (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splr {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ bf16x16_t cat16(bf16x8_t lo, bf16x8_t hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bfloat16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Split eight float32 values into bfloat16 high parts and bfloat16 corrections:
+// x ~= hi + lo with |x - hi - lo| <= 2^-18 |x| (about 16 significant bits).
+__device__ __forceinline__ void split_hi_lo(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  u32x4_t h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h0 = float_to_bf16_bits(x[2 * i]), h1 = float_to_bf16_bits(x[2 * i + 1]);
+    uint32_t l0 = float_to_bf16_bits(x[2 * i] - bf16_bits_to_float(h0));
+    uint32_t l1 = float_to_bf16_bits(x[2 * i + 1] - bf16_bits_to_float(h1));
+    h[i] = h0 | (h1 << 16);
+    l[i] = l0 | (l1 << 16);
+  }
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(l);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Structured-sparse MFMA, 16x16 output, 64 dense K. A: 8 kept bf16 per lane (4 groups of the
+// lane's 16-column K slice), B: 16 bf16 per lane, idx: the lane's 4 group nibbles in bits [15:0].
+__device__ __forceinline__ f32x4_t smfmac16x16x64(bf16x8_t a, bf16x16_t b, f32x4_t c, int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, 0);
+}
+
+__host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace splr

@@ -1,0 +1,47 @@
+// Y = X S^T + T U^T for float32 operands (T = X V^T from the first low-rank stage), float32
+// arithmetic throughout (LoSparse page, §3.2: the two products summed).  One lane per output;
+// the sparse sum walks the row's groups in order, two fused multiply-adds per group.  This path
+// exists for exact-type float32 layers (small, latency-bound); bf16 layers use the MFMA kernels.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace splr {
+namespace {
+
+__global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict__ X, const float* __restrict__ values,
+                                                        const uint32_t* __restrict__ meta,
+                                                        const float* __restrict__ U, const float* __restrict__ T,
+                                                        float* __restrict__ Y, int M, int K, int n_out, int r) {
+  const int n = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (n >= n_out || m >= M) return;
+  const float* x = X + (size_t)m * K;
+  const float* v = values + (size_t)n * (K / 2);
+  const uint32_t* mw = meta + (size_t)n * (K / 32);
+  float acc = 0.0f;
+  for (int w = 0; w < K / 32; ++w) {
+    const uint32_t word = mw[w];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int grp = w * 8 + g;
+      const uint32_t nib = (word >> (4 * g)) & 0xFu;
+      acc = fmaf(x[4 * grp + (nib & 3u)], v[2 * grp], acc);
+      acc = fmaf(x[4 * grp + (nib >> 2)], v[2 * grp + 1], acc);
+    }
+  }
+  float lr = 0.0f;
+  for (int j = 0; j < r; ++j) lr = fmaf(T[(size_t)m * r + j], U[(size_t)n * r + j], lr);
+  Y[(size_t)m * n_out + n] = acc + lr;
+}
+
+}  // namespace
+
+hipError_t launch_linear_f32(const float* X, int64_t M, int64_t n_in, const float* values, const uint32_t* meta,
+                             int64_t n_out, const float* U, int64_t r, const float* T, float* Y,
+                             hipStream_t stream) {
+  dim3 grid((unsigned)ceil_div(n_out, 64), (unsigned)ceil_div(M, 4));
+  linear_f32_kernel<<<grid, dim3(256), 0, stream>>>(X, values, meta, U, T, Y, (int)M, (int)n_in, (int)n_out, (int)r);
+  return hipGetLastError();
+}
+
+}  // namespace splr

@@ -1,0 +1,59 @@
+// W_hat = S + U V as a dense float32 matrix (LoSparse page, §3: the weight is approximated by the
+// sum of the sparse and the low-rank part).  One lane per group of four columns: the two stored
+// entries are widened exactly to float32 at their columns (+0 elsewhere); when r > 0 the rank-r
+// sum, accumulated in float32 over j in order, is added once.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace splr {
+namespace {
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, size_t i) {
+  if (BF16) return bf16_bits_to_float(((const uint16_t*)p)[i]);
+  return ((const float*)p)[i];
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void dense_reconstruct_kernel(const void* __restrict__ values,
+                                                               const uint32_t* __restrict__ meta,
+                                                               const void* __restrict__ U, const void* __restrict__ V,
+                                                               int64_t n_out, int K, int r, float* __restrict__ W) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int groups = K / 4;
+  if (t >= n_out * groups) return;
+  const int64_t n = t / groups;
+  const int g = (int)(t - n * groups);
+  const uint32_t nib = (meta[(size_t)n * (K / 32) + g / 8] >> (4 * (g % 8))) & 0xFu;
+  const int a = (int)(nib & 3u), b = (int)(nib >> 2);
+  float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  out[a] = load_elem<BF16>(values, (size_t)n * (K / 2) + 2 * g);
+  out[b] = load_elem<BF16>(values, (size_t)n * (K / 2) + 2 * g + 1);
+  if (r > 0) {
+    float lr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < r; ++j) {
+      const float u = load_elem<BF16>(U, (size_t)n * r + j);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lr[q] = fmaf(u, load_elem<BF16>(V, (size_t)j * K + 4 * g + q), lr[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] += lr[q];
+  }
+  *(f32x4_t*)(W + (size_t)n * K + 4 * g) = f32x4_t{out[0], out[1], out[2], out[3]};
+}
+
+}  // namespace
+
+hipError_t launch_dense_reconstruct(const void* values, const uint32_t* meta, const void* U, const void* V,
+                                    int64_t n_out, int64_t n_in, int64_t r, bool bf16, float* W_hat,
+                                    hipStream_t stream) {
+  const int64_t threads = n_out * (n_in / 4);
+  dim3 grid((unsigned)ceil_div(threads, 256));
+  if (bf16)
+    dense_reconstruct_kernel<true><<<grid, dim3(256), 0, stream>>>(values, meta, U, V, n_out, (int)n_in, (int)r, W_hat);
+  else
+    dense_reconstruct_kernel<false><<<grid, dim3(256), 0, stream>>>(values, meta, U, V, n_out, (int)n_in, (int)r, W_hat);
+  return hipGetLastError();
+}
+
+}  // namespace splr

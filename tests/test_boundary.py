@@ -1,0 +1,97 @@
+"""The C ABI on the CPU: the library loads, exports what include/splr.h declares, and rejects bad
+arguments before any HIP call (so these run without a GPU; no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_rank_linear_prune24_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, DTYPE, ALIGN, HIP, WORKSPACE = range(7)
+A = 0x10000          # an aligned, never dereferenced address
+MIS = 0x10008        # misaligned
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "splr.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**(splr_[a-z0-9_]+)\(", text, re.M)))
+
+
+def test_exports_match_header():
+    declared = header_functions()
+    assert set(declared) == set(binding.EXPORTS), declared
+    lib = binding.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert binding.version().count(".") == 2
+
+
+def test_status_strings():
+    lib = binding.lib()
+    for code in range(7):
+        assert lib.splr_status_string(code).decode().startswith(binding.STATUS[code])
+    assert lib.splr_status_string(99) == b"SPLR_ERR_UNKNOWN"
+
+
+def test_pack_validation():
+    f = binding.lib().splr_prune24_pack
+    assert f(None, 4, 64, 1, A, A, None) == NULL
+    assert f(A, 4, 64, 1, None, A, None) == NULL
+    assert f(A, 0, 64, 1, A, A, None) == SHAPE
+    assert f(A, 4, 48, 1, A, A, None) == SHAPE
+    assert f(A, 4, 0, 1, A, A, None) == SHAPE
+    assert f(A, -1, 64, 1, A, A, None) == SHAPE
+    assert f(A, 1 << 25, 64, 1, A, A, None) == SHAPE
+    assert f(A, 4, 64, 2, A, A, None) == DTYPE
+    assert f(MIS, 4, 64, 1, A, A, None) == ALIGN
+    assert f(A, 4, 64, 0, A, MIS, None) == ALIGN
+
+
+def test_linear_validation():
+    f = binding.lib().splr_linear
+    ws = binding.lib().splr_linear_workspace_bytes
+    good = dict(X=A, M=16, n_in=64, values=A, meta=A, n_out=32, U=A, V=A, r=16, dt=1, Y=A, ws=A,
+                wsb=1 << 30, stream=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["X"], a["M"], a["n_in"], a["values"], a["meta"], a["n_out"], a["U"], a["V"], a["r"], a["dt"],
+                 a["Y"], a["ws"], a["wsb"], a["stream"])
+
+    assert call(X=None) == NULL
+    assert call(Y=None) == NULL
+    assert call(U=None) == NULL
+    assert call(M=0) == SHAPE
+    assert call(n_out=0) == SHAPE
+    assert call(n_in=80) == SHAPE
+    assert call(r=8) == SHAPE
+    assert call(r=-16) == SHAPE
+    assert call(r=2048) == SHAPE
+    assert call(dt=7) == DTYPE
+    assert call(X=MIS) == ALIGN
+    assert call(V=MIS) == ALIGN
+    assert call(Y=MIS) == ALIGN
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=ws(16, 32, 64, 16, 1) - 1) == WORKSPACE
+    # r == 0: U, V may be NULL (this case would pass validation, so only the size query is checked)
+    assert ws(16, 32, 64, 0, 1) == 0
+    assert ws(16, 32, 64, 16, 1) > 0 and ws(2048, 4096, 4096, 64, 1) % 256 == 0
+    assert ws(0, 32, 64, 16, 1) == 0
+
+
+def test_reconstruct_validation():
+    f = binding.lib().splr_dense_reconstruct
+    assert f(None, A, A, A, 4, 64, 16, 1, A, None) == NULL
+    assert f(A, A, None, A, 4, 64, 16, 1, A, None) == NULL
+    assert f(A, A, A, A, 4, 40, 16, 1, A, None) == SHAPE
+    assert f(A, A, A, A, 4, 64, 17, 1, A, None) == SHAPE
+    assert f(A, A, A, A, 4, 64, 16, 5, A, None) == DTYPE
+    assert f(A, A, A, A, 4, 64, 16, 1, MIS, None) == ALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        binding.prune24_pack(torch.zeros((4, 64), dtype=torch.bfloat16))

@@ -1,0 +1,173 @@
+"""GPU parity of splr_linear against the float64 oracle.
+
+Bar (written here, checked on every case): max|Y_gpu - Y_ref| <= tau * rms(Y_ref) with tau = 1e-5 for
+float32 inputs and 1e-2 for bfloat16 inputs (float32 accumulation), Y_ref computed by the oracle on
+the same rounded inputs. Both sides pack their own S from the same residual R; the packs are
+compared bit for bit first.
+
+The bf16 cases also check a tighter bound, TIGHT = 2e-4: products of bfloat16 values are exact in
+float32 and sums over at most 14336 terms keep the float32 error near 1e-5 rms; the first low-rank
+stage is carried as a bfloat16 pair (relative error <= 2^-18 per element). A dropped term or a misplaced index
+shows up far above this bound, while the 1e-2 bar alone could miss the small rank-r term.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_rank_linear_prune24_amd import binding, configs, inputs
+from tests._helpers import TAU, from_dev, meta_from_dev, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+TIGHT = 2e-4
+
+
+def run_gpu(L, dtype, pack_on_gpu=True):
+    Xd, Ud, Vd = to_dev(L.X, dtype), to_dev(L.U if L.r else None, dtype), to_dev(L.V if L.r else None, dtype)
+    vd, md = binding.prune24_pack(to_dev(L.R, dtype))
+    Y = binding.linear(Xd, vd, md, Ud, Vd)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy(), from_dev(vd, dtype), meta_from_dev(md)
+
+
+def check_layer(L, dtype, tag, rows=None, tight=True):
+    print(f"[linear] {tag} dtype={dtype} M={L.M} n_in={L.n_in} n_out={L.n_out} r={L.r}", flush=True)
+    Y, v, m = run_gpu(L, dtype)
+    v_ref, m_ref = oracle.prune24_pack(L.R, dtype)
+    bits = np.uint32 if dtype == "fp32" else np.uint16
+    assert np.array_equal(m, m_ref) and np.array_equal(v.view(bits), v_ref.view(bits)), f"{tag}: pack differs"
+    U, V = (L.U, L.V) if L.r else (None, None)
+    Y_ref = oracle.linear(L.X, v_ref, m_ref, U, V, dtype, rows=rows)
+    Yg = Y if rows is None else Y[rows]
+    assert np.all(np.isfinite(Yg))
+    err = rel_err(Yg, Y_ref)
+    print(f"[linear] {tag}: max|dY|/rms = {err:.3e}", flush=True)
+    assert err <= TAU[dtype], f"{tag}: {err:.3e} > {TAU[dtype]}"
+    if dtype == "bf16" and tight:
+        assert err <= TIGHT, f"{tag}: {err:.3e} above the expected float32-accumulation error"
+    return err
+
+
+# shapes spanning several tiles, ragged in every dimension; M <= 64 takes the decode kernel
+SHAPES = [
+    (1, 64, 16, 16), (5, 32, 40, 16), (16, 256, 48, 32), (17, 96, 33, 16), (33, 512, 130, 48),
+    (64, 320, 64, 0), (65, 1024, 129, 64), (130, 96, 257, 16), (200, 2080, 300, 64), (257, 512, 513, 128),
+    (1024, 1024, 384, 64),
+]
+
+
+@pytest.mark.parametrize("M,n_in,n_out,r", SHAPES)
+def test_bf16_shapes(M, n_in, n_out, r):
+    L = inputs.random_case(M, n_in, n_out, r, "bf16", seed=M + n_in + n_out + r, n_outliers=2)
+    check_layer(L, "bf16", f"bf16 {M}x{n_in}->{n_out} r{r}")
+
+
+@pytest.mark.parametrize("M,n_in,n_out,r", [(32, 512, 512, 16), (3, 64, 20, 16), (70, 160, 33, 32), (16, 96, 8, 0)])
+def test_fp32_shapes(M, n_in, n_out, r):
+    L = inputs.random_case(M, n_in, n_out, r, "fp32", seed=M * n_in + r)
+    check_layer(L, "fp32", f"fp32 {M}x{n_in}->{n_out} r{r}")
+
+
+@pytest.mark.parametrize("cfg", ["C1", "C2", "C3"])
+def test_named_full(cfg):
+    c = configs.get(cfg)
+    L = inputs.make_layer(cfg, 0)
+    check_layer(L, c.dtype, cfg)
+
+
+@pytest.mark.parametrize("cfg", ["C4", "C5"])
+def test_named_sampled_rows(cfg):
+    """Full-size layers (the benchmark's launch configuration); the oracle evaluates sampled token
+    rows (first, last, tile edges and random ones), each compared element by element."""
+    c = configs.get(cfg)
+    g = np.random.default_rng(c.config_id)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, 255, c.M - 129, c.M - 1],
+                                     g.integers(0, c.M, size=23)]))
+    for li in range(len(c.layers)):
+        L = inputs.make_layer(cfg, li)
+        check_layer(L, c.dtype, f"{cfg}/{L.name}", rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("M", [16, 200])
+def test_special_cases(dtype, M):
+    n_in, n_out, r = 512, 192, 32
+    L = inputs.random_case(M, n_in, n_out, r, dtype, seed=77)
+    vd, md = binding.prune24_pack(to_dev(L.R, dtype))
+    v, m = from_dev(vd, dtype), meta_from_dev(md)
+    Xd, Ud, Vd = to_dev(L.X, dtype), to_dev(L.U, dtype), to_dev(L.V, dtype)
+
+    # S = 0: only the low-rank path. float32 operands: the 1e-5 bar. bfloat16 operands: T = X V^T
+    # is carried as a bfloat16 pair hi + lo with |T - hi - lo| <= 2^-18 |T| per element, so the
+    # largest output error is a small multiple of 2^-18 rms(Y); 4e-5 (~10 x 2^-18) bounds it.
+    zv = torch.zeros_like(vd)
+    Y = binding.linear(Xd, zv, md, Ud, Vd).cpu().numpy()
+    ref = oracle.linear(L.X, np.zeros_like(v), m, L.U, L.V, dtype)
+    assert rel_err(Y, ref) <= (1e-5 if dtype == "fp32" else 4e-5), "S = 0"
+    # U = 0 and r = 0: only the sparse product
+    Y0 = binding.linear(Xd, vd, md, torch.zeros_like(Ud), Vd).cpu().numpy()
+    Yr0 = binding.linear(Xd, vd, md, None, None).cpu().numpy()
+    ref = oracle.linear(L.X, v, m, None, None, dtype)
+    assert rel_err(Y0, ref) <= (1e-5 if dtype == "fp32" else TIGHT), "U = 0"
+    assert np.array_equal(Y0, Yr0), "U = 0 and r = 0 differ"
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_identity_input(dtype):
+    """X = I (M = n_in): Y is the transposed reconstruction S + U V."""
+    n_in, n_out, r = 128, 96, 16
+    L = inputs.random_case(n_in, n_in, n_out, r, dtype, seed=5)
+    vd, md = binding.prune24_pack(to_dev(L.R, dtype))
+    eye = to_dev(inputs.from_f64(np.eye(n_in), dtype), dtype)
+    Y = binding.linear(eye, vd, md, to_dev(L.U, dtype), to_dev(L.V, dtype)).cpu().numpy()
+    W = oracle.dense_reconstruct(from_dev(vd, dtype), meta_from_dev(md), L.U, L.V, dtype)
+    assert rel_err(Y, W.T) <= 1e-5
+
+
+@pytest.mark.parametrize("M", [16, 48, 256])
+def test_integer_exact_bitwise(M):
+    """Small integers make every product and partial sum exact in float32 (all < 2^24): the GPU
+    result must equal the oracle exactly, for both kernels (decode M <= 64, prefill above)."""
+    dtype, n_in, n_out, r = "bf16", 512, 160, 16
+    X = inputs.small_integers((M, n_in), -4, 4, dtype, seed=M, tensor_id=0)
+    U = inputs.small_integers((n_out, r), -2, 2, dtype, seed=M, tensor_id=2)
+    V = inputs.small_integers((r, n_in), -2, 2, dtype, seed=M, tensor_id=3)
+    R = inputs.small_integers((n_out, n_in), -4, 4, dtype, seed=M, tensor_id=1)
+    v_ref, m_ref = oracle.prune24_pack(R, dtype)
+    ref = oracle.linear(X, v_ref, m_ref, U, V, dtype)
+    vd, md = binding.prune24_pack(to_dev(R, dtype))
+    Y = binding.linear(to_dev(X, dtype), vd, md, to_dev(U, dtype), to_dev(V, dtype)).cpu().numpy()
+    assert np.array_equal(Y.astype(np.float64), ref)
+
+
+def test_balanced_scale_lowrank():
+    """U V as large as W: the rank-r term is no longer a small correction."""
+    dtype, M, n_in, n_out, r = "bf16", 256, 1024, 320, 64
+    uv_std = np.sqrt(0.02) / r ** 0.25
+    L = inputs.random_case(M, n_in, n_out, r, dtype, seed=9, uv_std=uv_std, n_outliers=8)
+    check_layer(L, dtype, "balanced")
+
+
+def test_deterministic():
+    L = inputs.random_case(300, 1024, 256, 64, "bf16", seed=3)
+    Xd, Ud, Vd = to_dev(L.X, "bf16"), to_dev(L.U, "bf16"), to_dev(L.V, "bf16")
+    vd, md = binding.prune24_pack(to_dev(L.R, "bf16"))
+    Y1 = binding.linear(Xd, vd, md, Ud, Vd)
+    Y2 = binding.linear(Xd, vd, md, Ud, Vd)
+    assert torch.equal(Y1, Y2)
+    Xs = Xd[:16].contiguous()
+    Y3 = binding.linear(Xs, vd, md, Ud, Vd)
+    Y4 = binding.linear(Xs, vd, md, Ud, Vd)
+    assert torch.equal(Y3, Y4)
+
+
+def test_workspace_errors():
+    L = inputs.random_case(64, 256, 64, 32, "bf16", seed=1)
+    Xd, Ud, Vd = to_dev(L.X, "bf16"), to_dev(L.U, "bf16"), to_dev(L.V, "bf16")
+    vd, md = binding.prune24_pack(to_dev(L.R, "bf16"))
+    need = binding.workspace_bytes(64, 64, 256, 32, torch.bfloat16)
+    assert need > 0
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(binding.SplrError) as e:
+        binding.linear(Xd, vd, md, Ud, Vd, workspace=small)
+    assert e.value.status == 6
