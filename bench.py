@@ -100,8 +100,8 @@ def main():
             ws_n = binding.workspace_bytes(L.M, L.n_out, L.n_in, L.r, tdt)
             s.append(dict(
                 R=R, X=to_dev(L.X), U=to_dev(L.U), V=to_dev(L.V),
-                values=torch.empty((L.n_out, L.n_in // 2), dtype=tdt, device=dev),
-                meta=torch.empty((L.n_out, L.n_in // 32), dtype=torch.int32, device=dev),
+                values=torch.empty((*binding.tiles(L.n_out, L.n_in), 64, 8), dtype=tdt, device=dev),
+                meta=torch.empty((*binding.tiles(L.n_out, L.n_in), 2, 16), dtype=torch.int32, device=dev),
                 Y=torch.empty((L.M, L.n_out), dtype=torch.float32, device=dev),
                 ws=torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)))
         sets.append(s)
@@ -119,8 +119,8 @@ def main():
             if ev is not None:
                 ev[1 + li].record(stream)
         for li, d in enumerate(s):
-            binding.linear(d["X"], d["values"], d["meta"], d["U"], d["V"], out=d["Y"], workspace=d["ws"],
-                           stream=stream)
+            binding.linear(d["X"], d["values"], d["meta"], d["U"], d["V"], n_out=d["Y"].shape[1], out=d["Y"],
+                           workspace=d["ws"], stream=stream)
             if ev is not None:
                 ev[1 + n_layers + li].record(stream)
 
@@ -225,7 +225,7 @@ def cpu_baseline(cfg, layers, dtype, flop_step, wbytes_step, decode, rows_arg):
         rows = min(rows, L.M)
         sel = np.linspace(0, L.M - 1, rows).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.linear(L.X, v, m, L.U, L.V, dtype, rows=sel)
+        oracle.linear(L.X, v, m, L.n_out, L.U, L.V, dtype, rows=sel)
         dt = time.perf_counter() - t0
         t_lin += dt * (L.M / rows)
         frac_rows.append(f"{L.name}: {rows}/{L.M} rows")

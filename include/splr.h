@@ -23,13 +23,19 @@
  *
  * Packed 2:4 layout (shared by every entry point)
  * -----------------------------------------------
- *  values [n_out][n_in/2] dtype  : the two kept entries of each group of four consecutive input
- *                                  columns, in ascending column order.
- *  meta   [n_out][n_in/32] uint32: group g of a row (columns 4g..4g+3) is described by the nibble
- *                                  (a | b << 2) stored at bits 4*(g % 8) of word g / 8, where
- *                                  a < b in {0,1,2,3} are the kept positions.  Valid nibbles:
- *                                  0x4 0x8 0xC 0x9 0xD 0xE.  Metadata not produced by
- *                                  splr_prune24_pack gives unspecified results (not checked).
+ * The pages fix no storage format; this one is laid out for gfx950's structured-sparse MFMA
+ * (v_smfmac_f32_16x16x64_bf16), so that one wave reads one operand fragment as 1 KiB of
+ * contiguous memory. S is cut into tiles of 16 rows x 64 input columns, TR = ceil(n_out/16) tile
+ * rows by TK = ceil(n_in/64) tile columns, tile (tr, tk) at index t = tr*TK + tk.
+ *  values: t-major, 64 slots of 8 entries per tile (TR*TK*512 entries of dtype). Row n, group g
+ *          (columns 4g..4g+3): gi = g % 16, slot L = n % 16 + 16*(gi / 4); its two kept entries,
+ *          in ascending column order, are entries 2*(gi % 4) and 2*(gi % 4)+1 of slot L.
+ *  meta:   t-major, 2 x 16 uint32 words per tile (TR*TK*32 words). Word (gi / 8)*16 + n % 16
+ *          of the tile holds the nibble (a | b << 2) of the group at bits 4*(gi % 8), where
+ *          a < b in {0,1,2,3} are the kept positions. Valid nibbles: 0x4 0x8 0xC 0x9 0xD 0xE.
+ *  Entries and nibbles outside the matrix (row padding n >= n_out, column padding k >= n_in)
+ *  are zero. splr_packed_bytes() gives both buffer sizes. Metadata not produced by
+ *  splr_prune24_pack gives unspecified results (it is not validated).
  */
 #ifndef SPLR_H_
 #define SPLR_H_
@@ -69,14 +75,21 @@ typedef enum {
  * infinities (by payload).  Equal magnitudes go to the lower column.  The result is bit-exact and
  * deterministic.
  *
- *   R      [n_out][n_in] dtype   input
- *   values [n_out][n_in/2] dtype output
- *   meta   [n_out][n_in/32] u32  output
+ *   R      [n_out][n_in] dtype, row-major       input
+ *   values, meta                               output, packed layout above (every entry written,
+ *                                              padding included)
  * Errors: NULL pointer -> SPLR_ERR_NULL; n_out < 1, n_in < 32 or n_in % 32 != 0 -> SPLR_ERR_SHAPE;
  *         bad dtype -> SPLR_ERR_DTYPE; misaligned pointer -> SPLR_ERR_ALIGN.
  */
 splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr_dtype_t dtype,
                                 void* values, uint32_t* meta, hipStream_t stream);
+
+/*
+ * splr_packed_bytes -- sizes of the packed values and metadata buffers for an n_out x n_in S.
+ * Returns SPLR_ERR_SHAPE / SPLR_ERR_DTYPE / SPLR_ERR_NULL like the other entry points.
+ */
+splr_status_t splr_packed_bytes(int64_t n_out, int64_t n_in, splr_dtype_t dtype, size_t* values_bytes,
+                                size_t* meta_bytes);
 
 /*
  * splr_linear_workspace_bytes -- device workspace that splr_linear needs for these sizes
@@ -89,7 +102,7 @@ size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64
  * splr_linear -- Y = X S^T + (X V^T) U^T  (LoSparse §3.2: both products, summed).
  *
  *   X      [M][n_in] dtype                       activations
- *   values [n_out][n_in/2] dtype, meta [n_out][n_in/32] u32   packed S (layout above)
+ *   values, meta                                 packed S (layout above)
  *   U      [n_out][r] dtype, V [r][n_in] dtype   thin factors; both may be NULL iff r == 0
  *   Y      [M][n_out] float32                    output, written once
  *   workspace / workspace_bytes                  device scratch of at least

@@ -5,6 +5,9 @@ package. It wraps `splr_oracle.c` (plain C, float64 sums in index order, OpenMP 
 outputs) through ctypes. It shares no code with the GPU library and never loads it.
 
 Conventions: "bf16" arrays are numpy uint16 bit patterns, "fp32" arrays numpy float32.
+Packed S is returned in its tiled layout (tiles of 16 rows x 64 input columns, see
+splr_oracle.c): values shaped (TR, TK, 64, 8) and meta (TR, TK, 2, 16) uint32, with
+TR = ceil(n_out / 16), TK = ceil(n_in / 64). `unpack` gives the logical per-group view.
 """
 from __future__ import annotations
 
@@ -43,6 +46,8 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         lib.splr_ref_prune24_pack.argtypes = [P, I64, I64, ctypes.c_int, P, P]
+        lib.splr_ref_unpack.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
+        lib.splr_ref_unpack.restype = ctypes.c_int
         lib.splr_ref_linear.argtypes = [P, I64, I64, P, P, I64, P, P, I64, ctypes.c_int, P, I64, P]
         lib.splr_ref_dense_reconstruct.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P]
         for f in (lib.splr_ref_prune24_pack, lib.splr_ref_linear, lib.splr_ref_dense_reconstruct):
@@ -62,28 +67,51 @@ def _check(a: np.ndarray, dtype: str, ndim: int, name: str) -> np.ndarray:
     return a
 
 
+def tiles(n_out: int, n_in: int) -> Tuple[int, int]:
+    """(TR, TK): tile rows and tile columns of the packed layout."""
+    return (n_out + 15) // 16, (n_in + 63) // 64
+
+
 def prune24_pack(R: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
-    """2:4 projection of R [n_out x n_in] -> (values [n_out x n_in/2], meta uint32 [n_out x n_in/32])."""
+    """2:4 projection of R [n_out x n_in] -> (values (TR, TK, 64, 8), meta uint32 (TR, TK, 2, 16))."""
     R = _check(R, dtype, 2, "R")
     n_out, n_in = R.shape
-    values = np.empty((n_out, n_in // 2), dtype=_NP[dtype])
-    meta = np.empty((n_out, n_in // 32), dtype=np.uint32)
+    TR, TK = tiles(n_out, n_in)
+    values = np.empty((TR, TK, 64, 8), dtype=_NP[dtype])
+    meta = np.empty((TR, TK, 2, 16), dtype=np.uint32)
     rc = _load().splr_ref_prune24_pack(_ptr(R), n_out, n_in, _DT[dtype], _ptr(values), _ptr(meta))
     if rc:
         raise ValueError(f"splr_ref_prune24_pack failed ({rc}) for shape {R.shape}")
     return values, meta
 
 
-def linear(X: np.ndarray, values: np.ndarray, meta: np.ndarray, U: Optional[np.ndarray],
+def _check_packed(values, meta, n_out, n_in, dtype):
+    TR, TK = tiles(n_out, n_in)
+    values = _check(values, dtype, 4, "values")
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    if values.shape != (TR, TK, 64, 8) or meta.shape != (TR, TK, 2, 16):
+        raise ValueError(f"packed shapes {values.shape} {meta.shape} do not match {n_out} x {n_in}")
+    return values, meta
+
+
+def unpack(values: np.ndarray, meta: np.ndarray, n_out: int, n_in: int, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Logical view: kept [n_out x n_in/2] (the two kept entries of each group, in order) and the
+    nibble (a | b << 2) of every group, uint8 [n_out x n_in/4]."""
+    values, meta = _check_packed(values, meta, n_out, n_in, dtype)
+    kept = np.empty((n_out, n_in // 2), dtype=_NP[dtype])
+    nib = np.empty((n_out, n_in // 4), dtype=np.uint8)
+    rc = _load().splr_ref_unpack(_ptr(values), _ptr(meta), n_out, n_in, _DT[dtype], _ptr(kept), _ptr(nib))
+    if rc:
+        raise ValueError(f"splr_ref_unpack failed ({rc})")
+    return kept, nib
+
+
+def linear(X: np.ndarray, values: np.ndarray, meta: np.ndarray, n_out: int, U: Optional[np.ndarray],
            V: Optional[np.ndarray], dtype: str, rows: Optional[np.ndarray] = None) -> np.ndarray:
     """float64 Y = X S^T + (X V^T) U^T for all token rows, or only for `rows` (in that order)."""
     X = _check(X, dtype, 2, "X")
-    values = _check(values, dtype, 2, "values")
-    meta = np.ascontiguousarray(meta, dtype=np.uint32)
     M, n_in = X.shape
-    n_out = values.shape[0]
-    if values.shape[1] * 2 != n_in or meta.shape != (n_out, n_in // 32):
-        raise ValueError("values/meta do not match X")
+    values, meta = _check_packed(values, meta, n_out, n_in, dtype)
     r = 0 if U is None else U.shape[1]
     if r:
         U = _check(U, dtype, 2, "U")
@@ -103,14 +131,10 @@ def linear(X: np.ndarray, values: np.ndarray, meta: np.ndarray, U: Optional[np.n
     return Y
 
 
-def dense_reconstruct(values: np.ndarray, meta: np.ndarray, U: Optional[np.ndarray],
+def dense_reconstruct(values: np.ndarray, meta: np.ndarray, n_out: int, n_in: int, U: Optional[np.ndarray],
                       V: Optional[np.ndarray], dtype: str) -> np.ndarray:
     """float64 W_hat = S + U V, S scattered from (values, meta)."""
-    values = _check(values, dtype, 2, "values")
-    meta = np.ascontiguousarray(meta, dtype=np.uint32)
-    n_out, n_in = values.shape[0], values.shape[1] * 2
-    if meta.shape != (n_out, n_in // 32):
-        raise ValueError("meta shape")
+    values, meta = _check_packed(values, meta, n_out, n_in, dtype)
     r = 0 if U is None else U.shape[1]
     if r:
         U = _check(U, dtype, 2, "U")

@@ -7,12 +7,17 @@
  * library.  Every sum is a sequential float64 loop in index order; OpenMP only splits independent
  * outputs between threads, so the result does not depend on the thread count.
  *
- * Layouts (row-major, contiguous):
- *   R, W_hat : [n_out][n_in]
- *   values   : [n_out][n_in/2]   the two kept entries of every group of 4, ascending index
- *   meta     : [n_out][n_in/32]  uint32; group g of a row has the nibble (a | b << 2) at bits
- *                                4*(g % 8) of word g / 8, a < b being the kept positions (0..3)
+ * Layouts (contiguous):
+ *   R, W_hat : [n_out][n_in] row-major
  *   X        : [M][n_in]   U : [n_out][r]   V : [r][n_in]   Y : [rows][n_out] (float64)
+ *   packed S : tiles of 16 rows x 64 input columns, tile (tr, tk) at index tr * TK + tk with
+ *              TR = ceil(n_out / 16), TK = ceil(n_in / 64). Row n, group g (columns 4g..4g+3)
+ *              has tile (n / 16, g / 16); within the tile gi = g % 16, q = gi / 4, slot
+ *              L = n % 16 + 16 q. Its two kept entries a < b (positions 0..3 in the group) are
+ *              values[((tile * 64 + L) * 8) + 2 (gi % 4) + {0, 1}], and its nibble (a | b << 2)
+ *              sits at bits 4 (gi % 8) of meta[(tile * 2 + gi / 8) * 16 + n % 16].
+ *              values holds TR * TK * 512 entries, meta TR * TK * 32 uint32 words; entries and
+ *              words outside the matrix (row or column padding) are zero.
  * dtype 0 = float32 storage, 1 = bfloat16 storage (uint16 bit patterns).
  *
  * Functions and the passages they follow:
@@ -71,6 +76,32 @@ static int outranks(const uint32_t key[4], int i, int j) {
   return key[i] > key[j] || (key[i] == key[j] && i < j);
 }
 
+/* ---- packed layout (see the header comment) ---- */
+static int64_t tiles_rows(int64_t n_out) { return (n_out + 15) / 16; }
+static int64_t tiles_cols(int64_t n_in) { return (n_in + 63) / 64; }
+
+/* index of kept slot s (0 or 1) of group g in row n */
+static size_t value_index(int64_t n, int64_t g, int s, int64_t n_in) {
+  const int64_t gi = g % 16, q = gi / 4;
+  const size_t tile = (size_t)(n / 16) * (size_t)tiles_cols(n_in) + (size_t)(g / 16);
+  return (tile * 64 + (size_t)(n % 16 + 16 * q)) * 8 + (size_t)(2 * (gi % 4) + s);
+}
+
+/* index of the metadata word holding group g of row n (nibble at bits 4 * (g % 8)) */
+static size_t meta_index(int64_t n, int64_t g, int64_t n_in) {
+  const int64_t gi = g % 16;
+  const size_t tile = (size_t)(n / 16) * (size_t)tiles_cols(n_in) + (size_t)(g / 16);
+  return (tile * 2 + (size_t)(gi / 8)) * 16 + (size_t)(n % 16);
+}
+
+size_t splr_ref_packed_values(int64_t n_out, int64_t n_in) {
+  return (size_t)tiles_rows(n_out) * (size_t)tiles_cols(n_in) * 512;
+}
+
+size_t splr_ref_packed_meta(int64_t n_out, int64_t n_in) {
+  return (size_t)tiles_rows(n_out) * (size_t)tiles_cols(n_in) * 32;
+}
+
 /*
  * 2:4 projection and pack.  For every row and every group of four consecutive input columns:
  * keep the entry that outranks the other three and the entry that outranks the remaining two,
@@ -83,10 +114,12 @@ int splr_ref_prune24_pack(const void *R, int64_t n_out, int64_t n_in, int dtype,
   if (!R || !values || !meta) return SPLR_REF_EINVAL;
   if (n_out < 0 || n_in < 0 || n_in % 32 != 0) return SPLR_REF_EINVAL;
   if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
-  const int64_t groups = n_in / 4, words = n_in / 32;
+  const int64_t groups = n_in / 4;
+  const size_t nv = splr_ref_packed_values(n_out, n_in), nm = splr_ref_packed_meta(n_out, n_in);
+  memset(values, 0, nv * (dtype == SPLR_REF_BF16 ? 2 : 4));
+  memset(meta, 0, nm * sizeof(uint32_t));
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < n_out; ++n) {
-    for (int64_t w = 0; w < words; ++w) meta[n * words + w] = 0;
     for (int64_t g = 0; g < groups; ++g) {
       const size_t base = (size_t)n * (size_t)n_in + 4 * (size_t)g;
       uint32_t key[4];
@@ -101,23 +134,41 @@ int splr_ref_prune24_pack(const void *R, int64_t n_out, int64_t n_in, int dtype,
       }
       const int a = first < second ? first : second;
       const int b = first < second ? second : first;
-      const size_t vi = (size_t)n * (size_t)(n_in / 2) + 2 * (size_t)g;
-      copy_elem(values, vi, R, base + a, dtype);
-      copy_elem(values, vi + 1, R, base + b, dtype);
-      meta[n * words + g / 8] |= (uint32_t)(a | (b << 2)) << (4 * (g % 8));
+      copy_elem(values, value_index(n, g, 0, n_in), R, base + a, dtype);
+      copy_elem(values, value_index(n, g, 1, n_in), R, base + b, dtype);
+      meta[meta_index(n, g, n_in)] |= (uint32_t)(a | (b << 2)) << (4 * (g % 8));
     }
   }
   return SPLR_REF_OK;
 }
 
-static void decode_nibble(const uint32_t *meta_row, int64_t g, int *a, int *b) {
-  const uint32_t nib = (meta_row[g / 8] >> (4 * (g % 8))) & 0xFu;
+static void decode_nibble(const uint32_t *meta, int64_t n, int64_t g, int64_t n_in, int *a, int *b) {
+  const uint32_t nib = (meta[meta_index(n, g, n_in)] >> (4 * (g % 8))) & 0xFu;
   *a = (int)(nib & 3u);
   *b = (int)(nib >> 2);
 }
 
 /*
- * Y[i][n] = sum_g ( X[m][4g+a] * values[n][2g] + X[m][4g+b] * values[n][2g+1] )
+ * The logical view of a packed matrix: kept[n][2g + s] (storage dtype) and the nibble of every
+ * group, nib[n][g].  Layout bookkeeping only; it takes no decision.
+ */
+int splr_ref_unpack(const void *values, const uint32_t *meta, int64_t n_out, int64_t n_in, int dtype,
+                    void *kept, uint8_t *nib) {
+  if (!values || !meta || !kept || !nib) return SPLR_REF_EINVAL;
+  if (n_out < 0 || n_in < 0 || n_in % 32 != 0) return SPLR_REF_EINVAL;
+  if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
+  const int64_t groups = n_in / 4;
+  for (int64_t n = 0; n < n_out; ++n)
+    for (int64_t g = 0; g < groups; ++g) {
+      for (int s = 0; s < 2; ++s)
+        copy_elem(kept, (size_t)n * (size_t)(n_in / 2) + 2 * (size_t)g + s, values, value_index(n, g, s, n_in), dtype);
+      nib[(size_t)n * (size_t)groups + g] = (uint8_t)((meta[meta_index(n, g, n_in)] >> (4 * (g % 8))) & 0xFu);
+    }
+  return SPLR_REF_OK;
+}
+
+/*
+ * Y[i][n] = sum_g ( X[m][4g+a] * S_a(n, g) + X[m][4g+b] * S_b(n, g) )
  *         + sum_j T[i][j] * U[n][j],      T[i][j] = sum_k X[m][k] * V[j][k],
  * for m = rows[i] (every m in 0..M-1 in order when rows is NULL), all in float64.
  * U and V may be NULL when r == 0.
@@ -132,7 +183,7 @@ int splr_ref_linear(const void *X, int64_t M, int64_t n_in, const void *values,
   if (!rows) n_rows = M;
   for (int64_t i = 0; i < (rows ? n_rows : 0); ++i)
     if (rows[i] < 0 || rows[i] >= M) return SPLR_REF_EINVAL;
-  const int64_t groups = n_in / 4, words = n_in / 32;
+  const int64_t groups = n_in / 4;
 
   double *xrows = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * (size_t)(n_in > 0 ? n_in : 1));
   double *T = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * (size_t)(r > 0 ? r : 1));
@@ -159,14 +210,12 @@ int splr_ref_linear(const void *X, int64_t M, int64_t n_in, const void *values,
   for (int64_t i = 0; i < n_rows; ++i)
     for (int64_t n = 0; n < n_out; ++n) {
       const double *x = xrows + i * n_in;
-      const uint32_t *mrow = meta + n * words;
-      const size_t vrow = (size_t)n * (size_t)(n_in / 2);
       double sparse = 0.0;
       for (int64_t g = 0; g < groups; ++g) {
         int a, b;
-        decode_nibble(mrow, g, &a, &b);
-        sparse += x[4 * g + a] * load_f64(values, dtype, vrow + 2 * (size_t)g);
-        sparse += x[4 * g + b] * load_f64(values, dtype, vrow + 2 * (size_t)g + 1);
+        decode_nibble(meta, n, g, n_in, &a, &b);
+        sparse += x[4 * g + a] * load_f64(values, dtype, value_index(n, g, 0, n_in));
+        sparse += x[4 * g + b] * load_f64(values, dtype, value_index(n, g, 1, n_in));
       }
       double lowrank = 0.0;
       for (int64_t j = 0; j < r; ++j) lowrank += T[i * r + j] * load_f64(U, dtype, (size_t)n * (size_t)r + j);
@@ -188,17 +237,16 @@ int splr_ref_dense_reconstruct(const void *values, const uint32_t *meta, const v
   if (r > 0 && (!U || !V)) return SPLR_REF_EINVAL;
   if (n_out < 0 || n_in < 0 || n_in % 32 != 0 || r < 0) return SPLR_REF_EINVAL;
   if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
-  const int64_t groups = n_in / 4, words = n_in / 32;
+  const int64_t groups = n_in / 4;
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < n_out; ++n) {
     double *w = W_hat + n * n_in;
     for (int64_t k = 0; k < n_in; ++k) w[k] = 0.0;
     for (int64_t g = 0; g < groups; ++g) {
       int a, b;
-      decode_nibble(meta + n * words, g, &a, &b);
-      const size_t vi = (size_t)n * (size_t)(n_in / 2) + 2 * (size_t)g;
-      w[4 * g + a] = load_f64(values, dtype, vi);
-      w[4 * g + b] = load_f64(values, dtype, vi + 1);
+      decode_nibble(meta, n, g, n_in, &a, &b);
+      w[4 * g + a] = load_f64(values, dtype, value_index(n, g, 0, n_in));
+      w[4 * g + b] = load_f64(values, dtype, value_index(n, g, 1, n_in));
     }
     for (int64_t k = 0; k < n_in; ++k) {
       double lowrank = 0.0;

@@ -5,7 +5,10 @@ HIP stream; every step of the computation runs in the library's kernels. There i
 if the library is missing or a call fails, an exception is raised.
 
 Conventions: bf16 tensors are torch.bfloat16, fp32 tensors torch.float32; metadata is int32
-(the bits of the library's uint32 words).
+(the bits of the library's uint32 words). Packed S uses the library's tiled layout (16 rows x 64
+input columns per tile, see include/splr.h): values are shaped (TR, TK, 64, 8) and metadata
+(TR, TK, 2, 16), TR = ceil(n_out / 16), TK = ceil(n_in / 64). The layer's n_out is passed
+explicitly where it cannot be read off U.
 """
 from __future__ import annotations
 
@@ -21,8 +24,8 @@ LIB_PATH = os.path.join(_PKG, "libsplr.so")
 SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
-EXPORTS = ("splr_prune24_pack", "splr_linear_workspace_bytes", "splr_linear", "splr_dense_reconstruct",
-           "splr_status_string", "splr_version")
+EXPORTS = ("splr_prune24_pack", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
+           "splr_dense_reconstruct", "splr_status_string", "splr_version")
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 _lib = None
@@ -43,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.splr_prune24_pack.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P]
         L.splr_prune24_pack.restype = _I32
+        L.splr_packed_bytes.argtypes = [_I64, _I64, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
+        L.splr_packed_bytes.restype = _I32
         L.splr_linear_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32]
         L.splr_linear_workspace_bytes.restype = _SZ
         L.splr_linear.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P, _SZ, _P]
@@ -85,14 +90,27 @@ def _check(fn: str, status: int):
         raise SplrError(fn, status)
 
 
+def tiles(n_out: int, n_in: int) -> Tuple[int, int]:
+    return (n_out + 15) // 16, (n_in + 63) // 64
+
+
+def packed_bytes(n_out: int, n_in: int, dtype: torch.dtype) -> Tuple[int, int]:
+    """(values bytes, metadata bytes) of the packed layout, as the library reports them."""
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    code = SPLR_BF16 if dtype == torch.bfloat16 else SPLR_FP32
+    _check("splr_packed_bytes", lib().splr_packed_bytes(n_out, n_in, code, ctypes.byref(vb), ctypes.byref(mb)))
+    return vb.value, mb.value
+
+
 def prune24_pack(R: torch.Tensor, values: Optional[torch.Tensor] = None, meta: Optional[torch.Tensor] = None,
                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """2:4 projection + pack of R [n_out, n_in] -> (values [n_out, n_in/2], meta int32 [n_out, n_in/32])."""
+    """2:4 projection + pack of R [n_out, n_in] -> (values (TR, TK, 64, 8), meta int32 (TR, TK, 2, 16))."""
     n_out, n_in = R.shape
+    TR, TK = tiles(n_out, n_in)
     if values is None:
-        values = torch.empty((n_out, n_in // 2), dtype=R.dtype, device=R.device)
+        values = torch.empty((TR, TK, 64, 8), dtype=R.dtype, device=R.device)
     if meta is None:
-        meta = torch.empty((n_out, max(n_in // 32, 0)), dtype=torch.int32, device=R.device)
+        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
     _check("splr_prune24_pack", lib().splr_prune24_pack(_dev(R, "R"), n_out, n_in, _dtype_code(R),
                                                         _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
     return values, meta
@@ -104,11 +122,12 @@ def workspace_bytes(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype) -
 
 
 def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
-           V: Optional[torch.Tensor], out: Optional[torch.Tensor] = None,
+           V: Optional[torch.Tensor], n_out: Optional[int] = None, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Y [M, n_out] float32 = X S^T + (X V^T) U^T."""
+    """Y [M, n_out] float32 = X S^T + (X V^T) U^T (n_out defaults to U's rows, else 16 * TR)."""
     M, n_in = X.shape
-    n_out = values.shape[0]
+    if n_out is None:
+        n_out = U.shape[0] if U is not None else values.shape[0] * 16
     r = 0 if U is None else U.shape[1]
     if out is None:
         out = torch.empty((M, n_out), dtype=torch.float32, device=X.device)
@@ -123,9 +142,13 @@ def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optiona
 
 
 def dense_reconstruct(values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
-                      V: Optional[torch.Tensor], out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """W_hat [n_out, n_in] float32 = S + U V."""
-    n_out, n_in = values.shape[0], values.shape[1] * 2
+                      V: Optional[torch.Tensor], n_out: Optional[int] = None, n_in: Optional[int] = None,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """W_hat [n_out, n_in] float32 = S + U V (sizes default to U / V's, else to the tile grid)."""
+    if n_out is None:
+        n_out = U.shape[0] if U is not None else values.shape[0] * 16
+    if n_in is None:
+        n_in = V.shape[1] if V is not None else values.shape[1] * 64
     r = 0 if U is None else U.shape[1]
     if out is None:
         out = torch.empty((n_out, n_in), dtype=torch.float32, device=values.device)

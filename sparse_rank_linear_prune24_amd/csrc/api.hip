@@ -33,9 +33,9 @@ splr_status_t check_rank(int64_t r) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t workspace_bytes(int64_t M, int64_t n_in, int64_t r, splr_dtype_t dtype) {
+  (void)n_in;
   if (r == 0) return 0;
-  const int ks = splr::lowrank_ksplit(M, n_in, r, dtype == SPLR_BF16);
-  return round_up((size_t)ks * (size_t)M * (size_t)r * sizeof(float), 256);
+  return round_up(splr::lowrank_workspace_bytes(M, r, dtype == SPLR_BF16), 256);
 }
 
 splr_status_t from_hip(hipError_t e) { return e == hipSuccess ? SPLR_OK : SPLR_ERR_HIP; }
@@ -53,6 +53,19 @@ splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
   if (!aligned16(R) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
   return from_hip(splr::launch_prune24_pack(R, n_out, n_in, dtype == SPLR_BF16, values, meta, stream));
+}
+
+splr_status_t splr_packed_bytes(int64_t n_out, int64_t n_in, splr_dtype_t dtype, size_t* values_bytes,
+                                size_t* meta_bytes) {
+  if (!values_bytes || !meta_bytes) return SPLR_ERR_NULL;
+  splr_status_t s = check_in(n_in);
+  if (s == SPLR_OK) s = check_rows(n_out, n_in);
+  if (s != SPLR_OK) return s;
+  if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  const size_t tiles = (size_t)((n_out + 15) / 16) * (size_t)((n_in + 63) / 64);
+  *values_bytes = tiles * 512 * (dtype == SPLR_BF16 ? 2 : 4);
+  *meta_bytes = tiles * 32 * sizeof(uint32_t);
+  return SPLR_OK;
 }
 
 size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64_t r, splr_dtype_t dtype) {
@@ -81,11 +94,11 @@ splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* va
 
   const bool bf16 = dtype == SPLR_BF16;
   float* T = static_cast<float*>(workspace);
-  const int ks = splr::lowrank_ksplit(M, n_in, r, bf16);
-  hipError_t e = splr::launch_lowrank(X, V, M, n_in, r, bf16, ks, T, stream);
+  hipError_t e = splr::launch_lowrank(X, V, M, n_in, r, bf16, workspace, stream);
   if (e != hipSuccess) return SPLR_ERR_HIP;
   if (bf16)
-    e = splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, T, ks, Y, stream);
+    e = splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, (const uint16_t*)workspace,
+                                 (const uint16_t*)workspace + (size_t)M * r, Y, stream);
   else
     e = splr::launch_linear_f32((const float*)X, M, n_in, (const float*)values, meta, n_out, (const float*)U, r, T,
                                 Y, stream);

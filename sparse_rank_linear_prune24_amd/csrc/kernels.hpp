@@ -10,16 +10,16 @@ namespace splr {
 hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
                                uint32_t* meta, hipStream_t stream);
 
-// First low-rank stage T = X V^T, float32, written as `ksplit` partial sums over disjoint K ranges:
-// Tpart[s][m][j] for s < ksplit (plane stride M * r floats).
-int lowrank_ksplit(int64_t M, int64_t n_in, int64_t r, bool bf16);
+// First low-rank stage T = X V^T, written at the start of the workspace: float32 [M][r] for the
+// fp32 path; for the bf16 path a bfloat16 pair, hi [M][r] then lo [M][r] (T ~= hi + lo).
+size_t lowrank_workspace_bytes(int64_t M, int64_t r, bool bf16);
 hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16,
-                          int ksplit, float* Tpart, hipStream_t stream);
+                          void* workspace, hipStream_t stream);
 
-// Y = X S^T + T U^T with T given as `ksplit` float32 partials (r == 0: no low-rank term).
+// Y = X S^T + T U^T with T = Thi + Tlo (bfloat16 planes [M][r]; r == 0: no low-rank term).
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int ksplit, float* Y,
-                              hipStream_t stream);
+                              int64_t n_out, const void* U, int64_t r, const uint16_t* Thi, const uint16_t* Tlo,
+                              float* Y, hipStream_t stream);
 hipError_t launch_linear_f32(const float* X, int64_t M, int64_t n_in, const float* values, const uint32_t* meta,
                              int64_t n_out, const float* U, int64_t r, const float* T, float* Y,
                              hipStream_t stream);

@@ -2,71 +2,94 @@
 // §3.2: the sparse product and the low-rank product are evaluated side by side and summed).
 //
 // The sparse product runs on gfx950's structured-sparse MFMA, v_smfmac_f32_16x16x64_bf16, as
-// Y^T tiles = S_tile * X_tile^T: S is the sparse A operand (16 rows x 64 columns, stored as the 32
-// kept values), X^T the dense B operand. The packed layout feeds it without conversion: a lane's
-// A operand is 8 consecutive kept values of one row (16 bytes), and its index operand is the 16
-// metadata bits of the same 4 groups, i.e. one half of a metadata word.
-// Lane layouts (gfx950):
-//   A (S):  lane l -> row l%16, dense columns 16*(l/16) .. +15  (kept values 8*(l/16) .. +7)
+// Y^T tiles = S_tile * X_tile^T: S is the sparse A operand, X^T the dense B operand. Lane layouts:
+//   A (S):  lane l -> row l%16, dense columns 16*(l/16) .. +15 (kept values 8*(l/16) .. +7), index
+//           operand = the 4 nibbles of those groups in bits [15:0]
 //   B (X):  lane l -> token l%16, columns 8*(l/16)+0..7 and 32+8*(l/16)+0..7
 //   D:      lane l -> rows (n) 4*(l/16)+0..3, token l%16
-// The low-rank epilogue uses dense v_mfma_f32_16x16x32_bf16, whose D layout is the same, so it
-// accumulates into the same registers: acc += U_tile * T_tile^T, with T (float32) split into a
-// bfloat16 high part and a bfloat16 correction. Y is stored once.
+// The packed layout stores each 16-row x 64-column tile in exactly this A order, so a wave reads
+// its S fragment as 1 KiB of contiguous memory and its metadata as 128 contiguous bytes. X is
+// row-major: it is loaded with row-contiguous (coalesced) 16-byte loads and staged in LDS with a
+// padded 144-byte row pitch, from which the B fragments are read without bank conflicts.
 //
-// Two kernels:
-//   prefill -- WG tile BN x BM, both operands staged through LDS in fragment order (each lane's
-//              16-byte pieces contiguous, so every LDS read is a conflict-free 1 KiB wave read),
-//              double-buffered, one barrier per 64-column K step; workgroups are remapped so the
-//              tiles that one XCD (own L2) runs share rows of X and S.
-//   decode  -- few tokens: HBM-bound on S. A workgroup owns 16 rows of S; its waves take
-//              interleaved 64-column K steps, stream S and its metadata straight into registers
-//              (several steps of loads in flight), read X from L2, and combine their partial
-//              accumulators through LDS in a fixed order.
+// The rank-r term is folded into the same accumulators in the epilogue with the same instruction:
+// dense U is the sum of two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of every group
+// of four ranks), so acc += U_tile T_tile^T is two structured-sparse MFMAs per 64 ranks with
+// constant index operands. T (float32) enters as a bfloat16 high part plus a bfloat16 correction.
+// Y is stored once.
+//
+// Kernels:
+//   prefill -- workgroup tile 16*NI*4 rows x 16*NJ tokens, 4 waves, each owning 16*NI rows and all
+//              tokens, so every S fragment is used by one wave and goes global -> registers; X is
+//              shared through a two-slot LDS ring; P K steps of loads in flight; one barrier per
+//              K step; workgroups remapped so the tiles that one XCD (own L2) runs share X and S.
+//   decode  -- few tokens: HBM-bound on S. A workgroup owns 16 rows; its 4 waves take interleaved
+//              64-column K steps, stream S straight into registers and X through a private LDS
+//              slot each, and combine their partial accumulators through LDS in a fixed order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace splr {
 namespace {
 
-// ---------------------------------------------------------------------------------------- shared
+// LDS row pitch of staged X in 16-byte units (128 bytes + 32 pad). With this pitch the B-fragment
+// reads (16 rows x one 16-byte chunk per quarter wave) run at the full ds_read_b128 rate on gfx950;
+// a 16-byte pad leaves them 2-way bank conflicted.
+constexpr int kXPitchU4 = 10;
 
-// Low-rank epilogue for one 16x16 accumulator block set.
-// acc[i][j] (rows n = nrow0 + 16 i, tokens m = mrow0 + 16 j) += U[n][:] . T[m][:]
+// LDS writes of this wave complete, then workgroup barrier. One asm statement with a memory
+// clobber: the compiler moves no LDS access across it, and (unlike __syncthreads(), whose fence
+// drains every outstanding global load) it leaves the register prefetches in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ----------------------------------------------------------------------------------- epilogue
+
+// acc[i][j] (rows n = nrow0 + 16 i + ..., tokens m = mrow0 + 16 j + ...) += U[n][:] . T[m][:], with
+// T = Thi + Tlo given as two bfloat16 planes [M][r]. All fragments of a 64-rank block are loaded
+// before its MFMAs.
 template <int NI, int NJ>
 __device__ __forceinline__ void lowrank_epilogue(f32x4_t (&acc)[NI][NJ], const uint16_t* __restrict__ U,
-                                                 const float* __restrict__ Tpart, int ksplit, int M, int n_out,
-                                                 int r, int nrow0, int mrow0, int lane) {
-  const int sub = lane & 15, koff = 8 * (lane >> 4);
-  const size_t plane = (size_t)M * r;
-  for (int j0 = 0; j0 < r; j0 += 32) {
-    const int jj = j0 + koff;
-    const bool j_ok = jj < r;  // r % 16 == 0: a lane's 8 ranks are all valid or all past the end
-    bf16x8_t thi[NJ], tlo[NJ];
+                                                 const uint16_t* __restrict__ Thi, const uint16_t* __restrict__ Tlo,
+                                                 int M, int n_out, int r, int nrow0, int mrow0, int lane) {
+  const int sub = lane & 15, quad = lane >> 4;
+  const u32x4_t zero = {0, 0, 0, 0};
+  for (int j0 = 0; j0 < r; j0 += 64) {
+    // B operand: T[m][j0 + 8q .. +7] and T[m][j0 + 32 + 8q .. +7]
+    const int ja = j0 + 8 * quad, jb = j0 + 32 + 8 * quad;
+    u32x4_t th[NJ][2], tl[NJ][2];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int m = mrow0 + 16 * j + sub;
-      float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (m < M && j_ok) {
-        const float* p = Tpart + (size_t)m * r + jj;
-        for (int s = 0; s < ksplit; ++s) {
-          const f32x4_t a = *(const f32x4_t*)(p + s * plane);
-          const f32x4_t b = *(const f32x4_t*)(p + s * plane + 4);
-          t[0] += a[0]; t[1] += a[1]; t[2] += a[2]; t[3] += a[3];
-          t[4] += b[0]; t[5] += b[1]; t[6] += b[2]; t[7] += b[3];
-        }
-      }
-      split_hi_lo(t, thi[j], tlo[j]);
+      const size_t row = (size_t)min(mrow0 + 16 * j + sub, M - 1) * r;
+      th[j][0] = ja < r ? *(const u32x4_t*)(Thi + row + ja) : zero;
+      th[j][1] = jb < r ? *(const u32x4_t*)(Thi + row + jb) : zero;
+      tl[j][0] = ja < r ? *(const u32x4_t*)(Tlo + row + ja) : zero;
+      tl[j][1] = jb < r ? *(const u32x4_t*)(Tlo + row + jb) : zero;
     }
+    // A operand: U[n][j0 + 16q .. +15] split into the (0,1) and (2,3) positions of each group
+    const int ju = j0 + 16 * quad;
+    u32x4_t ud[NI][2];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int n = nrow0 + 16 * i + sub;
-      const u32x4_t zero = {0, 0, 0, 0};
-      const bf16x8_t u = as_bf16x8((n < n_out && j_ok) ? *(const u32x4_t*)(U + (size_t)n * r + jj) : zero);
+      const bool ok = n < n_out && ju < r;
+      const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
+      ud[i][0] = ok ? *(const u32x4_t*)p : zero;
+      ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bf16x8_t u01 = as_bf16x8(u32x4_t{ud[i][0][0], ud[i][0][2], ud[i][1][0], ud[i][1][2]});
+      const bf16x8_t u23 = as_bf16x8(u32x4_t{ud[i][0][1], ud[i][0][3], ud[i][1][1], ud[i][1][3]});
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        acc[i][j] = mfma16x16x32(u, thi[j], acc[i][j]);
-        acc[i][j] = mfma16x16x32(u, tlo[j], acc[i][j]);
+        const bf16x16_t thi = cat16(as_bf16x8(th[j][0]), as_bf16x8(th[j][1]));
+        const bf16x16_t tlo = cat16(as_bf16x8(tl[j][0]), as_bf16x8(tl[j][1]));
+        acc[i][j] = smfmac16x16x64(u01, thi, acc[i][j], 0x4444);
+        acc[i][j] = smfmac16x16x64(u23, thi, acc[i][j], 0xEEEE);
+        acc[i][j] = smfmac16x16x64(u01, tlo, acc[i][j], 0x4444);
+        acc[i][j] = smfmac16x16x64(u23, tlo, acc[i][j], 0xEEEE);
       }
     }
   }
@@ -96,213 +119,222 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], float* 
   }
 }
 
-// ---------------------------------------------------------------------------------------- prefill
+// ----------------------------------------------------------------------------------- prefill
 
-template <int BN, int BM, int WN, int WM>
-struct PrefillCfg {
-  static constexpr int kWavesN = BN / WN, kWavesM = BM / WM;
-  static constexpr int kThreads = 64 * kWavesN * kWavesM;
-  static constexpr int NI = WN / 16, NJ = WM / 16;
-  // LDS stage, in 16-byte units: A fragments (BN/16 x 64 lanes), X fragments (BM/16 x 2 x 64),
-  // then metadata (BN rows x 2 words = BN/2 units).
-  static constexpr int kAUnits = BN * 4;
-  static constexpr int kXUnits = BM * 8;
-  static constexpr int kMUnits = BN / 2;
-  static constexpr int kStageUnits = kAUnits + kXUnits + kMUnits;
-  static constexpr int kAChunksPerThread = (kAUnits + kThreads - 1) / kThreads;
-  static constexpr int kXChunksPerThread = (kXUnits + kThreads - 1) / kThreads;
-  static constexpr int kMWordsPerThread = (BN * 2 + kThreads - 1) / kThreads;
-};
+template <int NI, int NJ, int P>
+__global__ __launch_bounds__(256) void linear_prefill_kernel(
+    const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
+    const uint16_t* __restrict__ U, const uint16_t* __restrict__ Thi, const uint16_t* __restrict__ Tlo,
+    float* __restrict__ Y, int M, int K, int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
+  constexpr int WAVES = 4;
+  constexpr int BN = 16 * NI * WAVES;
+  constexpr int BM = 16 * NJ;
+  constexpr int kXLoads = BM / (8 * WAVES);  // X load instructions per wave per step (8 tokens each)
+  static_assert(BM % (8 * WAVES) == 0, "X stage must split evenly over the waves");
+  static_assert(P % 2 == 0, "the prefetch distance is also the unroll factor; it must be even");
+  // the two LDS slots are separate objects, so the compiler may move reads of one past writes of
+  // the other
+  __shared__ u32x4_t xs0[BM * kXPitchU4];
+  __shared__ u32x4_t xs1[BM * kXPitchU4];
 
-template <int BN, int BM, int WN, int WM>
-__global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void linear_prefill_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, float* __restrict__ Y, int M, int K,
-    int n_out, int r, int ksplit, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
-  using C = PrefillCfg<BN, BM, WN, WM>;
-  __shared__ u32x4_t lds[2 * C::kStageUnits];
-
-  // --- XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a contiguous range of
-  // logical tiles, and walk logical tiles in groups of `group_m` token tiles so that the tiles of
-  // one XCD share X rows and S rows.
+  // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a contiguous range of
+  // logical tiles, walked in groups of `group_m` token tiles, so its tiles share X and S rows.
   const int b = blockIdx.x;
   const int logical = (b & 7) * tiles_per_xcd + (b >> 3);
-  const int n_tiles = tiles_n * tiles_m;
-  if (logical >= n_tiles) return;
+  if (logical >= tiles_n * tiles_m) return;
   const int per_group = group_m * tiles_n;
   const int g = logical / per_group;
   const int first_m = g * group_m;
   const int gsize = min(group_m, tiles_m - first_m);
   const int in_group = logical - g * per_group;
-  const int tile_m = first_m + in_group % gsize;
-  const int tile_n = in_group / gsize;
-  const int n0 = tile_n * BN, m0 = tile_m * BM;
+  const int m0 = (first_m + in_group % gsize) * BM;
+  const int n0 = (in_group / gsize) * BN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % C::kWavesN, wm = wave / C::kWavesN;
-  const int Kc = K / 2;          // kept values per row
-  const int Kw = K / 32;         // metadata words per row
-  const int nk = (K + 63) / 64;  // 64-column K steps (the last may be half)
-
-  // global -> register staging for one K step
-  u32x4_t ra[C::kAChunksPerThread], rx[C::kXChunksPerThread];
-  uint32_t rm[C::kMWordsPerThread];
-  const u32x4_t zero = {0, 0, 0, 0};
-
-  auto load_stage = [&](int kc) {
-#pragma unroll
-    for (int c = 0; c < C::kAChunksPerThread; ++c) {
-      const int q = tid + c * C::kThreads;
-      const int row = q >> 2, part = q & 3;
-      const int n = n0 + row;
-      const int kv = kc * 32 + part * 8;  // kept-value column
-      ra[c] = (q < C::kAUnits && n < n_out && kv < Kc) ? *(const u32x4_t*)(values + (size_t)n * Kc + kv) : zero;
-    }
-#pragma unroll
-    for (int c = 0; c < C::kXChunksPerThread; ++c) {
-      const int q = tid + c * C::kThreads;
-      const int row = q >> 3, part = q & 7;
-      const int m = m0 + row;
-      const int k = kc * 64 + part * 8;
-      rx[c] = (q < C::kXUnits && m < M && k < K) ? *(const u32x4_t*)(X + (size_t)m * K + k) : zero;
-    }
-#pragma unroll
-    for (int c = 0; c < C::kMWordsPerThread; ++c) {
-      const int q = tid + c * C::kThreads;
-      const int row = q >> 1, w = q & 1;
-      const int n = n0 + row;
-      const int kw = kc * 2 + w;
-      rm[c] = (q < BN * 2 && n < n_out && kw < Kw) ? meta[(size_t)n * Kw + kw] : 0u;
-    }
-  };
-  auto store_stage = [&](int buf) {
-    u32x4_t* st = lds + buf * C::kStageUnits;
-#pragma unroll
-    for (int c = 0; c < C::kAChunksPerThread; ++c) {
-      const int q = tid + c * C::kThreads;
-      if (q < C::kAUnits) {
-        const int row = q >> 2, part = q & 3;
-        st[(row >> 4) * 64 + (row & 15) + 16 * part] = ra[c];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < C::kXChunksPerThread; ++c) {
-      const int q = tid + c * C::kThreads;
-      if (q < C::kXUnits) {
-        const int row = q >> 3, part = q & 7;
-        st[C::kAUnits + ((row >> 4) * 2 + (part >> 2)) * 64 + (row & 15) + 16 * (part & 3)] = rx[c];
-      }
-    }
-    uint32_t* sm = (uint32_t*)(st + C::kAUnits + C::kXUnits);
-#pragma unroll
-    for (int c = 0; c < C::kMWordsPerThread; ++c) {
-      const int q = tid + c * C::kThreads;
-      if (q < BN * 2) sm[q] = rm[c];
-    }
-  };
-
-  f32x4_t acc[C::NI][C::NJ];
-#pragma unroll
-  for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & 15, quad = lane >> 4;
-  for (int kc = 0; kc < nk; ++kc) {
-    const int cur = kc & 1;
-    if (kc + 1 < nk) load_stage(kc + 1);
-    const u32x4_t* st = lds + cur * C::kStageUnits;
-    const uint32_t* sm = (const uint32_t*)(st + C::kAUnits + C::kXUnits);
-    bf16x8_t a[C::NI];
-    int idx[C::NI];
+  const int TK = (K + 63) / 64, TR = (n_out + 15) / 16;
+  const int nk_pad = (TK + P - 1) / P * P;
+
+  // S fragments of this wave: tile rows (clamped; rows past n_out are zero padding or unused)
+  const u32x4_t* vsrc[NI];
+  const uint16_t* msrc[NI];  // this lane's 16 index bits: half (quad & 1) of its metadata word
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i) {
-      const int rowblk = wn * C::NI + i;
-      a[i] = as_bf16x8(st[rowblk * 64 + lane]);
-      const uint32_t w = sm[(rowblk * 16 + sub) * 2 + (quad >> 1)];
-      idx[i] = (int)(w >> (16 * (quad & 1)));
-    }
+  for (int i = 0; i < NI; ++i) {
+    const int tr = min(n0 / 16 + wave * NI + i, TR - 1);
+    vsrc[i] = values + (size_t)tr * TK * 64 + lane;
+    msrc[i] = (const uint16_t*)(meta + (size_t)tr * TK * 32 + sub + 16 * (quad >> 1)) + (quad & 1);
+  }
+  // X rows this lane loads: token m0 + wave*BM/4 + 8 t + lane/8, 16-byte chunk lane%8 of a step
+  const int xchunk = lane & 7;
+  const uint16_t* xsrc[kXLoads];
+  int xdst[kXLoads];
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-      const int colblk = wm * C::NJ + j;
-      const bf16x16_t bx = cat16(as_bf16x8(st[C::kAUnits + (colblk * 2) * 64 + lane]),
-                                 as_bf16x8(st[C::kAUnits + (colblk * 2 + 1) * 64 + lane]));
-#pragma unroll
-      for (int i = 0; i < C::NI; ++i) acc[i][j] = smfmac16x16x64(a[i], bx, acc[i][j], idx[i]);
-    }
-    if (kc + 1 < nk) store_stage(cur ^ 1);
-    __syncthreads();
+  for (int t = 0; t < kXLoads; ++t) {
+    const int tloc = wave * (BM / WAVES) + 8 * t + (lane >> 3);
+    xsrc[t] = X + (size_t)min(m0 + tloc, M - 1) * K + 8 * xchunk;
+    xdst[t] = tloc * kXPitchU4 + xchunk;
   }
 
-  const int nrow0 = n0 + wn * WN, mrow0 = m0 + wm * WM;
-  if (r > 0) lowrank_epilogue<C::NI, C::NJ>(acc, U, Tpart, ksplit, M, n_out, r, nrow0, mrow0, lane);
-  store_tile<C::NI, C::NJ>(acc, Y, M, n_out, nrow0, mrow0, lane);
+  constexpr int PX = 2;  // X register ring: X of step kc is loaded two steps before it goes to LDS
+  u32x4_t xr[PX][kXLoads];
+  u32x4_t sa[P][NI];
+  uint32_t sw[P][NI];  // index operands, zero-extended 16-bit loads
+  bf16x16_t bx[2][NJ];
+  auto load_x = [&](int kc, u32x4_t (&v)[kXLoads]) {
+    int col = min(kc, TK - 1) * 64;
+    if (col + 8 * xchunk >= K) col -= 32;  // half tail step: re-read valid columns (S is zero there)
+#pragma unroll
+    for (int t = 0; t < kXLoads; ++t) v[t] = *(const u32x4_t*)(xsrc[t] + col);
+  };
+  auto load_s = [&](int kc, u32x4_t (&va)[NI], uint32_t (&wa)[NI]) {
+    const int kk = min(kc, TK - 1);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      va[i] = vsrc[i][(size_t)kk * 64];
+      wa[i] = msrc[i][(size_t)kk * 64];
+    }
+  };
+  auto store_x = [&](u32x4_t* slot, const u32x4_t (&v)[kXLoads]) {
+#pragma unroll
+    for (int t = 0; t < kXLoads; ++t) slot[xdst[t]] = v[t];
+  };
+  auto read_b = [&](const u32x4_t* slot, bf16x16_t (&b)[NJ]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int row = (16 * j + sub) * kXPitchU4;
+      b[j] = cat16(as_bf16x8(slot[row + quad]), as_bf16x8(slot[row + 4 + quad]));
+    }
+  };
+  f32x4_t acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
+
+  // Software pipeline, one barrier per K step. At step kc (S register slot d = kc % P, parity
+  // b = kc % 2): the B fragments of step kc are already in registers bx[b] and X of step kc+1 is in
+  // LDS slot b^1. The step reads the B fragments of step kc+1 into bx[b^1] while its MFMAs run,
+  // refills S slot d with step kc+P, writes X of step kc+2 into LDS slot b (whose reads, of step kc,
+  // all completed before the previous barrier), reloads that X register slot with step kc+4, and
+  // ends with the barrier. Padding steps (kc >= TK) zero the S operand.
+  auto step = [&](int kc, auto dd, auto masked) {
+    constexpr int d = decltype(dd)::value;
+    constexpr int b = d & 1;
+    read_b(b ? xs0 : xs1, bx[b ^ 1]);
+    const uint32_t keep = (!decltype(masked)::value || kc < TK) ? ~0u : 0u;
+    bf16x8_t a[NI];
+    int idx[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      a[i] = decltype(masked)::value ? as_bf16x8(sa[d][i] & keep) : as_bf16x8(sa[d][i]);
+      idx[i] = (int)(sw[d][i] & keep);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[i][j] = smfmac16x16x64(a[i], bx[b][j], acc[i][j], idx[i]);
+    load_s(kc + P, sa[d], sw[d]);
+    store_x(b ? xs1 : xs0, xr[b]);
+    load_x(kc + 2 + PX, xr[b]);
+    lds_barrier();
+  };
+
+#pragma unroll
+  for (int d = 0; d < P; ++d) load_s(d, sa[d], sw[d]);
+  load_x(0, xr[0]);
+  load_x(1, xr[1]);
+  store_x(xs0, xr[0]);
+  store_x(xs1, xr[1]);
+  load_x(2, xr[0]);
+  load_x(3, xr[1]);
+  lds_barrier();
+  read_b(xs0, bx[0]);
+  lds_barrier();  // every wave's reads of slot 0 are done before step 0 overwrites it
+  const int nk_full = TK / P * P;  // steps that need no masking
+  for (int kc0 = 0; kc0 < nk_full; kc0 += P) {
+    step(kc0 + 0, std::integral_constant<int, 0>{}, std::false_type{});
+    step(kc0 + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    if constexpr (P >= 4) {
+      step(kc0 + 2, std::integral_constant<int, 2 % P>{}, std::false_type{});
+      step(kc0 + 3, std::integral_constant<int, 3 % P>{}, std::false_type{});
+    }
+  }
+  for (int kc0 = nk_full; kc0 < nk_pad; kc0 += P) {
+    step(kc0 + 0, std::integral_constant<int, 0>{}, std::true_type{});
+    step(kc0 + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    if constexpr (P >= 4) {
+      step(kc0 + 2, std::integral_constant<int, 2 % P>{}, std::true_type{});
+      step(kc0 + 3, std::integral_constant<int, 3 % P>{}, std::true_type{});
+    }
+  }
+
+  const int nrow0 = n0 + wave * 16 * NI;
+  if (r > 0) lowrank_epilogue<NI, NJ>(acc, U, Thi, Tlo, M, n_out, r, nrow0, m0, lane);
+  store_tile<NI, NJ>(acc, Y, M, n_out, nrow0, m0, lane);
 }
 
-// ---------------------------------------------------------------------------------------- decode
+// ----------------------------------------------------------------------------------- decode
 
-template <int KW, int MB, int UNROLL>
-__global__ __launch_bounds__(64 * KW) void linear_decode_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, float* __restrict__ Y, int M, int K,
-    int n_out, int r, int ksplit) {
-  __shared__ f32x4_t red[(KW - 1) * MB * 64];
+template <int MB, int P>
+__global__ __launch_bounds__(256) void linear_decode_kernel(
+    const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
+    const uint16_t* __restrict__ U, const uint16_t* __restrict__ Thi, const uint16_t* __restrict__ Tlo,
+    float* __restrict__ Y, int M, int K, int n_out, int r) {
+  constexpr int WAVES = 4;
+  constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
+  __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
+  __shared__ f32x4_t red[(WAVES - 1) * MB * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16 * MB;
   const int sub = lane & 15, quad = lane >> 4;
-  const int Kc = K / 2, Kw = K / 32;
-  const int nk = (K + 63) / 64;
+  const int tr = blockIdx.x, m0 = blockIdx.y * 16 * MB;
+  const int TK = (K + 63) / 64;
 
-  const int n = n0 + sub;
-  const bool n_ok = n < n_out;
-  const uint16_t* vrow = values + (size_t)(n_ok ? n : 0) * Kc + 8 * quad;
-  const uint32_t* mrow = meta + (size_t)(n_ok ? n : 0) * Kw + (quad >> 1);
-  const int mshift = 16 * (quad & 1);
-  const uint16_t* xrow[MB];
-  bool m_ok[MB];
+  const u32x4_t* vsrc = values + (size_t)tr * TK * 64 + lane;
+  const uint16_t* msrc = (const uint16_t*)(meta + (size_t)tr * TK * 32 + sub + 16 * (quad >> 1)) + (quad & 1);
+  const int xchunk = lane & 7;
+  const uint16_t* xsrc[kXLoads];
+  int xdst[kXLoads];
 #pragma unroll
-  for (int j = 0; j < MB; ++j) {
-    const int m = m0 + 16 * j + sub;
-    m_ok[j] = m < M;
-    xrow[j] = X + (size_t)(m_ok[j] ? m : 0) * K + 8 * quad;
+  for (int t = 0; t < kXLoads; ++t) {
+    const int tloc = 8 * t + (lane >> 3);
+    xsrc[t] = X + (size_t)min(m0 + tloc, M - 1) * K + 8 * xchunk;
+    xdst[t] = tloc * kXPitchU4 + xchunk;
   }
+  u32x4_t* st = xs[wave];
 
   f32x4_t acc[1][MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j) acc[0][j] = f32x4_t{0, 0, 0, 0};
-  const u32x4_t zero = {0, 0, 0, 0};
 
-  for (int kc0 = wave; kc0 < nk; kc0 += KW * UNROLL) {
-    u32x4_t av[UNROLL], xv[UNROLL][MB][2];
-    uint32_t mv[UNROLL];
+  // this wave's steps: kc = wave, wave + 4, ... ; P of them in flight
+  const int my_steps = (TK - wave + WAVES - 1) / WAVES;
+  for (int s0 = 0; s0 < my_steps; s0 += P) {
+    u32x4_t sa[P], xr[P][kXLoads];
+    uint32_t sw[P];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int kc = kc0 + u * KW;
-      const bool in = kc < nk;
-      const bool a_in = in && n_ok && kc * 32 + 8 * quad < Kc;
-      av[u] = a_in ? __builtin_nontemporal_load((const u32x4_t*)(vrow + (size_t)kc * 32)) : zero;
-      mv[u] = (in && n_ok && kc * 2 + (quad >> 1) < Kw) ? mrow[(size_t)kc * 2] : 0u;
+    for (int u = 0; u < P; ++u) {
+      const int kc = min(wave + (s0 + u) * WAVES, TK - 1);
+      sa[u] = vsrc[(size_t)kc * 64];
+      sw[u] = msrc[(size_t)kc * 64];
+      int col = kc * 64;
+      if (col + 8 * xchunk >= K) col -= 32;
 #pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        const size_t k = (size_t)kc * 64;
-        const bool x0 = in && m_ok[j] && (int)k + 8 * quad < K;
-        const bool x1 = in && m_ok[j] && (int)k + 32 + 8 * quad < K;
-        xv[u][j][0] = x0 ? *(const u32x4_t*)(xrow[j] + k) : zero;
-        xv[u][j][1] = x1 ? *(const u32x4_t*)(xrow[j] + k + 32) : zero;
-      }
+      for (int t = 0; t < kXLoads; ++t) xr[u][t] = *(const u32x4_t*)(xsrc[t] + col);
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int idx = (int)(mv[u] >> mshift);
+    for (int u = 0; u < P; ++u) {
+      const bool live = s0 + u < my_steps;  // wave-uniform
 #pragma unroll
-      for (int j = 0; j < MB; ++j)
-        acc[0][j] = smfmac16x16x64(as_bf16x8(av[u]), cat16(as_bf16x8(xv[u][j][0]), as_bf16x8(xv[u][j][1])),
-                                   acc[0][j], idx);
+      for (int t = 0; t < kXLoads; ++t) st[xdst[t]] = xr[u][t];
+      const uint32_t keep = live ? ~0u : 0u;
+      const bf16x8_t a = as_bf16x8(sa[u] & keep);
+      const int idx = (int)(sw[u] & keep);
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int row = (16 * j + sub) * kXPitchU4;
+        const bf16x16_t bx = cat16(as_bf16x8(st[row + quad]), as_bf16x8(st[row + 4 + quad]));
+        acc[0][j] = smfmac16x16x64(a, bx, acc[0][j], idx);
+      }
     }
   }
 
@@ -314,44 +346,44 @@ __global__ __launch_bounds__(64 * KW) void linear_decode_kernel(
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 1; w < KW; ++w)
+  for (int w = 1; w < WAVES; ++w)
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[0][j] += red[((w - 1) * MB + j) * 64 + lane];
 
-  if (r > 0) lowrank_epilogue<1, MB>(acc, U, Tpart, ksplit, M, n_out, r, n0, m0, lane);
-  store_tile<1, MB>(acc, Y, M, n_out, n0, m0, lane);
+  if (r > 0) lowrank_epilogue<1, MB>(acc, U, Thi, Tlo, M, n_out, r, tr * 16, m0, lane);
+  store_tile<1, MB>(acc, Y, M, n_out, tr * 16, m0, lane);
 }
 
 template <int MB>
 hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                         int64_t n_out, const void* U, int64_t r, const float* Tpart, int ksplit, float* Y,
-                         hipStream_t stream) {
-  constexpr int KW = 8, UNROLL = 2;
+                         int64_t n_out, const void* U, int64_t r, const uint16_t* Thi, const uint16_t* Tlo,
+                         float* Y, hipStream_t stream) {
+  constexpr int P = MB == 1 ? 8 : 4;
   dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(M, 16 * MB));
-  linear_decode_kernel<KW, MB, UNROLL><<<grid, dim3(64 * KW), 0, stream>>>(
-      (const uint16_t*)X, (const uint16_t*)values, meta, (const uint16_t*)U, Tpart, Y, (int)M, (int)n_in,
-      (int)n_out, (int)r, ksplit);
+  linear_decode_kernel<MB, P><<<grid, dim3(256), 0, stream>>>(
+      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Thi, Tlo, Y, (int)M, (int)n_in,
+      (int)n_out, (int)r);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int ksplit, float* Y,
-                              hipStream_t stream) {
-  if (M <= 16) return launch_decode<1>(X, M, n_in, values, meta, n_out, U, r, Tpart, ksplit, Y, stream);
-  if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Tpart, ksplit, Y, stream);
-  if (M <= kDecodeMaxTokens) return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Tpart, ksplit, Y, stream);
+                              int64_t n_out, const void* U, int64_t r, const uint16_t* Thi, const uint16_t* Tlo,
+                              float* Y, hipStream_t stream) {
+  if (M <= 16) return launch_decode<1>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
+  if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
+  if (M <= kDecodeMaxTokens) return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
 
-  constexpr int BN = 128, BM = 128, WN = 64, WM = 64;
-  using C = PrefillCfg<BN, BM, WN, WM>;
+  constexpr int NI = 4, NJ = 8, P = 4;
+  constexpr int BN = 16 * NI * 4, BM = 16 * NJ;
   const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
   const int n_tiles = tiles_n * tiles_m;
   const int per_xcd = (int)ceil_div(n_tiles, 8);
   const int group_m = 4;
-  linear_prefill_kernel<BN, BM, WN, WM><<<dim3((unsigned)(8 * per_xcd)), dim3(C::kThreads), 0, stream>>>(
-      (const uint16_t*)X, (const uint16_t*)values, meta, (const uint16_t*)U, Tpart, Y, (int)M, (int)n_in,
-      (int)n_out, (int)r, ksplit, tiles_n, tiles_m, per_xcd, group_m);
+  linear_prefill_kernel<NI, NJ, P><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
+      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Thi, Tlo, Y, (int)M, (int)n_in,
+      (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   return hipGetLastError();
 }
 

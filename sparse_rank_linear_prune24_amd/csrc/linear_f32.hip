@@ -1,7 +1,8 @@
 // Y = X S^T + T U^T for float32 operands (T = X V^T from the first low-rank stage), float32
 // arithmetic throughout (LoSparse page, §3.2: the two products summed).  One lane per output;
-// the sparse sum walks the row's groups in order, two fused multiply-adds per group.  This path
-// exists for exact-type float32 layers (small, latency-bound); bf16 layers use the MFMA kernels.
+// the sparse sum walks the row's groups in order (through the packed tiles of 16 rows x 64
+// columns), two fused multiply-adds per group.  This path exists for exact-type float32 layers
+// (small, latency-bound); bf16 layers use the MFMA kernels.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -16,18 +17,16 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict
   const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (n >= n_out || m >= M) return;
   const float* x = X + (size_t)m * K;
-  const float* v = values + (size_t)n * (K / 2);
-  const uint32_t* mw = meta + (size_t)n * (K / 32);
+  const int TK = (K + 63) / 64;
+  const float* v = values + (size_t)(n / 16) * TK * 512;  // this row's tile row
+  const uint32_t* mw = meta + (size_t)(n / 16) * TK * 32 + (n % 16);
   float acc = 0.0f;
-  for (int w = 0; w < K / 32; ++w) {
-    const uint32_t word = mw[w];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int grp = w * 8 + g;
-      const uint32_t nib = (word >> (4 * g)) & 0xFu;
-      acc = fmaf(x[4 * grp + (nib & 3u)], v[2 * grp], acc);
-      acc = fmaf(x[4 * grp + (nib >> 2)], v[2 * grp + 1], acc);
-    }
+  for (int grp = 0; grp < K / 4; ++grp) {
+    const int tk = grp / 16, gi = grp % 16;
+    const uint32_t nib = (mw[tk * 32 + (gi / 8) * 16] >> (4 * (gi % 8))) & 0xFu;
+    const float* kept = v + (size_t)tk * 512 + ((n % 16) + 16 * (gi / 4)) * 8 + 2 * (gi % 4);
+    acc = fmaf(x[4 * grp + (nib & 3u)], kept[0], acc);
+    acc = fmaf(x[4 * grp + (nib >> 2)], kept[1], acc);
   }
   float lr = 0.0f;
   for (int j = 0; j < r; ++j) lr = fmaf(T[(size_t)m * r + j], U[(size_t)n * r + j], lr);

@@ -1,10 +1,14 @@
 // First stage of the low-rank product, T = X V^T (LoSparse page, §3.2: the input is multiplied by
 // the thin factors; in the orientation used here X [M x n_in] times V^T [n_in x r]).
 //
-// bf16: dense MFMA 16x16x32 with float32 accumulation. One wave owns 16 tokens x 64 ranks over one
-// slice of K; K is split across waves when there are few token blocks (decode shapes) so enough
-// waves stream X and V, and the slices' partial sums are written as separate float32 planes which
-// the consumer adds in a fixed order (no atomics: bitwise reproducible).
+// bf16: a workgroup owns 16*TF tokens x 16*RF ranks over the whole of K; its waves take
+// interleaved 64-column K steps, each wave staging its own X and V rows in a private LDS region
+// (row-contiguous loads, padded pitch) with several steps of loads in flight, and feed gfx950's
+// structured-sparse MFMA: X is the dense B operand; V is the A operand, dense V being the sum of
+// two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of every group of four columns).
+// The waves' partial sums are combined through LDS in wave order (deterministic, no atomics, no
+// communication between workgroups), and T is written as a bfloat16 pair: hi = T rounded to nearest
+// even, lo = (T - hi) rounded to nearest even (hi + lo carries about 16 significant bits).
 // fp32: one wave per output, lanes stride over K, fixed-order butterfly reduction.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -12,63 +16,124 @@
 namespace splr {
 namespace {
 
-constexpr int kRankBlocks = 4;  // 16-wide rank blocks per wave (64 ranks)
-constexpr int kStepUnroll = 4;  // K steps (32 columns each) whose loads are issued together
+constexpr int kPitchU4 = 10;  // LDS row pitch in 16-byte units (128 bytes + 32 pad): conflict-free b128 reads
 
-__global__ __launch_bounds__(64) void lowrank_bf16_kernel(const uint16_t* __restrict__ X,
-                                                         const uint16_t* __restrict__ V, int M, int K,
-                                                         int r, int steps_per_split,
-                                                         float* __restrict__ Tpart) {
-  const int lane = threadIdx.x;
-  const int m0 = blockIdx.x * 16;
-  const int j0 = blockIdx.y * 16 * kRankBlocks;
-  const int split = blockIdx.z;
-  const int nsteps = K / 32;
-  const int s_begin = split * steps_per_split;
-  const int s_end = min(nsteps, s_begin + steps_per_split);
+int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-  const int row = lane & 15;       // A row (token) / B column (rank) owned by this lane
-  const int koff = 8 * (lane >> 4);  // this lane's 8-column slice of a 32-column K step
-  const bool m_ok = m0 + row < M;
-  const uint16_t* xrow = X + (size_t)(m_ok ? m0 + row : 0) * K + koff;
-  const uint16_t* vrow[kRankBlocks];
-  bool j_ok[kRankBlocks];
-#pragma unroll
-  for (int b = 0; b < kRankBlocks; ++b) {
-    const int j = j0 + 16 * b + row;
-    j_ok[b] = j < r;
-    vrow[b] = V + (size_t)(j_ok[b] ? j : 0) * K + koff;
-  }
-  f32x4_t acc[kRankBlocks];
-#pragma unroll
-  for (int b = 0; b < kRankBlocks; ++b) acc[b] = f32x4_t{0, 0, 0, 0};
+template <int TF, int RF, int WAVES, int D>
+__global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t* __restrict__ X,
+                                                                 const uint16_t* __restrict__ V, int M, int K,
+                                                                 int r, uint16_t* __restrict__ Thi,
+                                                                 uint16_t* __restrict__ Tlo) {
+  constexpr int kRows = 16 * (TF + RF);    // staged rows per wave: X tokens, then V ranks
+  constexpr int kLoads = kRows / 8;        // 8 rows x 128 bytes per load instruction
+  __shared__ u32x4_t stage[WAVES][kRows * kPitchU4];
+  __shared__ f32x4_t red[(WAVES - 1) * RF * TF * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 15, quad = lane >> 4;
+  const int m0 = blockIdx.x * 16 * TF, j0 = blockIdx.y * 16 * RF;
+  const int TK = (K + 63) / 64;
+  u32x4_t* st = stage[wave];
 
-  const u32x4_t zero = {0, 0, 0, 0};
-  for (int s = s_begin; s < s_end; s += kStepUnroll) {
-    u32x4_t xa[kStepUnroll], vb[kStepUnroll][kRankBlocks];
+  // this lane's rows: instruction t covers staged rows 8t .. 8t+7, chunk lane % 8 of a step
+  const int ch = lane & 7;
+  const uint16_t* src[kLoads];
+  bool zrow[kLoads], is_v[kLoads];
+  int dst[kLoads];
 #pragma unroll
-    for (int u = 0; u < kStepUnroll; ++u) {
-      const bool in = s + u < s_end;
-      const size_t k = (size_t)(s + u) * 32;
-      xa[u] = (in && m_ok) ? *(const u32x4_t*)(xrow + k) : zero;
-#pragma unroll
-      for (int b = 0; b < kRankBlocks; ++b) vb[u][b] = (in && j_ok[b]) ? *(const u32x4_t*)(vrow[b] + k) : zero;
+  for (int t = 0; t < kLoads; ++t) {
+    const int row = 8 * t + (lane >> 3);
+    dst[t] = row * kPitchU4 + ch;
+    is_v[t] = row >= 16 * TF;
+    if (!is_v[t]) {
+      src[t] = X + (size_t)min(m0 + row, M - 1) * K + 8 * ch;
+      zrow[t] = false;
+    } else {
+      const int j = j0 + row - 16 * TF;
+      zrow[t] = j >= r;
+      src[t] = V + (size_t)min(j, r - 1) * K + 8 * ch;
     }
+  }
+  auto load = [&](int kc, u32x4_t (&v)[kLoads]) {
+    int col = min(kc, TK - 1) * 64;
+    if (col + 8 * ch >= K) col -= 32;  // 32-column tail step: re-read valid columns (V zeroed there)
 #pragma unroll
-    for (int u = 0; u < kStepUnroll; ++u)
+    for (int t = 0; t < kLoads; ++t) v[t] = *(const u32x4_t*)(src[t] + col);
+  };
+
+  f32x4_t acc[RF][TF];
 #pragma unroll
-      for (int b = 0; b < kRankBlocks; ++b) acc[b] = mfma16x16x32(as_bf16x8(xa[u]), as_bf16x8(vb[u][b]), acc[b]);
+  for (int a = 0; a < RF; ++a)
+#pragma unroll
+    for (int f = 0; f < TF; ++f) acc[a][f] = f32x4_t{0, 0, 0, 0};
+
+  // steps kc = wave, wave + WAVES, ...; a ring of D steps of loads stays in flight (slot u holds
+  // step s0 + u and is refilled with step s0 + u + D right after it is written to LDS)
+  const int my_steps = (TK - wave + WAVES - 1) / WAVES;
+  u32x4_t ring[D][kLoads];
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(wave + u * WAVES, ring[u]);
+  for (int s0 = 0; s0 < my_steps; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int kc = wave + (s0 + u) * WAVES;
+      if (s0 + u < my_steps) {  // wave-uniform
+#pragma unroll
+        for (int t = 0; t < kLoads; ++t) {
+          const bool z = zrow[t] || (is_v[t] && kc * 64 + 8 * ch >= K);
+          st[dst[t]] = z ? u32x4_t{0, 0, 0, 0} : ring[u][t];
+        }
+        load(kc + D * WAVES, ring[u]);
+#pragma unroll
+        for (int a = 0; a < RF; ++a) {
+          const int vrow = (16 * TF + 16 * a + sub) * kPitchU4;
+          const u32x4_t d0 = st[vrow + 2 * quad], d1 = st[vrow + 2 * quad + 1];
+          const bf16x8_t a01 = as_bf16x8(u32x4_t{d0[0], d0[2], d1[0], d1[2]});
+          const bf16x8_t a23 = as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]});
+#pragma unroll
+          for (int f = 0; f < TF; ++f) {
+            const int xrow = (16 * f + sub) * kPitchU4;
+            const bf16x16_t bx = cat16(as_bf16x8(st[xrow + quad]), as_bf16x8(st[xrow + 4 + quad]));
+            acc[a][f] = smfmac16x16x64(a01, bx, acc[a][f], 0x4444);
+            acc[a][f] = smfmac16x16x64(a23, bx, acc[a][f], 0xEEEE);
+          }
+        }
+      }
+    }
   }
 
-  float* out = Tpart + (size_t)split * M * r;
+  // combine the waves in order, then T (D rows = ranks j0 + 16 a + 4*(lane/16) + 0..3, column =
+  // token m0 + 16 f + lane%16) as hi / lo bfloat16 planes
+  if (wave > 0) {
 #pragma unroll
-  for (int b = 0; b < kRankBlocks; ++b) {
-    const int j = j0 + 16 * b + (lane & 15);
+    for (int a = 0; a < RF; ++a)
+#pragma unroll
+      for (int f = 0; f < TF; ++f) red[(((wave - 1) * RF + a) * TF + f) * 64 + lane] = acc[a][f];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w)
+#pragma unroll
+    for (int a = 0; a < RF; ++a)
+#pragma unroll
+      for (int f = 0; f < TF; ++f) acc[a][f] += red[(((w - 1) * RF + a) * TF + f) * 64 + lane];
+#pragma unroll
+  for (int a = 0; a < RF; ++a) {
+    const int j = j0 + 16 * a + 4 * quad;
     if (j >= r) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 4 * (lane >> 4) + i;
-      if (m < M) out[(size_t)m * r + j] = acc[b][i];
+    for (int f = 0; f < TF; ++f) {
+      const int m = m0 + 16 * f + sub;
+      if (m >= M) continue;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = float_to_bf16_bits(acc[a][f][e]);
+        l[e] = float_to_bf16_bits(acc[a][f][e] - bf16_bits_to_float(h[e]));
+      }
+      *(u32x2_t*)(Thi + (size_t)m * r + j) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *(u32x2_t*)(Tlo + (size_t)m * r + j) = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
     }
   }
 }
@@ -90,30 +155,30 @@ __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restric
 
 }  // namespace
 
-int lowrank_ksplit(int64_t M, int64_t n_in, int64_t r, bool bf16) {
-  if (!bf16 || r == 0) return 1;
-  const int64_t waves = ceil_div(M, 16) * ceil_div(r, 16 * kRankBlocks);
-  const int64_t nsteps = n_in / 32;
-  int64_t ks = ceil_div(512, waves);
-  ks = ks < 16 ? ks : 16;
-  const int64_t max_by_k = nsteps / 8 > 1 ? nsteps / 8 : 1;  // keep >= 8 steps (256 columns) per slice
-  ks = ks < max_by_k ? ks : max_by_k;
-  return (int)(ks > 0 ? ks : 1);
+size_t lowrank_workspace_bytes(int64_t M, int64_t r, bool bf16) {
+  if (r == 0) return 0;
+  return bf16 ? (size_t)M * r * 2 * sizeof(uint16_t) : (size_t)M * r * sizeof(float);
 }
 
-hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16, int ksplit,
-                          float* Tpart, hipStream_t stream) {
+hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16,
+                          void* workspace, hipStream_t stream) {
   if (r == 0) return hipSuccess;
   if (bf16) {
-    const int nsteps = (int)(n_in / 32);
-    const int per = (int)ceil_div(nsteps, ksplit);
-    dim3 grid((unsigned)ceil_div(M, 16), (unsigned)ceil_div(r, 16 * kRankBlocks), (unsigned)ksplit);
-    lowrank_bf16_kernel<<<grid, dim3(64), 0, stream>>>((const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in,
-                                                      (int)r, per, Tpart);
+    uint16_t* Thi = (uint16_t*)workspace;
+    uint16_t* Tlo = Thi + (size_t)M * r;
+    if (M <= 16) {  // few tokens: more waves per workgroup stream K
+      dim3 grid((unsigned)cdiv(M, 16), (unsigned)cdiv(r, 16));
+      lowrank_bf16_kernel<1, 1, 16, 4><<<grid, dim3(1024), 0, stream>>>(
+          (const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in, (int)r, Thi, Tlo);
+    } else {
+      dim3 grid((unsigned)cdiv(M, 32), (unsigned)cdiv(r, 16));
+      lowrank_bf16_kernel<2, 1, 4, 4><<<grid, dim3(256), 0, stream>>>(
+          (const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in, (int)r, Thi, Tlo);
+    }
   } else {
     const int64_t waves = M * r;
     lowrank_f32_kernel<<<dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, stream>>>(
-        (const float*)X, (const float*)V, (int)M, (int)n_in, (int)r, Tpart);
+        (const float*)X, (const float*)V, (int)M, (int)n_in, (int)r, (float*)workspace);
   }
   return hipGetLastError();
 }

@@ -4,12 +4,13 @@
 // 3BASiL article, "A three-block ADMM replaces alternating minimization"): keep the two entries of
 // largest magnitude as bit copies, ties to the lower column.
 //
-// The work is pure HBM streaming: each lane owns one 16-byte chunk of R per step (two bf16 groups
-// or one fp32 group), ranks the four entries of a group with integer compares of the sign-cleared
-// bit patterns (six compares, no floating point, so the result is bit-exact and independent of
-// denormal modes), writes its kept pair as one 8-byte store, and the lanes of a quad (bf16) or an
-// octet (fp32) merge their nibbles into one metadata word with cross-lane shuffles. Loads of a wave
-// cover 1 KiB of contiguous R, value stores 512 contiguous bytes.
+// HBM streaming kernel. A workgroup owns 16 rows x 512 bytes of R (four bf16 tiles or two fp32
+// tiles of the packed layout). Each lane reads 16-byte chunks with row-contiguous, fully
+// coalesced loads, ranks the four entries of each group with integer compares of the sign-cleared
+// bit patterns (six compares, no floating point: bit-exact and independent of denormal modes),
+// and scatters its kept pair into the tile image in LDS; the lanes that share a metadata word
+// merge their nibbles with cross-lane shuffles. The finished tiles leave LDS as contiguous
+// 16-byte stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -17,110 +18,116 @@ namespace splr {
 namespace {
 
 constexpr int kPackThreads = 256;
-constexpr int kPackIter = 4;  // chunks per lane, loaded before any is processed
 
-// Rank four magnitude keys; returns the keep mask bits for positions a < b via (a, b).
-__device__ __forceinline__ void top2_of_4(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3, int& a,
-                                          int& b, bool& keep0, bool& keep1, bool& keep2, bool& keep3) {
-  // i outranks j  <=>  k_i > k_j, or k_i == k_j and i < j.  An entry is kept iff it outranks at
-  // least two of the other three (the ranks of four distinct-by-order entries are 3, 2, 1, 0).
+// Keep positions of four magnitude keys: i outranks j <=> k_i > k_j, or k_i == k_j and i < j. An
+// entry is kept iff it outranks at least two of the other three (ranks of four entries in a
+// strict order are 3, 2, 1, 0). Returns the nibble (a | b << 2) and the kept bit patterns.
+__device__ __forceinline__ uint32_t top2_of_4(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3, uint32_t e0,
+                                              uint32_t e1, uint32_t e2, uint32_t e3, uint32_t& va, uint32_t& vb) {
   const int w0 = (k0 >= k1) + (k0 >= k2) + (k0 >= k3);
   const int w1 = (k1 > k0) + (k1 >= k2) + (k1 >= k3);
   const int w2 = (k2 > k0) + (k2 > k1) + (k2 >= k3);
   const int w3 = (k3 > k0) + (k3 > k1) + (k3 > k2);
-  keep0 = w0 >= 2;
-  keep1 = w1 >= 2;
-  keep2 = w2 >= 2;
-  keep3 = w3 >= 2;
-  a = keep0 ? 0 : (keep1 ? 1 : 2);
-  b = keep3 ? 3 : (keep2 ? 2 : 1);
+  const bool keep0 = w0 >= 2, keep1 = w1 >= 2, keep2 = w2 >= 2, keep3 = w3 >= 2;
+  const int a = keep0 ? 0 : (keep1 ? 1 : 2);
+  const int b = keep3 ? 3 : (keep2 ? 2 : 1);
+  va = keep0 ? e0 : (keep1 ? e1 : e2);
+  vb = keep3 ? e3 : (keep2 ? e2 : e1);
+  return (uint32_t)(a | (b << 2));
 }
 
-// One bf16 group held in two dwords (e0 | e1 << 16, e2 | e3 << 16) -> packed kept pair, nibble.
-__device__ __forceinline__ uint32_t select_bf16_group(uint32_t lo, uint32_t hi, uint32_t& nibble) {
-  const uint32_t e0 = lo & 0xFFFFu, e1 = lo >> 16, e2 = hi & 0xFFFFu, e3 = hi >> 16;
-  int a, b;
-  bool k0, k1, k2, k3;
-  top2_of_4(e0 & 0x7FFFu, e1 & 0x7FFFu, e2 & 0x7FFFu, e3 & 0x7FFFu, a, b, k0, k1, k2, k3);
-  const uint32_t va = k0 ? e0 : (k1 ? e1 : e2);
-  const uint32_t vb = k3 ? e3 : (k2 ? e2 : e1);
-  nibble = (uint32_t)(a | (b << 2));
-  return va | (vb << 16);
-}
+template <bool BF16>
+__global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_t* __restrict__ R, int n_out, int K,
+                                                                    int TK, u32x4_t* __restrict__ values,
+                                                                    uint32_t* __restrict__ meta) {
+  constexpr int kEsz = BF16 ? 2 : 4;            // bytes per entry
+  constexpr int kPerChunk = 16 / kEsz;          // entries per 16-byte chunk (8 bf16 = 2 groups, 4 fp32 = 1)
+  constexpr int kCols = 32 * kPerChunk;         // columns per workgroup (32 chunks a row)
+  constexpr int kTiles = kCols / 64;            // packed tiles per workgroup (4 bf16, 2 fp32)
+  constexpr int kTileU4 = 512 * kEsz / 16;      // 16-byte units of values per tile (64 / 128)
+  __shared__ u32x4_t sv[kTiles * kTileU4];
+  __shared__ uint32_t sm[kTiles * 32];
 
-__global__ __launch_bounds__(kPackThreads) void prune24_pack_bf16_kernel(const u32x4_t* __restrict__ R,
-                                                                        u32x2_t* __restrict__ values,
-                                                                        uint32_t* __restrict__ meta,
-                                                                        int64_t n_chunks) {
-  const int64_t base = (int64_t)blockIdx.x * (kPackThreads * kPackIter) + threadIdx.x;
-  u32x4_t x[kPackIter];
+  const int tr = blockIdx.x;                    // tile row
+  const int tk0 = blockIdx.y * kTiles;          // first tile column of this workgroup
+  const int tid = threadIdx.x;
+
+  u32x4_t x[2];
+  bool valid[2];
 #pragma unroll
-  for (int it = 0; it < kPackIter; ++it) {
-    const int64_t c = base + (int64_t)it * kPackThreads;
-    x[it] = c < n_chunks ? __builtin_nontemporal_load(R + c) : u32x4_t{0, 0, 0, 0};
+  for (int c = 0; c < 2; ++c) {
+    const int q = tid + c * kPackThreads;
+    const int r = q >> 5, ch = q & 31;
+    const int n = tr * 16 + r;
+    const int k = blockIdx.y * kCols + ch * kPerChunk;
+    valid[c] = n < n_out && k < K;
+    x[c] = valid[c] ? __builtin_nontemporal_load((const u32x4_t*)(R + ((size_t)n * K + k) * kEsz))
+                    : u32x4_t{0, 0, 0, 0};
   }
 #pragma unroll
-  for (int it = 0; it < kPackIter; ++it) {
-    const int64_t c = base + (int64_t)it * kPackThreads;
-    uint32_t n0, n1;
-    const uint32_t v0 = select_bf16_group(x[it][0], x[it][1], n0);
-    const uint32_t v1 = select_bf16_group(x[it][2], x[it][3], n1);
-    // chunk c holds groups 2c, 2c+1 -> byte (c % 4) of metadata word c / 4
-    uint32_t w = n0 | (n1 << 4);
-    w |= (uint32_t)__shfl_down((int)w, 1) << 8;
-    w |= (uint32_t)__shfl_down((int)w, 2) << 16;
-    if (c < n_chunks) {
-      values[c] = u32x2_t{v0, v1};
-      if ((threadIdx.x & 3) == 0) meta[c >> 2] = w;
+  for (int c = 0; c < 2; ++c) {
+    const int q = tid + c * kPackThreads;
+    const int r = q >> 5, ch = q & 31;
+    uint32_t word;  // this chunk's nibbles, merged below into metadata words
+    if constexpr (BF16) {
+      // chunk = groups gi0, gi0+1 of tile tkl (gi0 even)
+      const int tkl = ch >> 3, gi0 = 2 * (ch & 7);
+      uint32_t v[4];
+      const uint32_t d0 = x[c][0], d1 = x[c][1], d2 = x[c][2], d3 = x[c][3];
+      uint32_t n0 = top2_of_4(d0 & 0x7FFFu, (d0 >> 16) & 0x7FFFu, d1 & 0x7FFFu, (d1 >> 16) & 0x7FFFu, d0 & 0xFFFFu,
+                              d0 >> 16, d1 & 0xFFFFu, d1 >> 16, v[0], v[1]);
+      uint32_t n1 = top2_of_4(d2 & 0x7FFFu, (d2 >> 16) & 0x7FFFu, d3 & 0x7FFFu, (d3 >> 16) & 0x7FFFu, d2 & 0xFFFFu,
+                              d2 >> 16, d3 & 0xFFFFu, d3 >> 16, v[2], v[3]);
+      if (!valid[c]) n0 = n1 = 0;  // padding: zero entries (already zero) and zero nibbles
+      const int slot = r + 16 * (gi0 >> 2);
+      // 4 entries (8 bytes) at entry 2*(gi0 % 4) of the slot: half (gi0 % 4) / 2 of its 16 bytes
+      u32x2_t* dst = (u32x2_t*)&sv[tkl * kTileU4 + slot] + ((gi0 & 3) >> 1);
+      *dst = u32x2_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+      // byte (gi0 % 8) / 2 of word (gi0 / 8) of row r: the four lanes ch % 4 = 0..3 share it
+      word = n0 | (n1 << 4);
+      word |= (uint32_t)__shfl_down((int)word, 1) << 8;
+      word |= (uint32_t)__shfl_down((int)word, 2) << 16;
+      if ((ch & 3) == 0) sm[tkl * 32 + (gi0 >> 3) * 16 + r] = word;
+    } else {
+      // chunk = group gi of tile tkl
+      const int tkl = ch >> 4, gi = ch & 15;
+      const uint32_t e0 = x[c][0], e1 = x[c][1], e2 = x[c][2], e3 = x[c][3];
+      uint32_t va, vb;
+      uint32_t nb = top2_of_4(e0 & 0x7FFFFFFFu, e1 & 0x7FFFFFFFu, e2 & 0x7FFFFFFFu, e3 & 0x7FFFFFFFu, e0, e1, e2, e3,
+                              va, vb);
+      if (!valid[c]) nb = 0;
+      const int slot = r + 16 * (gi >> 2);
+      u32x2_t* dst = (u32x2_t*)&sv[tkl * kTileU4 + 2 * slot] + (gi & 3);
+      *dst = u32x2_t{va, vb};
+      // nibble gi % 8 of word gi / 8 of row r: the eight lanes ch % 8 = 0..7 share it
+      word = nb;
+      word |= (uint32_t)__shfl_down((int)word, 1) << 4;
+      word |= (uint32_t)__shfl_down((int)word, 2) << 8;
+      word |= (uint32_t)__shfl_down((int)word, 4) << 16;
+      if ((ch & 7) == 0) sm[tkl * 32 + (gi >> 3) * 16 + r] = word;
     }
   }
-}
-
-__global__ __launch_bounds__(kPackThreads) void prune24_pack_f32_kernel(const u32x4_t* __restrict__ R,
-                                                                       u32x2_t* __restrict__ values,
-                                                                       uint32_t* __restrict__ meta,
-                                                                       int64_t n_chunks) {
-  const int64_t base = (int64_t)blockIdx.x * (kPackThreads * kPackIter) + threadIdx.x;
-  u32x4_t x[kPackIter];
-#pragma unroll
-  for (int it = 0; it < kPackIter; ++it) {
-    const int64_t c = base + (int64_t)it * kPackThreads;
-    x[it] = c < n_chunks ? __builtin_nontemporal_load(R + c) : u32x4_t{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int it = 0; it < kPackIter; ++it) {
-    const int64_t c = base + (int64_t)it * kPackThreads;
-    const uint32_t e0 = x[it][0], e1 = x[it][1], e2 = x[it][2], e3 = x[it][3];
-    int a, b;
-    bool k0, k1, k2, k3;
-    top2_of_4(e0 & 0x7FFFFFFFu, e1 & 0x7FFFFFFFu, e2 & 0x7FFFFFFFu, e3 & 0x7FFFFFFFu, a, b, k0, k1, k2, k3);
-    const uint32_t va = k0 ? e0 : (k1 ? e1 : e2);
-    const uint32_t vb = k3 ? e3 : (k2 ? e2 : e1);
-    // chunk c is group c -> nibble (c % 8) of metadata word c / 8
-    uint32_t w = (uint32_t)(a | (b << 2));
-    w |= (uint32_t)__shfl_down((int)w, 1) << 4;
-    w |= (uint32_t)__shfl_down((int)w, 2) << 8;
-    w |= (uint32_t)__shfl_down((int)w, 4) << 16;
-    if (c < n_chunks) {
-      values[c] = u32x2_t{va, vb};
-      if ((threadIdx.x & 7) == 0) meta[c >> 3] = w;
-    }
-  }
+  __syncthreads();
+  // tiles (tr, tk0 .. tk0 + kTiles - 1) are contiguous in the packed arrays
+  const size_t t0 = (size_t)tr * TK + tk0;
+  const int n_tiles = min(kTiles, TK - tk0);
+  if (tid < n_tiles * kTileU4) values[t0 * kTileU4 + tid] = sv[tid];
+  if (tid < n_tiles * 8) ((u32x4_t*)meta)[t0 * 8 + tid] = ((const u32x4_t*)sm)[tid];
 }
 
 }  // namespace
 
 hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
                                uint32_t* meta, hipStream_t stream) {
-  // 16-byte chunks: bf16 -> 8 entries (2 groups), fp32 -> 4 entries (1 group)
-  const int64_t n_chunks = n_out * n_in / (bf16 ? 8 : 4);
-  const int64_t blocks = ceil_div(n_chunks, (int64_t)kPackThreads * kPackIter);
+  const int TK = (int)ceil_div(n_in, 64);
+  const int cols = bf16 ? 256 : 128;
+  dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(n_in, cols));
   if (bf16)
-    prune24_pack_bf16_kernel<<<dim3((unsigned)blocks), dim3(kPackThreads), 0, stream>>>(
-        (const u32x4_t*)R, (u32x2_t*)values, meta, n_chunks);
+    prune24_pack_kernel<true><<<grid, dim3(kPackThreads), 0, stream>>>((const uint8_t*)R, (int)n_out, (int)n_in, TK,
+                                                                      (u32x4_t*)values, meta);
   else
-    prune24_pack_f32_kernel<<<dim3((unsigned)blocks), dim3(kPackThreads), 0, stream>>>(
-        (const u32x4_t*)R, (u32x2_t*)values, meta, n_chunks);
+    prune24_pack_kernel<false><<<grid, dim3(kPackThreads), 0, stream>>>((const uint8_t*)R, (int)n_out, (int)n_in, TK,
+                                                                       (u32x4_t*)values, meta);
   return hipGetLastError();
 }
 

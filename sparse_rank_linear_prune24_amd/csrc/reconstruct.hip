@@ -24,11 +24,15 @@ __global__ __launch_bounds__(256) void dense_reconstruct_kernel(const void* __re
   if (t >= n_out * groups) return;
   const int64_t n = t / groups;
   const int g = (int)(t - n * groups);
-  const uint32_t nib = (meta[(size_t)n * (K / 32) + g / 8] >> (4 * (g % 8))) & 0xFu;
+  // packed tiles of 16 rows x 64 columns: tile (n / 16, g / 16), slot n % 16 + 16 * (gi / 4)
+  const int TK = (K + 63) / 64, gi = g % 16;
+  const size_t tile = (size_t)(n / 16) * TK + g / 16;
+  const uint32_t nib = (meta[tile * 32 + (gi / 8) * 16 + n % 16] >> (4 * (gi % 8))) & 0xFu;
   const int a = (int)(nib & 3u), b = (int)(nib >> 2);
+  const size_t e = (tile * 64 + (size_t)(n % 16) + 16 * (gi / 4)) * 8 + 2 * (gi % 4);
   float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  out[a] = load_elem<BF16>(values, (size_t)n * (K / 2) + 2 * g);
-  out[b] = load_elem<BF16>(values, (size_t)n * (K / 2) + 2 * g + 1);
+  out[a] = load_elem<BF16>(values, e);
+  out[b] = load_elem<BF16>(values, e + 1);
   if (r > 0) {
     float lr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < r; ++j) {

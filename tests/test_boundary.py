@@ -49,6 +49,19 @@ def test_pack_validation():
     assert f(A, 4, 64, 0, A, MIS, None) == ALIGN
 
 
+def test_packed_bytes():
+    import ctypes
+    f = binding.lib().splr_packed_bytes
+    vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert f(17, 96, 1, ctypes.byref(vb), ctypes.byref(mb)) == OK
+    assert (vb.value, mb.value) == (2 * 2 * 512 * 2, 2 * 2 * 32 * 4)
+    assert f(4096, 4096, 0, ctypes.byref(vb), ctypes.byref(mb)) == OK
+    assert (vb.value, mb.value) == (4096 * 4096 // 2 * 4, 4096 * 4096 // 8)
+    assert f(16, 48, 1, ctypes.byref(vb), ctypes.byref(mb)) == SHAPE
+    assert f(16, 64, 9, ctypes.byref(vb), ctypes.byref(mb)) == DTYPE
+    assert f(16, 64, 1, None, ctypes.byref(mb)) == NULL
+
+
 def test_linear_validation():
     f = binding.lib().splr_linear
     ws = binding.lib().splr_linear_workspace_bytes

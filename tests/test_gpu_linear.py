@@ -25,7 +25,7 @@ TIGHT = 2e-4
 def run_gpu(L, dtype, pack_on_gpu=True):
     Xd, Ud, Vd = to_dev(L.X, dtype), to_dev(L.U if L.r else None, dtype), to_dev(L.V if L.r else None, dtype)
     vd, md = binding.prune24_pack(to_dev(L.R, dtype))
-    Y = binding.linear(Xd, vd, md, Ud, Vd)
+    Y = binding.linear(Xd, vd, md, Ud, Vd, n_out=L.n_out)
     torch.cuda.synchronize()
     return Y.cpu().numpy(), from_dev(vd, dtype), meta_from_dev(md)
 
@@ -37,7 +37,7 @@ def check_layer(L, dtype, tag, rows=None, tight=True):
     bits = np.uint32 if dtype == "fp32" else np.uint16
     assert np.array_equal(m, m_ref) and np.array_equal(v.view(bits), v_ref.view(bits)), f"{tag}: pack differs"
     U, V = (L.U, L.V) if L.r else (None, None)
-    Y_ref = oracle.linear(L.X, v_ref, m_ref, U, V, dtype, rows=rows)
+    Y_ref = oracle.linear(L.X, v_ref, m_ref, L.n_out, U, V, dtype, rows=rows)
     Yg = Y if rows is None else Y[rows]
     assert np.all(np.isfinite(Yg))
     err = rel_err(Yg, Y_ref)
@@ -102,12 +102,12 @@ def test_special_cases(dtype, M):
     # largest output error is a small multiple of 2^-18 rms(Y); 4e-5 (~10 x 2^-18) bounds it.
     zv = torch.zeros_like(vd)
     Y = binding.linear(Xd, zv, md, Ud, Vd).cpu().numpy()
-    ref = oracle.linear(L.X, np.zeros_like(v), m, L.U, L.V, dtype)
+    ref = oracle.linear(L.X, np.zeros_like(v), m, n_out, L.U, L.V, dtype)
     assert rel_err(Y, ref) <= (1e-5 if dtype == "fp32" else 4e-5), "S = 0"
     # U = 0 and r = 0: only the sparse product
     Y0 = binding.linear(Xd, vd, md, torch.zeros_like(Ud), Vd).cpu().numpy()
-    Yr0 = binding.linear(Xd, vd, md, None, None).cpu().numpy()
-    ref = oracle.linear(L.X, v, m, None, None, dtype)
+    Yr0 = binding.linear(Xd, vd, md, None, None, n_out=n_out).cpu().numpy()
+    ref = oracle.linear(L.X, v, m, n_out, None, None, dtype)
     assert rel_err(Y0, ref) <= (1e-5 if dtype == "fp32" else TIGHT), "U = 0"
     assert np.array_equal(Y0, Yr0), "U = 0 and r = 0 differ"
 
@@ -120,7 +120,7 @@ def test_identity_input(dtype):
     vd, md = binding.prune24_pack(to_dev(L.R, dtype))
     eye = to_dev(inputs.from_f64(np.eye(n_in), dtype), dtype)
     Y = binding.linear(eye, vd, md, to_dev(L.U, dtype), to_dev(L.V, dtype)).cpu().numpy()
-    W = oracle.dense_reconstruct(from_dev(vd, dtype), meta_from_dev(md), L.U, L.V, dtype)
+    W = oracle.dense_reconstruct(from_dev(vd, dtype), meta_from_dev(md), n_out, n_in, L.U, L.V, dtype)
     assert rel_err(Y, W.T) <= 1e-5
 
 
@@ -134,7 +134,7 @@ def test_integer_exact_bitwise(M):
     V = inputs.small_integers((r, n_in), -2, 2, dtype, seed=M, tensor_id=3)
     R = inputs.small_integers((n_out, n_in), -4, 4, dtype, seed=M, tensor_id=1)
     v_ref, m_ref = oracle.prune24_pack(R, dtype)
-    ref = oracle.linear(X, v_ref, m_ref, U, V, dtype)
+    ref = oracle.linear(X, v_ref, m_ref, n_out, U, V, dtype)
     vd, md = binding.prune24_pack(to_dev(R, dtype))
     Y = binding.linear(to_dev(X, dtype), vd, md, to_dev(U, dtype), to_dev(V, dtype)).cpu().numpy()
     assert np.array_equal(Y.astype(np.float64), ref)

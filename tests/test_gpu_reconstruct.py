@@ -18,12 +18,12 @@ def test_reconstruct(dtype, n_out, n_in, r):
     vd, md = binding.prune24_pack(to_dev(L.R, dtype))
     v, m = from_dev(vd, dtype), meta_from_dev(md)
     # S only: exact (kept entries widened, +0 elsewhere, signed zeros preserved)
-    W0 = binding.dense_reconstruct(vd, md, None, None).cpu().numpy()
-    ref0 = oracle.dense_reconstruct(v, m, None, None, dtype).astype(np.float32)
+    W0 = binding.dense_reconstruct(vd, md, None, None, n_out=n_out, n_in=n_in).cpu().numpy()
+    ref0 = oracle.dense_reconstruct(v, m, n_out, n_in, None, None, dtype).astype(np.float32)
     assert np.array_equal(W0.view(np.uint32), ref0.view(np.uint32))
     # S + U V
     W = binding.dense_reconstruct(vd, md, to_dev(L.U, dtype), to_dev(L.V, dtype)).cpu().numpy()
-    ref = oracle.dense_reconstruct(v, m, L.U, L.V, dtype)
+    ref = oracle.dense_reconstruct(v, m, n_out, n_in, L.U, L.V, dtype)
     assert rel_err(W, ref) <= 1e-6
 
 
@@ -32,5 +32,5 @@ def test_signed_zeros_survive():
     R[0, 0] = 0x8000          # -0 kept at position 0 of the first group
     R[0, 3] = 0x3F80
     vd, md = binding.prune24_pack(to_dev(R, "bf16"))
-    W = binding.dense_reconstruct(vd, md, None, None).cpu().numpy().view(np.uint32)
+    W = binding.dense_reconstruct(vd, md, None, None, n_out=2, n_in=32).cpu().numpy().view(np.uint32)
     assert W[0, 0] == 0x80000000 and W[0, 3] == 0x3F800000 and W[0, 1] == 0 and W[0, 2] == 0

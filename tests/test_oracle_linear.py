@@ -44,10 +44,10 @@ def test_linear_matches_dense_matmul(dtype, M, n_in, n_out, r):
     L = inputs.random_case(M, n_in, n_out, r, dtype, seed=5, n_outliers=2)
     S = random_24_dense(n_out, n_in, dtype, seed=9)
     values, meta = oracle.prune24_pack(S, dtype)           # lossless on a 2:4 matrix
-    S_back = inputs.from_f64(oracle.dense_reconstruct(values, meta, None, None, dtype), dtype)
+    S_back = inputs.from_f64(oracle.dense_reconstruct(values, meta, n_out, n_in, None, None, dtype), dtype)
     assert np.array_equal(S_back, S)
     U, V = (L.U, L.V) if r else (None, None)
-    Y = oracle.linear(L.X, values, meta, U, V, dtype)
+    Y = oracle.linear(L.X, values, meta, n_out, U, V, dtype)
     Xf, Sf = inputs.to_f64(L.X, dtype), inputs.to_f64(S, dtype)
     Wf = Sf + (inputs.to_f64(L.U, dtype) @ inputs.to_f64(L.V, dtype) if r else 0.0)
     Y_np = Xf @ Wf.T
@@ -66,20 +66,20 @@ def test_special_cases(dtype):
 
     # U = 0: only the sparse product remains
     zU = np.zeros_like(L.U)
-    Y = oracle.linear(L.X, values, meta, zU, L.V, dtype)
+    Y = oracle.linear(L.X, values, meta, n_out, zU, L.V, dtype)
     assert np.max(np.abs(Y - Xf @ Sf.T)) <= 1e-13 * scale
     # r = 0 gives the same
-    Y0 = oracle.linear(L.X, values, meta, None, None, dtype)
+    Y0 = oracle.linear(L.X, values, meta, n_out, None, None, dtype)
     assert np.array_equal(Y0, Y)
     # S = 0: only the low-rank product (X V^T) U^T remains
     zv = np.zeros_like(values)
-    Y = oracle.linear(L.X, zv, meta, L.U, L.V, dtype)
+    Y = oracle.linear(L.X, zv, meta, n_out, L.U, L.V, dtype)
     lr = (Xf @ Vf.T) @ Uf.T
     assert np.max(np.abs(Y - lr)) <= 1e-13 * rms(lr)
     # X = I (M = n_in): Y = (S + U V)^T, i.e. the transposed reconstruction
     eye = inputs.from_f64(np.eye(n_in), dtype)
-    Y = oracle.linear(eye, values, meta, L.U, L.V, dtype)
-    W = oracle.dense_reconstruct(values, meta, L.U, L.V, dtype)
+    Y = oracle.linear(eye, values, meta, n_out, L.U, L.V, dtype)
+    W = oracle.dense_reconstruct(values, meta, n_out, n_in, L.U, L.V, dtype)
     assert np.array_equal(Y, W.T)
     assert np.max(np.abs(W - (Sf + Uf @ Vf))) <= 1e-15 * rms(W) * 10
 
@@ -92,7 +92,7 @@ def test_integer_exact(dtype):
     V = inputs.small_integers((r, n_in), -2, 2, dtype, seed=1, tensor_id=3)
     S = random_24_dense(n_out, n_in, dtype, seed=2, int_range=(-4, 4))
     values, meta = oracle.prune24_pack(S, dtype)
-    Y = oracle.linear(X, values, meta, U, V, dtype)
+    Y = oracle.linear(X, values, meta, n_out, U, V, dtype)
     Xi = inputs.to_f64(X, dtype).astype(np.int64)
     Si = inputs.to_f64(S, dtype).astype(np.int64)
     Ui = inputs.to_f64(U, dtype).astype(np.int64)
@@ -105,18 +105,18 @@ def test_linearity_and_rows():
     dtype = "fp32"
     L = inputs.random_case(20, 256, 40, 16, dtype, seed=31)
     values, meta = oracle.prune24_pack(L.R, dtype)
-    Y1 = oracle.linear(L.X, values, meta, L.U, L.V, dtype)
+    Y1 = oracle.linear(L.X, values, meta, 40, L.U, L.V, dtype)
     # scaling by a power of two is exact on both sides
-    Y2x = oracle.linear(L.X * np.float32(2.0), values, meta, L.U, L.V, dtype)
+    Y2x = oracle.linear(L.X * np.float32(2.0), values, meta, 40, L.U, L.V, dtype)
     assert np.array_equal(Y2x, 2.0 * Y1)
     # additivity over inputs with disjoint column supports (their sum is exact)
     Xa = L.X.copy(); Xa[:, 1::2] = 0
     Xb = L.X.copy(); Xb[:, 0::2] = 0
-    Ya = oracle.linear(Xa, values, meta, L.U, L.V, dtype)
-    Yb = oracle.linear(Xb, values, meta, L.U, L.V, dtype)
+    Ya = oracle.linear(Xa, values, meta, 40, L.U, L.V, dtype)
+    Yb = oracle.linear(Xb, values, meta, 40, L.U, L.V, dtype)
     assert np.max(np.abs(Y1 - (Ya + Yb))) <= 1e-13 * rms(Y1)
     rows = np.array([19, 0, 7, 7, 3])
-    Yr = oracle.linear(L.X, values, meta, L.U, L.V, dtype, rows=rows)
+    Yr = oracle.linear(L.X, values, meta, 40, L.U, L.V, dtype, rows=rows)
     assert np.array_equal(Yr, Y1[rows])
 
 
@@ -124,8 +124,8 @@ def test_named_workload_small():
     """C1 end to end: pack the residual, then the product equals X (S + U V)^T in numpy."""
     L = inputs.make_layer("C1", 0)
     values, meta = oracle.prune24_pack(L.R, "fp32")
-    Y = oracle.linear(L.X, values, meta, L.U, L.V, "fp32")
-    S = oracle.dense_reconstruct(values, meta, None, None, "fp32")
+    Y = oracle.linear(L.X, values, meta, 512, L.U, L.V, "fp32")
+    S = oracle.dense_reconstruct(values, meta, 512, 512, None, None, "fp32")
     W = S + L.U.astype(np.float64) @ L.V.astype(np.float64)
     Y_np = L.X.astype(np.float64) @ W.T
     assert np.max(np.abs(Y - Y_np)) <= 1e-12 * rms(Y_np)

@@ -42,13 +42,11 @@ def brute_force_group(group_bits, dtype):
     return best[1], best[2]
 
 
-def nibbles(meta):
-    meta = np.asarray(meta, dtype=np.uint32)
-    n_out, words = meta.shape
-    out = np.empty((n_out, words * 8), dtype=np.uint32)
-    for g in range(8):
-        out[:, g::8] = (meta >> (4 * g)) & 0xF
-    return out
+def pack_logical(R, dtype):
+    """Oracle pack, returned as its logical view: kept [n_out x n_in/2], nibbles [n_out x n_in/4]."""
+    values, meta = oracle.prune24_pack(R, dtype)
+    kept, nib = oracle.unpack(values, meta, R.shape[0], R.shape[1], dtype)
+    return kept, nib.astype(np.uint32), values, meta
 
 
 def groups_to_matrix(groups, dtype):
@@ -62,8 +60,7 @@ def groups_to_matrix(groups, dtype):
 
 
 def check_against_brute_force(R, dtype):
-    values, meta = oracle.prune24_pack(R, dtype)
-    nib = nibbles(meta)
+    values, nib, _, _ = pack_logical(R, dtype)
     n_out, n_in = R.shape
     for n in range(n_out):
         for g in range(n_in // 4):
@@ -114,8 +111,8 @@ def test_special_value_fixture():
             groups = [[0, 0, 0, 0]] * shift + [c[0] for c in cases]
             bits = np.array(groups, dtype=np.uint32 if dtype == "fp32" else np.uint16)
             R, ng = groups_to_matrix(bits.view(NP[dtype]), dtype)
-            values, meta = oracle.prune24_pack(R, dtype)
-            nib = nibbles(meta).reshape(-1)
+            values, nib, _, _ = pack_logical(R, dtype)
+            nib = nib.reshape(-1)
             vals = values.reshape(-1, 2)
             for i, (xs, want_nib, v0, v1) in enumerate(cases):
                 k = i + shift
@@ -124,20 +121,19 @@ def test_special_value_fixture():
                 assert int(got[0]) == v0 and int(got[1]) == v1, (dtype, [hex(x) for x in xs])
 
 
-def _dense_of(values, meta, dtype):
+def _dense_of(values, meta, shape, dtype):
     """The packed matrix scattered back to storage dtype (exact: S entries are stored values)."""
-    return inputs.from_f64(oracle.dense_reconstruct(values, meta, None, None, dtype), dtype)
+    return inputs.from_f64(oracle.dense_reconstruct(values, meta, shape[0], shape[1], None, None, dtype), dtype)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_invariants_gaussian(dtype):
     g = np.random.default_rng(11)
     R = inputs.from_f64(g.standard_normal((96, 256)) * 0.02, dtype)
-    values, meta = oracle.prune24_pack(R, dtype)
-    nib = nibbles(meta)
+    values, nib, pv, pm = pack_logical(R, dtype)
     assert set(np.unique(nib).tolist()) <= VALID_NIBBLES
 
-    S = _dense_of(values, meta, dtype)
+    S = _dense_of(pv, pm, R.shape, dtype)
     Sf = inputs.to_f64(S, dtype)
     nz = (Sf.reshape(96, -1, 4) != 0).sum(axis=2)
     assert nz.max() <= 2
@@ -147,14 +143,14 @@ def test_invariants_gaussian(dtype):
 
     # idempotence: projecting an already-2:4 matrix changes nothing
     v2, m2 = oracle.prune24_pack(S, dtype)
-    assert np.array_equal(v2, values) and np.array_equal(m2, meta)
+    assert np.array_equal(v2, pv) and np.array_equal(m2, pm)
 
     # sign equivariance: same positions, negated values (sign bit flipped)
     sign = np.uint32(0x80000000) if dtype == "fp32" else np.uint16(0x8000)
     Rb = R.view(np.uint32) if dtype == "fp32" else R
     Rneg = (Rb ^ sign).view(R.dtype) if dtype == "fp32" else Rb ^ sign
-    vn, mn = oracle.prune24_pack(Rneg, dtype)
-    assert np.array_equal(mn, meta)
+    vn, nn, _, _ = pack_logical(Rneg, dtype)
+    assert np.array_equal(nn, nib)
     vb = values.view(np.uint32) if dtype == "fp32" else values
     vnb = vn.view(np.uint32) if dtype == "fp32" else vn
     assert np.array_equal(vnb, vb ^ sign)
@@ -162,15 +158,15 @@ def test_invariants_gaussian(dtype):
     # power-of-two scaling changes no decision (no overflow / underflow at these magnitudes)
     for e in (-6, 3):
         Rs = inputs.from_f64(inputs.to_f64(R, dtype) * 2.0 ** e, dtype)
-        vs, ms = oracle.prune24_pack(Rs, dtype)
-        assert np.array_equal(ms, meta)
+        vs, ns, _, _ = pack_logical(Rs, dtype)
+        assert np.array_equal(ns, nib)
         assert np.array_equal(inputs.to_f64(vs, dtype), inputs.to_f64(values, dtype) * 2.0 ** e)
 
     # permuting whole groups permutes the nibbles and value pairs the same way
     perm = g.permutation(256 // 4)
     Rp = R.reshape(96, -1, 4)[:, perm, :].reshape(96, 256)
-    vp, mp = oracle.prune24_pack(Rp, dtype)
-    assert np.array_equal(nibbles(mp), nib[:, perm])
+    vp, np_, _, _ = pack_logical(Rp, dtype)
+    assert np.array_equal(np_, nib[:, perm])
     assert np.array_equal(vp.reshape(96, -1, 2), values.reshape(96, -1, 2)[:, perm, :])
 
     # kept energy is at least half of every group's energy (top two of four squares)
@@ -184,8 +180,7 @@ def test_optimal_against_every_pattern_vectorised(dtype):
     """Large-scale brute force: the kept pattern discards no more energy than any of the six."""
     g = np.random.default_rng(3)
     R = inputs.from_f64(g.standard_normal((128, 512)) * 0.02, dtype)
-    values, meta = oracle.prune24_pack(R, dtype)
-    nib = nibbles(meta)
+    values, nib, _, _ = pack_logical(R, dtype)
     x2 = inputs.to_f64(R, dtype).reshape(128, -1, 4) ** 2
     a = nib & 3
     b = nib >> 2
@@ -199,3 +194,36 @@ def test_optimal_against_every_pattern_vectorised(dtype):
 def test_shape_errors():
     with pytest.raises(ValueError):
         oracle.prune24_pack(np.zeros((4, 48), dtype=np.float32), "fp32")   # 48 % 32 != 0
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_tiled_layout_positions(dtype):
+    """Physical placement of the packed layout, checked at hand-derived positions.
+
+    Layout (our reading; the pages fix no storage format): tiles of 16 rows x 64 input columns;
+    group g of row n lives in tile (n // 16, g // 16), at slot L = n % 16 + 16 * ((g % 16) // 4),
+    entries 2 * (g % 4) and 2 * (g % 4) + 1; its nibble is at bits 4 * (g % 8) of metadata word
+    ((g % 16) // 8, n % 16) of the tile. Padding is zero."""
+    n_out, n_in = 17, 96                   # 2 x 2 tiles, ragged in both directions
+    g = np.random.default_rng(5)
+    f = g.standard_normal((n_out, n_in)) + 3.0  # all positive, no ties
+    R = inputs.from_f64(f, dtype)
+    kept, nib, values, meta = pack_logical(R, dtype)
+    assert values.shape == (2, 2, 64, 8) and meta.shape == (2, 2, 2, 16)
+    cases = [  # (row, group) -> (tile row, tile col, slot, entry, meta word, meta row, nibble shift)
+        ((0, 0), (0, 0, 0, 0, 0, 0, 0)),
+        ((5, 13), (0, 0, 53, 2, 1, 5, 20)),
+        ((16, 17), (1, 1, 0, 2, 0, 0, 4)),
+        ((3, 20), (0, 1, 19, 0, 0, 3, 16)),
+        ((9, 7), (0, 0, 25, 6, 0, 9, 28)),
+    ]
+    for (n, grp), (tr, tk, slot, e, w, mr, sh) in cases:
+        assert values[tr, tk, slot, e] == kept[n, 2 * grp] and values[tr, tk, slot, e + 1] == kept[n, 2 * grp + 1]
+        assert (meta[tr, tk, w, mr] >> sh) & 0xF == nib[n, grp]
+    # column padding: the second tile column holds groups 16..23 only (slots 0..31, word 0)
+    assert not values[:, 1, 32:, :].any() and not meta[:, 1, 1, :].any()
+    # row padding: only row 16 exists in the second tile row
+    rows_used = np.zeros(64, dtype=bool)
+    rows_used[[0, 16, 32, 48]] = True
+    assert not values[1][:, ~rows_used, :].any()
+    assert not meta[1][:, :, 1:].any()
