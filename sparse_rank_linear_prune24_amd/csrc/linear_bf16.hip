@@ -27,6 +27,7 @@
 //              64-column K steps, stream S straight into registers and X through a private LDS
 //              slot each, and combine their partial accumulators through LDS in a fixed order.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -39,10 +40,28 @@ namespace {
 // a 16-byte pad leaves them 2-way bank conflicted.
 constexpr int kXPitchU4 = 10;
 
+
 // LDS writes of this wave complete, then workgroup barrier. One asm statement with a memory
 // clobber: the compiler moves no LDS access across it, and (unlike __syncthreads(), whose fence
 // drains every outstanding global load) it leaves the register prefetches in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The builtin wait after it is free at run time; it tells the compiler's wait-count tracking that no
+// LDS access is outstanding, so it adds no conservative waits after the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
+}
+
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}), in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ----------------------------------------------------------------------------------- epilogue
 
@@ -121,7 +140,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], float* 
 
 // ----------------------------------------------------------------------------------- prefill
 
-template <int NI, int NJ, int P>
+template <int NI, int NJ, int P, int PX>
 __global__ __launch_bounds__(256) void linear_prefill_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ Thi, const uint16_t* __restrict__ Tlo,
@@ -131,7 +150,8 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   constexpr int BM = 16 * NJ;
   constexpr int kXLoads = BM / (8 * WAVES);  // X load instructions per wave per step (8 tokens each)
   static_assert(BM % (8 * WAVES) == 0, "X stage must split evenly over the waves");
-  static_assert(P % 2 == 0, "the prefetch distance is also the unroll factor; it must be even");
+  static_assert(P >= 2 && PX >= 2 && P % 2 == 0 && PX % 2 == 0, "prefetch distances must be even");
+  constexpr int kUnroll = P * PX / gcd_int(P, PX);  // unroll factor: every register slot index is a constant
   // the two LDS slots are separate objects, so the compiler may move reads of one past writes of
   // the other
   __shared__ u32x4_t xs0[BM * kXPitchU4];
@@ -150,10 +170,12 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   const int m0 = (first_m + in_group % gsize) * BM;
   const int n0 = (in_group / gsize) * BN;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave; readfirstlane lets the compiler see that (scalar
+  // loop control instead of exec-mask loops)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane & 15, quad = lane >> 4;
   const int TK = (K + 63) / 64, TR = (n_out + 15) / 16;
-  const int nk_pad = (TK + P - 1) / P * P;
+  const int nk_pad = (TK + kUnroll - 1) / kUnroll * kUnroll;
 
   // S fragments of this wave: tile rows (clamped; rows past n_out are zero padding or unused)
   const u32x4_t* vsrc[NI];
@@ -175,8 +197,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
     xdst[t] = tloc * kXPitchU4 + xchunk;
   }
 
-  constexpr int PX = 2;  // X register ring: X of step kc is loaded two steps before it goes to LDS
-  u32x4_t xr[PX][kXLoads];
+  u32x4_t xr[PX][kXLoads];  // X register ring: X of step kc is loaded PX steps before it goes to LDS
   u32x4_t sa[P][NI];
   uint32_t sw[P][NI];  // index operands, zero-extended 16-bit loads
   bf16x16_t bx[2][NJ];
@@ -211,15 +232,19 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
 
-  // Software pipeline, one barrier per K step. At step kc (S register slot d = kc % P, parity
-  // b = kc % 2): the B fragments of step kc are already in registers bx[b] and X of step kc+1 is in
-  // LDS slot b^1. The step reads the B fragments of step kc+1 into bx[b^1] while its MFMAs run,
-  // refills S slot d with step kc+P, writes X of step kc+2 into LDS slot b (whose reads, of step kc,
-  // all completed before the previous barrier), reloads that X register slot with step kc+4, and
-  // ends with the barrier. Padding steps (kc >= TK) zero the S operand.
-  auto step = [&](int kc, auto dd, auto masked) {
-    constexpr int d = decltype(dd)::value;
-    constexpr int b = d & 1;
+  // Software pipeline, one barrier per K step. At step kc (S register slot kc % P, X register slot
+  // (kc+2) % PX, LDS slot and B register parity b = kc % 2): the B fragments of step kc are already
+  // in registers bx[b], X of step kc+1 is in LDS slot b^1, X of step kc+2 is in registers. The step
+  // writes X of step kc+2 into LDS slot b (whose reads, of step kc, completed before the previous
+  // barrier), reads the B fragments of step kc+1 into bx[b^1] while its MFMAs run, refills the S
+  // slot of step kc-1 with step kc+P-1 and the X register slot with step kc+2+PX, and ends with the
+  // barrier. The instruction order inside a step is pinned (LDS writes, then LDS reads and global
+  // loads each paired with an MFMA), and no instruction crosses a step boundary. Padding steps
+  // (kc >= TK) zero the S operand.
+  auto step = [&](int kc, auto uu, auto masked) {
+    constexpr int u = decltype(uu)::value;
+    constexpr int d = u % P, b = u & 1, dprev = (u + P - 1) % P, xq = (u + 2) % PX;
+    store_x(b ? xs1 : xs0, xr[xq]);
     read_b(b ? xs0 : xs1, bx[b ^ 1]);
     const uint32_t keep = (!decltype(masked)::value || kc < TK) ? ~0u : 0u;
     bf16x8_t a[NI];
@@ -233,40 +258,53 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < NI; ++i) acc[i][j] = smfmac16x16x64(a[i], bx[b][j], acc[i][j], idx[i]);
-    load_s(kc + P, sa[d], sw[d]);
-    store_x(b ? xs1 : xs0, xr[b]);
-    load_x(kc + 2 + PX, xr[b]);
+    load_s(kc + P - 1, sa[dprev], sw[dprev]);
+    load_x(kc + 2 + PX, xr[xq]);
+    // pinned order: the LDS writes, LDS reads and global loads are spread evenly over the MFMAs,
+    // one after each MFMA, in kXLoads rounds of (1 LDS write, 2*NJ/kXLoads LDS reads, the loads'
+    // share), so that no queue fills and blocks the in-order issue of the MFMAs
+    constexpr int kReads = 2 * NJ, kLoads = 2 * NI + kXLoads, kMfma = NI * NJ, kRounds = kXLoads;
+    static_assert(kReads % kRounds == 0 && kLoads % kRounds == 0, "even spread");
+    static_assert(kRounds * (1 + kReads / kRounds + kLoads / kRounds) <= kMfma, "one MFMA per memory op");
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+#pragma unroll
+      for (int t = 0; t < kReads / kRounds; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < kLoads / kRounds; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kRounds * (1 + (kReads + kLoads) / kRounds), 0);
     lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-#pragma unroll
-  for (int d = 0; d < P; ++d) load_s(d, sa[d], sw[d]);
-  load_x(0, xr[0]);
-  load_x(1, xr[1]);
-  store_x(xs0, xr[0]);
-  store_x(xs1, xr[1]);
-  load_x(2, xr[0]);
-  load_x(3, xr[1]);
+  // Prologue: virtual steps v = -VS .. -1 issue exactly what a step would (X of step v+2 into LDS,
+  // S of step v+P-1, X of step v+2+PX), so the loop is entered with the loads in flight in the same
+  // order as in the steady state and the wait counts the compiler derives need no extra waits.
+  constexpr int VS = (P - 1 > PX + 2) ? P - 1 : PX + 2;
+  static_for<VS>([&](auto ii) {
+    constexpr int v = decltype(ii)::value - VS;
+    if constexpr (v >= -2) store_x(((v + 2) & 1) ? xs1 : xs0, xr[(v + 2 + PX) % PX]);
+    if constexpr (v + P - 1 >= 0) load_s(v + P - 1, sa[(v + P - 1) % P], sw[(v + P - 1) % P]);
+    if constexpr (v + 2 + PX >= 0) load_x(v + 2 + PX, xr[(v + 2 + PX) % PX]);
+  });
   lds_barrier();
   read_b(xs0, bx[0]);
   lds_barrier();  // every wave's reads of slot 0 are done before step 0 overwrites it
-  const int nk_full = TK / P * P;  // steps that need no masking
-  for (int kc0 = 0; kc0 < nk_full; kc0 += P) {
-    step(kc0 + 0, std::integral_constant<int, 0>{}, std::false_type{});
-    step(kc0 + 1, std::integral_constant<int, 1>{}, std::false_type{});
-    if constexpr (P >= 4) {
-      step(kc0 + 2, std::integral_constant<int, 2 % P>{}, std::false_type{});
-      step(kc0 + 3, std::integral_constant<int, 3 % P>{}, std::false_type{});
-    }
-  }
-  for (int kc0 = nk_full; kc0 < nk_pad; kc0 += P) {
-    step(kc0 + 0, std::integral_constant<int, 0>{}, std::true_type{});
-    step(kc0 + 1, std::integral_constant<int, 1>{}, std::true_type{});
-    if constexpr (P >= 4) {
-      step(kc0 + 2, std::integral_constant<int, 2 % P>{}, std::true_type{});
-      step(kc0 + 3, std::integral_constant<int, 3 % P>{}, std::true_type{});
-    }
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int nk_full = TK / kUnroll * kUnroll;  // steps that need no masking
+  for (int kc0 = 0; kc0 < nk_full; kc0 += kUnroll)
+    static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, u, std::false_type{}); });
+  for (int kc0 = nk_full; kc0 < nk_pad; kc0 += kUnroll)
+    static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, u, std::true_type{}); });
 
   const int nrow0 = n0 + wave * 16 * NI;
   if (r > 0) lowrank_epilogue<NI, NJ>(acc, U, Thi, Tlo, M, n_out, r, nrow0, m0, lane);
@@ -284,7 +322,9 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
   constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
   __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
   __shared__ f32x4_t red[(WAVES - 1) * MB * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave; readfirstlane lets the compiler see that (scalar
+  // loop control instead of exec-mask loops)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane & 15, quad = lane >> 4;
   const int tr = blockIdx.x, m0 = blockIdx.y * 16 * MB;
   const int TK = (K + 63) / 64;
@@ -375,13 +415,13 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
   if (M <= kDecodeMaxTokens) return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
 
-  constexpr int NI = 4, NJ = 8, P = 4;
+  constexpr int NI = 4, NJ = 8, P = 4, PX = 2;
   constexpr int BN = 16 * NI * 4, BM = 16 * NJ;
   const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
   const int n_tiles = tiles_n * tiles_m;
   const int per_xcd = (int)ceil_div(n_tiles, 8);
   const int group_m = 4;
-  linear_prefill_kernel<NI, NJ, P><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
+  linear_prefill_kernel<NI, NJ, P, PX><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
       (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Thi, Tlo, Y, (int)M, (int)n_in,
       (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   return hipGetLastError();

@@ -10,6 +10,9 @@
 // communication between workgroups), and T is written as a bfloat16 pair: hi = T rounded to nearest
 // even, lo = (T - hi) rounded to nearest even (hi + lo carries about 16 significant bits).
 // fp32: one wave per output, lanes stride over K, fixed-order butterfly reduction.
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,43 +23,49 @@ constexpr int kPitchU4 = 10;  // LDS row pitch in 16-byte units (128 bytes + 32 
 
 int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}), in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int TF, int RF, int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t* __restrict__ X,
                                                                  const uint16_t* __restrict__ V, int M, int K,
                                                                  int r, uint16_t* __restrict__ Thi,
                                                                  uint16_t* __restrict__ Tlo) {
-  constexpr int kRows = 16 * (TF + RF);    // staged rows per wave: X tokens, then V ranks
-  constexpr int kLoads = kRows / 8;        // 8 rows x 128 bytes per load instruction
+  constexpr int kRows = 16 * (TF + RF);  // staged rows per wave: X tokens, then V ranks
+  constexpr int kLoads = kRows / 8;      // 8 rows x 128 bytes per load instruction
   __shared__ u32x4_t stage[WAVES][kRows * kPitchU4];
   __shared__ f32x4_t red[(WAVES - 1) * RF * TF * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave; readfirstlane lets the compiler see that (scalar
+  // loop control instead of exec-mask loops)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane & 15, quad = lane >> 4;
   const int m0 = blockIdx.x * 16 * TF, j0 = blockIdx.y * 16 * RF;
   const int TK = (K + 63) / 64;
+  const bool half_tail = (K & 63) != 0;  // the last step holds 32 valid columns
   u32x4_t* st = stage[wave];
 
-  // this lane's rows: instruction t covers staged rows 8t .. 8t+7, chunk lane % 8 of a step
+  // this lane's rows: instruction t covers staged rows 8t .. 8t+7, 16-byte chunk lane % 8 of a step
+  // (rank rows are always valid: r is a multiple of 16)
   const int ch = lane & 7;
   const uint16_t* src[kLoads];
-  bool zrow[kLoads], is_v[kLoads];
   int dst[kLoads];
 #pragma unroll
   for (int t = 0; t < kLoads; ++t) {
     const int row = 8 * t + (lane >> 3);
     dst[t] = row * kPitchU4 + ch;
-    is_v[t] = row >= 16 * TF;
-    if (!is_v[t]) {
-      src[t] = X + (size_t)min(m0 + row, M - 1) * K + 8 * ch;
-      zrow[t] = false;
-    } else {
-      const int j = j0 + row - 16 * TF;
-      zrow[t] = j >= r;
-      src[t] = V + (size_t)min(j, r - 1) * K + 8 * ch;
-    }
+    src[t] = row < 16 * TF ? X + (size_t)min(m0 + row, M - 1) * K + 8 * ch
+                           : V + (size_t)(j0 + row - 16 * TF) * K + 8 * ch;
   }
   auto load = [&](int kc, u32x4_t (&v)[kLoads]) {
     int col = min(kc, TK - 1) * 64;
-    if (col + 8 * ch >= K) col -= 32;  // 32-column tail step: re-read valid columns (V zeroed there)
+    if (col + 8 * ch >= K) col -= 32;  // 32-column tail step: re-read valid columns (masked below)
 #pragma unroll
     for (int t = 0; t < kLoads; ++t) v[t] = *(const u32x4_t*)(src[t] + col);
   };
@@ -67,39 +76,47 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
 #pragma unroll
     for (int f = 0; f < TF; ++f) acc[a][f] = f32x4_t{0, 0, 0, 0};
 
-  // steps kc = wave, wave + WAVES, ...; a ring of D steps of loads stays in flight (slot u holds
-  // step s0 + u and is refilled with step s0 + u + D right after it is written to LDS)
+  // This wave's steps are kc = wave, wave + WAVES, ...; a ring of D steps of loads stays in flight:
+  // slot u holds step s0 + u and is refilled with step s0 + u + D right after it is written to LDS.
+  // The loop is branch-free: steps past the wave's last one (and the duplicated half of a 32-column
+  // tail step) contribute through a zeroed A operand, never through masked loads.
   const int my_steps = (TK - wave + WAVES - 1) / WAVES;
+  const int n_pad = (my_steps + D - 1) / D * D;
   u32x4_t ring[D][kLoads];
+  static_for<D>([&](auto uu) {  // issued in slot order (fenced), as the loop refills them
+    load(wave + decltype(uu)::value * WAVES, ring[decltype(uu)::value]);
+    asm volatile("" ::: "memory");
+  });
+  for (int s0 = 0; s0 < n_pad; s0 += D) {
+    static_for<D>([&](auto uu) {
+      constexpr int u = decltype(uu)::value;
+      const int s = s0 + u, kc = wave + s * WAVES;
 #pragma unroll
-  for (int u = 0; u < D; ++u) load(wave + u * WAVES, ring[u]);
-  for (int s0 = 0; s0 < my_steps; s0 += D) {
+      for (int t = 0; t < kLoads; ++t) st[dst[t]] = ring[u][t];
+      load(kc + D * WAVES, ring[u]);
+      // compiler-only fence: the refill stays in this step (not rotated into the next iteration,
+      // which would shorten the prefetch distance of this slot)
+      asm volatile("" ::: "memory");
+      // A operand (V rows j0 + 16 a + sub, dense columns 16 q .. 16 q + 15) as two fixed-pattern
+      // 2:4 halves; zero when the step is past this wave's last, or when it is the tail step and
+      // these columns are the re-read ones (q >= 2)
+      const bool live = s < my_steps && !(half_tail && kc == TK - 1 && quad >= 2);
+      const uint32_t keep = live ? ~0u : 0u;
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int kc = wave + (s0 + u) * WAVES;
-      if (s0 + u < my_steps) {  // wave-uniform
+      for (int a = 0; a < RF; ++a) {
+        const int vrow = (16 * TF + 16 * a + sub) * kPitchU4;
+        const u32x4_t d0 = st[vrow + 2 * quad] & keep, d1 = st[vrow + 2 * quad + 1] & keep;
+        const bf16x8_t a01 = as_bf16x8(u32x4_t{d0[0], d0[2], d1[0], d1[2]});
+        const bf16x8_t a23 = as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]});
 #pragma unroll
-        for (int t = 0; t < kLoads; ++t) {
-          const bool z = zrow[t] || (is_v[t] && kc * 64 + 8 * ch >= K);
-          st[dst[t]] = z ? u32x4_t{0, 0, 0, 0} : ring[u][t];
-        }
-        load(kc + D * WAVES, ring[u]);
-#pragma unroll
-        for (int a = 0; a < RF; ++a) {
-          const int vrow = (16 * TF + 16 * a + sub) * kPitchU4;
-          const u32x4_t d0 = st[vrow + 2 * quad], d1 = st[vrow + 2 * quad + 1];
-          const bf16x8_t a01 = as_bf16x8(u32x4_t{d0[0], d0[2], d1[0], d1[2]});
-          const bf16x8_t a23 = as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]});
-#pragma unroll
-          for (int f = 0; f < TF; ++f) {
-            const int xrow = (16 * f + sub) * kPitchU4;
-            const bf16x16_t bx = cat16(as_bf16x8(st[xrow + quad]), as_bf16x8(st[xrow + 4 + quad]));
-            acc[a][f] = smfmac16x16x64(a01, bx, acc[a][f], 0x4444);
-            acc[a][f] = smfmac16x16x64(a23, bx, acc[a][f], 0xEEEE);
-          }
+        for (int f = 0; f < TF; ++f) {
+          const int xrow = (16 * f + sub) * kPitchU4;
+          const bf16x16_t bx = cat16(as_bf16x8(st[xrow + quad]), as_bf16x8(st[xrow + 4 + quad]));
+          acc[a][f] = smfmac16x16x64(a01, bx, acc[a][f], 0x4444);
+          acc[a][f] = smfmac16x16x64(a23, bx, acc[a][f], 0xEEEE);
         }
       }
-    }
+    });
   }
 
   // combine the waves in order, then T (D rows = ranks j0 + 16 a + 4*(lane/16) + 0..3, column =
@@ -121,7 +138,6 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
 #pragma unroll
   for (int a = 0; a < RF; ++a) {
     const int j = j0 + 16 * a + 4 * quad;
-    if (j >= r) continue;
 #pragma unroll
     for (int f = 0; f < TF; ++f) {
       const int m = m0 + 16 * f + sub;
