@@ -2,24 +2,33 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input: for every layer of the
 workload, the 2:4 projection + pack of the residual R = W - U V (splr_prune24_pack), then the layer
-product Y = X S^T + (X V^T) U^T with the freshly packed S (splr_linear). Inputs are resident in
-HBM before timing starts. Each step reads a different copy of the weights and activations when
-one step's footprint is small, so repeated steps are not served from the 256 MB Infinity Cache.
+product Y = X S^T + (X V^T) U^T with the freshly packed S (splr_linear, issued as its two stages:
+splr_linear_stage1 computes T = X V^T, splr_linear_stage2 the sparse product and the low-rank
+epilogue). Inputs are resident in HBM before timing starts. Each step reads a different copy of the
+weights and activations when one step's footprint is small, so repeated steps are not served from
+the 256 MB Infinity Cache.
+
+Timed region (value): exactly K steps issued on one stream between two events. A spin kernel queued
+before the start event keeps the GPU busy while the host enqueues all K steps, so the region
+measures back-to-back GPU execution of the steps, not host launch gaps (measured here, replaying
+HIP graphs of the steps was slower than plain stream launches; --graph times that variant).
+Per-kernel region: the same K steps again, with an event after every library call.
 
 Prints one JSON line. `value` is dense-equivalent TFLOP/s (2 M n_out n_in per layer) of the whole
 step for the prefill workloads, or GB/s of the weight-side bytes (packed values, metadata, U, V)
-for the decode workload. Per-call durations come from HIP events recorded on the benchmark stream
-around every library call inside the timed loop.
+for the decode workload. `roofline` describes the kernel with the largest share of the step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -33,6 +42,10 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 (vector / MFMA)
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 MALL_DEFEAT_BYTES = 640 << 20  # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+# library call -> source file of the kernel it launches (the traffic figures are tied to it)
+KERNEL_SOURCE = {"pack": "pack.hip", "stage2": "linear_bf16.hip"}
 
 
 def parse():
@@ -43,6 +56,9 @@ def parse():
     p.add_argument("--workload", default="C2", help="C1..C5 (default: C2, the prefill q_proj layer)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     p.add_argument("--cpu-rows", type=int, default=0, help="token rows of the oracle sample (0 = auto)")
+    p.add_argument("--graph", action="store_true", help="replay the steps from HIP graphs (for comparison)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy 5 times (scale for HBM counters) and exit")
     return p.parse_args()
 
 
@@ -56,6 +72,37 @@ def pack_bytes(n_in, n_out, itemsize):
     return n_out * n_in * itemsize + n_out * n_in // 2 * itemsize + n_out * n_in // 8
 
 
+def stage2_work(L, itemsize, decode):
+    """Algorithmic work of splr_linear_stage2: the kept products (M n_out n_in / 2 multiply-adds)
+    plus the rank-r epilogue (M n_out r multiply-adds), in FLOP; or, for decode, the bytes it must
+    move: packed values, metadata, U, X, T (as the bfloat16 pair) and the float32 Y."""
+    if decode:
+        return (L.n_out * L.n_in // 2 * itemsize + L.n_out * L.n_in // 8 + L.n_out * L.r * itemsize
+                + L.M * L.n_in * itemsize + L.M * L.r * 4 + L.M * L.n_out * 4)
+    return L.M * L.n_out * L.n_in + 2 * L.M * L.n_out * L.r
+
+
+def source_sha(name):
+    path = os.path.join(ROOT, "sparse_rank_linear_prune24_amd", "csrc", name)
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary, or None
+    when there is none or the kernel source changed since the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    pat = re.compile(r"^\|\s*(\w+)\s*\|\s*(\w+)\s*\|\s*([0-9a-f]{16})\s*\|.*\|\s*([0-9.]+)\s*\|$")
+    want = source_sha(KERNEL_SOURCE[kernel])
+    with open(COUNTERS_FILE) as fh:
+        for line in fh:
+            m = pat.match(line.strip())
+            if m and m.group(1) == kernel and m.group(2) == workload:
+                return float(m.group(4)) if m.group(3) == want else None
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -64,6 +111,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes=src.numel(), calls=5)), flush=True)
+        return
 
     from sparse_rank_linear_prune24_amd import binding, configs, inputs
 
@@ -74,6 +130,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     binding.lib()
+    decode = cfg.M <= 64
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -96,10 +153,9 @@ def main():
     for c in range(copies):
         s = []
         for L in layers:
-            R = to_dev(L.R)
             ws_n = binding.workspace_bytes(L.M, L.n_out, L.n_in, L.r, tdt)
             s.append(dict(
-                R=R, X=to_dev(L.X), U=to_dev(L.U), V=to_dev(L.V),
+                R=to_dev(L.R), X=to_dev(L.X), U=to_dev(L.U), V=to_dev(L.V),
                 values=torch.empty((*binding.tiles(L.n_out, L.n_in), 64, 8), dtype=tdt, device=dev),
                 meta=torch.empty((*binding.tiles(L.n_out, L.n_in), 2, 16), dtype=torch.int32, device=dev),
                 Y=torch.empty((L.M, L.n_out), dtype=torch.float32, device=dev),
@@ -109,95 +165,141 @@ def main():
 
     stream = torch.cuda.Stream()
     n_layers = len(layers)
+    calls = ("pack", "stage1", "stage2")
 
     def step(i, ev=None):
+        """One step on `stream`; ev[c][li] is recorded after call c of layer li when given."""
         s = sets[i % copies]
-        if ev is not None:
-            ev[0].record(stream)
         for li, d in enumerate(s):
             binding.prune24_pack(d["R"], d["values"], d["meta"], stream=stream)
             if ev is not None:
-                ev[1 + li].record(stream)
+                ev[0][li].record(stream)
         for li, d in enumerate(s):
-            binding.linear(d["X"], d["values"], d["meta"], d["U"], d["V"], n_out=d["Y"].shape[1], out=d["Y"],
-                           workspace=d["ws"], stream=stream)
+            binding.linear_stage1(d["X"], d["V"], d["ws"], stream=stream)
             if ev is not None:
-                ev[1 + n_layers + li].record(stream)
+                ev[1][li].record(stream)
+            binding.linear_stage2(d["X"], d["values"], d["meta"], d["U"], d["ws"], n_out=d["Y"].shape[1],
+                                  out=d["Y"], stream=stream)
+            if ev is not None:
+                ev[2][li].record(stream)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
 
-        # timed region 1: the steps alone
+        # optional: one graph per weight copy, each holding exactly one step
+        graphs = []
+        if args.graph:
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(c)
+                graphs.append(g)
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+        spin_cycles = int(4e4 * args.steps * 3 * n_layers)  # ~60 us of GPU time per library call issued
+
+        # timed region: exactly K steps
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(spin_cycles)
         start.record(stream)
         for i in range(args.steps):
-            step(i)
+            if graphs:
+                graphs[i % copies].replay()
+            else:
+                step(i)
         end.record(stream)
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
 
-        # timed region 2: the same steps with an event after every library call
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(1 + 2 * n_layers)] for _ in range(args.steps)]
+        # per-kernel region: the same K steps, an event after every call; then pairs of events with
+        # nothing between them, whose interval (the cost of an event itself) is taken off each call
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(n_layers)] for _ in calls]
+               for _ in range(args.steps)]
+        first = torch.cuda.Event(enable_timing=True)
+        empty = [torch.cuda.Event(enable_timing=True) for _ in range(41)]
+        torch.cuda._sleep(spin_cycles)
+        first.record(stream)
         for i in range(args.steps):
             step(i, evs[i])
+        for e in empty:
+            e.record(stream)
         torch.cuda.synchronize()
+        event_ms = float(np.median([empty[j].elapsed_time(empty[j + 1]) for j in range(len(empty) - 1)]))
 
-    pack_ms = np.zeros(n_layers)
-    lin_ms = np.zeros(n_layers)
-    for ev in evs:
-        for li in range(n_layers):
-            pack_ms[li] += ev[li].elapsed_time(ev[1 + li]) if li == 0 else ev[li].elapsed_time(ev[1 + li])
-            prev = ev[n_layers] if li == 0 else ev[n_layers + li]
-            lin_ms[li] += prev.elapsed_time(ev[1 + n_layers + li])
-    pack_ms /= args.steps
-    lin_ms /= args.steps
+    # per-call durations (ms), averaged over the steps: the interval since the previous event
+    call_ms = {c: np.zeros(n_layers) for c in calls}
+    order = [(0, li) for li in range(n_layers)] + [(c, li) for li in range(n_layers) for c in (1, 2)]
+    for i, ev in enumerate(evs):
+        prev = first if i == 0 else evs[i - 1][2][n_layers - 1]
+        for c, li in order:
+            call_ms[calls[c]][li] += prev.elapsed_time(ev[c][li])
+            prev = ev[c][li]
+    for c in calls:
+        call_ms[c] = call_ms[c] / args.steps - event_ms
 
     ms_per_step = total_ms / args.steps
     flop_step = sum(2 * L.M * L.n_out * L.n_in for L in layers)
     wbytes_step = sum(layer_bytes(L.n_in, L.n_out, L.r, isz) for L in layers)
     pbytes_step = sum(pack_bytes(L.n_in, L.n_out, isz) for L in layers)
-    decode = cfg.M <= 64
+    s2_work = sum(stage2_work(L, isz, decode) for L in layers)
 
     per_layer = []
     for li, L in enumerate(layers):
-        fl = 2 * L.M * L.n_out * L.n_in
-        wb = layer_bytes(L.n_in, L.n_out, L.r, isz)
         pb = pack_bytes(L.n_in, L.n_out, isz)
+        lin = call_ms["stage1"][li] + call_ms["stage2"][li]
         per_layer.append(dict(
-            layer=L.name, pack_us=round(pack_ms[li] * 1e3, 2), pack_GBps=round(pb / (pack_ms[li] * 1e-3) / 1e9, 1),
-            linear_us=round(lin_ms[li] * 1e3, 2), linear_TFLOPs=round(fl / (lin_ms[li] * 1e-3) / 1e12, 1),
-            linear_weight_GBps=round(wb / (lin_ms[li] * 1e-3) / 1e9, 1)))
+            layer=L.name, pack_us=round(call_ms["pack"][li] * 1e3, 2),
+            pack_GBps=round(pb / (call_ms["pack"][li] * 1e-3) / 1e9, 1),
+            stage1_us=round(call_ms["stage1"][li] * 1e3, 2), stage2_us=round(call_ms["stage2"][li] * 1e3, 2),
+            linear_dense_equiv_TFLOPs=round(2 * L.M * L.n_out * L.n_in / (lin * 1e-3) / 1e12, 1),
+            linear_weight_GBps=round(layer_bytes(L.n_in, L.n_out, L.r, isz) / (lin * 1e-3) / 1e9, 1)))
 
-    peak_mfma = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
-    lin_total_s = lin_ms.sum() * 1e-3
-    if decode:
-        value = wbytes_step / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        ach = wbytes_step / lin_total_s / 1e9
+    # roofline of the kernel with the largest share of the step
+    pack_s, s2_s = call_ms["pack"].sum() * 1e-3, call_ms["stage2"].sum() * 1e-3
+    wl = cfg.name
+    if pack_s >= s2_s:
+        ach = pbytes_step / pack_s / 1e9
         roofline = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                        frac=round(ach / PEAK_HBM_GBPS, 4), traffic=None, kernel="splr_linear (decode)")
+                        frac=round(ach / PEAK_HBM_GBPS, 4), traffic=recorded_traffic("pack", wl),
+                        kernel="prune24_pack_kernel", work="bytes read + written: R, packed values, metadata")
+    elif decode:
+        ach = s2_work / s2_s / 1e9
+        roofline = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                        frac=round(ach / PEAK_HBM_GBPS, 4), traffic=recorded_traffic("stage2", wl),
+                        kernel="linear_decode_kernel", work="bytes: packed values, metadata, U, X, T, Y")
     else:
-        value = flop_step / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        ach = flop_step / lin_total_s / 1e12
-        roofline = dict(bound="mfma", achieved=round(ach, 1), peak=peak_mfma, unit="TFLOP/s",
-                        frac=round(ach / peak_mfma, 4), traffic=None, kernel="splr_linear (prefill)")
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+        ach = s2_work / s2_s / 1e12
+        roofline = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
+                        frac=round(ach / peak, 4), traffic=recorded_traffic("stage2", wl),
+                        kernel="linear_prefill_kernel",
+                        work="algorithmic FLOP: kept 2:4 products (M n_out n_in) + rank-r epilogue (2 M n_out r)",
+                        dense_equiv_TFLOPs=round(flop_step / s2_s / 1e12, 1))
+
+    if decode:
+        value, unit = wbytes_step / (ms_per_step * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = flop_step / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
 
     out = dict(
         metric=METRIC, value=round(value, 2), unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype=dtype, data="synthetic",
         config=dict(workload=f"{cfg.name}: {cfg.description}", tokens=cfg.M, rank=cfg.r,
-                    layers=[f"{n}:{k}->{o}" for n, k, o in cfg.layers], step="prune24_pack on every layer's "
-                    "residual, then splr_linear on every layer", parallelism="single GPU", copies_rotated=copies),
+                    layers=[f"{n}:{k}->{o}" for n, k, o in cfg.layers],
+                    step="prune24_pack on every layer's residual, then splr_linear (stage 1 + stage 2) on every "
+                         "layer", launch="graph replay" if graphs else "stream, queue pre-filled", parallelism="single GPU",
+                    copies_rotated=copies),
         roofline=roofline,
         kernels=dict(per_layer=per_layer,
-                     pack_GBps=round(pbytes_step / (pack_ms.sum() * 1e-3) / 1e9, 1),
-                     pack_frac_hbm=round(pbytes_step / (pack_ms.sum() * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                     linear_TFLOPs=round(flop_step / lin_total_s / 1e12, 1),
-                     linear_weight_GBps=round(wbytes_step / lin_total_s / 1e9, 1)),
+                     pack_GBps=round(pbytes_step / pack_s / 1e9, 1),
+                     linear_dense_equiv_TFLOPs=round(
+                         flop_step / ((call_ms["stage1"].sum() + call_ms["stage2"].sum()) * 1e-3) / 1e12, 1)),
+        event_overhead_us=round(event_ms * 1e3, 3),
         input_generation_s=round(gen_s, 1),
     )
 

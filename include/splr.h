@@ -93,7 +93,8 @@ splr_status_t splr_packed_bytes(int64_t n_out, int64_t n_in, splr_dtype_t dtype,
 
 /*
  * splr_linear_workspace_bytes -- device workspace that splr_linear needs for these sizes
- * (0 when none).  It holds the first low-rank stage T = X V^T.
+ * (0 when none).  It holds the first low-rank stage T = X V^T and, for larger problems, float32
+ * partial sums of T over slices of n_in (at most 16 slices).
  */
 size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64_t r,
                                    splr_dtype_t dtype);
@@ -121,6 +122,28 @@ splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* va
                           const uint32_t* meta, int64_t n_out, const void* U, const void* V,
                           int64_t r, splr_dtype_t dtype, float* Y, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * splr_linear_stage1 / splr_linear_stage2 -- the two stages of splr_linear, for callers that want
+ * to schedule them apart (for example stage 1 on another stream while the residual is packed).
+ * splr_linear(...) is exactly stage1 followed by stage2 on one stream with one workspace.
+ *
+ *   stage1: T = X V^T into `workspace` (the first low-rank stage; nothing else is read or
+ *           written).  No-op when r == 0.
+ *   stage2: Y = X S^T + T U^T, reading T from `workspace` as left there by stage1 with the same
+ *           X, M, n_in, r and dtype (stage2 does not read V).
+ * The workspace must stay untouched between the two stages, and stage2 must be ordered after
+ * stage1 (same stream, or an event).  Arguments mean what they mean for splr_linear; V may be NULL
+ * for stage2 and values, meta, U, Y are not used by stage1.
+ * Errors: as splr_linear, for the arguments that stage uses.
+ */
+splr_status_t splr_linear_stage1(const void* X, int64_t M, int64_t n_in, const void* V, int64_t r,
+                                 splr_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+splr_status_t splr_linear_stage2(const void* X, int64_t M, int64_t n_in, const void* values,
+                                 const uint32_t* meta, int64_t n_out, const void* U, int64_t r,
+                                 splr_dtype_t dtype, float* Y, const void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * splr_dense_reconstruct -- W_hat = S + U V as a dense float32 matrix (LoSparse §3: the weight is

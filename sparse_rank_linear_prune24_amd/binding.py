@@ -25,7 +25,8 @@ SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
 EXPORTS = ("splr_prune24_pack", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
-           "splr_dense_reconstruct", "splr_status_string", "splr_version")
+           "splr_linear_stage1", "splr_linear_stage2", "splr_dense_reconstruct", "splr_status_string",
+           "splr_version")
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 _lib = None
@@ -52,6 +53,10 @@ def lib() -> ctypes.CDLL:
         L.splr_linear_workspace_bytes.restype = _SZ
         L.splr_linear.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P, _SZ, _P]
         L.splr_linear.restype = _I32
+        L.splr_linear_stage1.argtypes = [_P, _I64, _I64, _P, _I64, _I32, _P, _SZ, _P]
+        L.splr_linear_stage1.restype = _I32
+        L.splr_linear_stage2.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P]
+        L.splr_linear_stage2.restype = _I32
         L.splr_dense_reconstruct.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]
         L.splr_dense_reconstruct.restype = _I32
         L.splr_status_string.argtypes = [_I32]
@@ -121,10 +126,7 @@ def workspace_bytes(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype) -
     return int(lib().splr_linear_workspace_bytes(M, n_out, n_in, r, code))
 
 
-def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
-           V: Optional[torch.Tensor], n_out: Optional[int] = None, out: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Y [M, n_out] float32 = X S^T + (X V^T) U^T (n_out defaults to U's rows, else 16 * TR)."""
+def _linear_args(X, values, U, n_out, out, workspace, with_workspace=True):
     M, n_in = X.shape
     if n_out is None:
         n_out = U.shape[0] if U is not None else values.shape[0] * 16
@@ -132,12 +134,44 @@ def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optiona
     if out is None:
         out = torch.empty((M, n_out), dtype=torch.float32, device=X.device)
     need = workspace_bytes(M, n_out, n_in, r, X.dtype)
-    if workspace is None and need:
+    if workspace is None and need and with_workspace:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return M, n_in, n_out, r, out, workspace, ws_bytes
+
+
+def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
+           V: Optional[torch.Tensor], n_out: Optional[int] = None, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y [M, n_out] float32 = X S^T + (X V^T) U^T (n_out defaults to U's rows, else 16 * TR)."""
+    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, U, n_out, out, workspace)
     _check("splr_linear", lib().splr_linear(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
                                             _dev(U, "U"), _dev(V, "V"), r, _dtype_code(X), _dev(out, "out"),
                                             _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return out
+
+
+def linear_stage1(X: torch.Tensor, V: Optional[torch.Tensor], workspace: torch.Tensor, n_out: int = 0,
+                  stream=None) -> torch.Tensor:
+    """First low-rank stage T = X V^T into `workspace` (sized by workspace_bytes); returns it."""
+    M, n_in = X.shape
+    r = 0 if V is None else V.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("splr_linear_stage1", lib().splr_linear_stage1(_dev(X, "X"), M, n_in, _dev(V, "V"), r, _dtype_code(X),
+                                                          _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return workspace
+
+
+def linear_stage2(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
+                  workspace: Optional[torch.Tensor], n_out: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Y = X S^T + T U^T with T left in `workspace` by linear_stage1 (same X and r)."""
+    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, U, n_out, out, workspace,
+                                                               with_workspace=False)
+    _check("splr_linear_stage2",
+           lib().splr_linear_stage2(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
+                                    _dev(U, "U"), r, _dtype_code(X), _dev(out, "out"), _dev(workspace, "workspace"),
+                                    ws_bytes, _stream(stream)))
     return out
 
 

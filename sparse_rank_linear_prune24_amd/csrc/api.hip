@@ -33,9 +33,8 @@ splr_status_t check_rank(int64_t r) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t workspace_bytes(int64_t M, int64_t n_in, int64_t r, splr_dtype_t dtype) {
-  (void)n_in;
   if (r == 0) return 0;
-  return round_up(splr::lowrank_workspace_bytes(M, r, dtype == SPLR_BF16), 256);
+  return round_up(splr::lowrank_workspace_bytes(M, n_in, r, dtype == SPLR_BF16), 256);
 }
 
 splr_status_t from_hip(hipError_t e) { return e == hipSuccess ? SPLR_OK : SPLR_ERR_HIP; }
@@ -74,35 +73,70 @@ size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64
   return workspace_bytes(M, n_in, r, dtype);
 }
 
-splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                          int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, float* Y,
-                          void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (!X || !values || !meta || !Y) return SPLR_ERR_NULL;
-  if (r > 0 && (!U || !V)) return SPLR_ERR_NULL;
+namespace {
+
+// Argument checks shared by splr_linear and its two stages. V is checked only when need_v.
+splr_status_t check_linear(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                           int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, const float* Y,
+                           const void* workspace, size_t ws_bytes, bool need_sparse, bool need_v) {
+  if (!X) return SPLR_ERR_NULL;
+  if (need_sparse && (!values || !meta || !Y || (r > 0 && !U))) return SPLR_ERR_NULL;
+  if (need_v && r > 0 && !V) return SPLR_ERR_NULL;
   splr_status_t s = check_in(n_in);
   if (s == SPLR_OK) s = check_rows(M, n_in);
-  if (s == SPLR_OK) s = check_rows(n_out, n_in);
+  if (s == SPLR_OK && need_sparse) s = check_rows(n_out, n_in);
   if (s == SPLR_OK) s = check_rank(r);
-  if (s == SPLR_OK && M * n_out > kMaxElems) s = SPLR_ERR_SHAPE;
+  if (s == SPLR_OK && need_sparse && M * n_out > kMaxElems) s = SPLR_ERR_SHAPE;
   if (s != SPLR_OK) return s;
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
-  if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(Y)) return SPLR_ERR_ALIGN;
-  if (r > 0 && (!aligned16(U) || !aligned16(V))) return SPLR_ERR_ALIGN;
+  if (!aligned16(X)) return SPLR_ERR_ALIGN;
+  if (need_sparse && (!aligned16(values) || !aligned16(meta) || !aligned16(Y) || (r > 0 && !aligned16(U))))
+    return SPLR_ERR_ALIGN;
+  if (need_v && r > 0 && !aligned16(V)) return SPLR_ERR_ALIGN;
   const size_t need = workspace_bytes(M, n_in, r, dtype);
   if (need > 0 && (!workspace || ws_bytes < need)) return SPLR_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return SPLR_ERR_ALIGN;
+  return SPLR_OK;
+}
 
-  const bool bf16 = dtype == SPLR_BF16;
-  float* T = static_cast<float*>(workspace);
-  hipError_t e = splr::launch_lowrank(X, V, M, n_in, r, bf16, workspace, stream);
-  if (e != hipSuccess) return SPLR_ERR_HIP;
-  if (bf16)
-    e = splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, (const uint16_t*)workspace,
-                                 (const uint16_t*)workspace + (size_t)M * r, Y, stream);
-  else
-    e = splr::launch_linear_f32((const float*)X, M, n_in, (const float*)values, meta, n_out, (const float*)U, r, T,
-                                Y, stream);
-  return from_hip(e);
+splr_status_t run_stage2(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                         int64_t n_out, const void* U, int64_t r, splr_dtype_t dtype, float* Y, void* workspace,
+                         hipStream_t stream) {
+  if (dtype == SPLR_BF16)
+    return from_hip(splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, (const uint16_t*)workspace,
+                                             (const uint16_t*)workspace + (size_t)M * r, Y, stream));
+  return from_hip(splr::launch_linear_f32((const float*)X, M, n_in, (const float*)values, meta, n_out,
+                                          (const float*)U, r, (const float*)workspace, Y, stream));
+}
+
+}  // namespace
+
+splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                          int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, float* Y,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const splr_status_t s =
+      check_linear(X, M, n_in, values, meta, n_out, U, V, r, dtype, Y, workspace, ws_bytes, true, true);
+  if (s != SPLR_OK) return s;
+  if (splr::launch_lowrank(X, V, M, n_in, r, dtype == SPLR_BF16, workspace, stream) != hipSuccess)
+    return SPLR_ERR_HIP;
+  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, workspace, stream);
+}
+
+splr_status_t splr_linear_stage1(const void* X, int64_t M, int64_t n_in, const void* V, int64_t r,
+                                 splr_dtype_t dtype, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const splr_status_t s =
+      check_linear(X, M, n_in, nullptr, nullptr, 0, nullptr, V, r, dtype, nullptr, workspace, ws_bytes, false, true);
+  if (s != SPLR_OK) return s;
+  return from_hip(splr::launch_lowrank(X, V, M, n_in, r, dtype == SPLR_BF16, workspace, stream));
+}
+
+splr_status_t splr_linear_stage2(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                                 int64_t n_out, const void* U, int64_t r, splr_dtype_t dtype, float* Y,
+                                 const void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const splr_status_t s =
+      check_linear(X, M, n_in, values, meta, n_out, U, nullptr, r, dtype, Y, workspace, ws_bytes, true, false);
+  if (s != SPLR_OK) return s;
+  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, const_cast<void*>(workspace), stream);
 }
 
 splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, const void* U, const void* V,

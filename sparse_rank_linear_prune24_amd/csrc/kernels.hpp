@@ -11,8 +11,9 @@ hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool 
                                uint32_t* meta, hipStream_t stream);
 
 // First low-rank stage T = X V^T, written at the start of the workspace: float32 [M][r] for the
-// fp32 path; for the bf16 path a bfloat16 pair, hi [M][r] then lo [M][r] (T ~= hi + lo).
-size_t lowrank_workspace_bytes(int64_t M, int64_t r, bool bf16);
+// fp32 path; for the bf16 path a bfloat16 pair, hi [M][r] then lo [M][r] (T ~= hi + lo), followed by
+// float32 partial sums over K slices when the pre-pass splits K.
+size_t lowrank_workspace_bytes(int64_t M, int64_t n_in, int64_t r, bool bf16);
 hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16,
                           void* workspace, hipStream_t stream);
 

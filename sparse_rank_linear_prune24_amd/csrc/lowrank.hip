@@ -1,15 +1,19 @@
 // First stage of the low-rank product, T = X V^T (LoSparse page, §3.2: the input is multiplied by
 // the thin factors; in the orientation used here X [M x n_in] times V^T [n_in x r]).
 //
-// bf16: a workgroup owns 16*TF tokens x 16*RF ranks over the whole of K; its waves take
-// interleaved 64-column K steps, each wave staging its own X and V rows in a private LDS region
-// (row-contiguous loads, padded pitch) with several steps of loads in flight, and feed gfx950's
-// structured-sparse MFMA: X is the dense B operand; V is the A operand, dense V being the sum of
-// two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of every group of four columns).
-// The waves' partial sums are combined through LDS in wave order (deterministic, no atomics, no
-// communication between workgroups), and T is written as a bfloat16 pair: hi = T rounded to nearest
-// even, lo = (T - hi) rounded to nearest even (hi + lo carries about 16 significant bits).
+// bf16: a workgroup owns 16*TF tokens x 16*RF ranks (all of r when r is a multiple of 64) over one
+// slice of K; its waves take interleaved 64-column K steps of the slice, each wave staging its own X
+// and V rows in a private LDS region (row-contiguous loads, padded pitch) with several steps of
+// loads in flight, and feed gfx950's structured-sparse MFMA: X is the dense B operand; V is the A
+// operand, dense V being the sum of two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of
+// every group of four columns). Covering all ranks in one workgroup stages each X row once; the K
+// slices give the chip enough workgroups. The waves' partial sums are combined through LDS in wave
+// order; with one slice T is written directly, otherwise each slice writes a float32 partial and a
+// second kernel adds the slices in slice order (deterministic, no atomics). T is stored as a
+// bfloat16 pair: hi = T rounded to nearest even, lo = (T - hi) rounded to nearest even (hi + lo
+// carries about 16 significant bits).
 // fp32: one wave per output, lanes stride over K, fixed-order butterfly reduction.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -33,11 +37,27 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Round T to the bfloat16 pair (hi, lo) for 4 consecutive ranks and store both planes.
+__device__ __forceinline__ void store_hi_lo(const f32x4_t t, uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = float_to_bf16_bits(t[e]);
+    l[e] = float_to_bf16_bits(t[e] - bf16_bits_to_float(h[e]));
+  }
+  *(u32x2_t*)hi = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  *(u32x2_t*)lo = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+// Grid (token blocks, rank blocks, K slices); slice z covers K steps [z*steps_per_slice, ...).
+// part == nullptr: one slice, write Thi/Tlo. Otherwise write float32 partial part[z][m][j].
 template <int TF, int RF, int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t* __restrict__ X,
                                                                  const uint16_t* __restrict__ V, int M, int K,
-                                                                 int r, uint16_t* __restrict__ Thi,
-                                                                 uint16_t* __restrict__ Tlo) {
+                                                                 int r, int steps_per_slice,
+                                                                 uint16_t* __restrict__ Thi,
+                                                                 uint16_t* __restrict__ Tlo,
+                                                                 float* __restrict__ part) {
   constexpr int kRows = 16 * (TF + RF);  // staged rows per wave: X tokens, then V ranks
   constexpr int kLoads = kRows / 8;      // 8 rows x 128 bytes per load instruction
   __shared__ u32x4_t stage[WAVES][kRows * kPitchU4];
@@ -48,11 +68,12 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
   const int sub = lane & 15, quad = lane >> 4;
   const int m0 = blockIdx.x * 16 * TF, j0 = blockIdx.y * 16 * RF;
   const int TK = (K + 63) / 64;
+  const int kb = blockIdx.z * steps_per_slice, ke = min(TK, kb + steps_per_slice);
   const bool half_tail = (K & 63) != 0;  // the last step holds 32 valid columns
   u32x4_t* st = stage[wave];
 
   // this lane's rows: instruction t covers staged rows 8t .. 8t+7, 16-byte chunk lane % 8 of a step
-  // (rank rows are always valid: r is a multiple of 16)
+  // (rank rows are always valid: 16*RF divides r)
   const int ch = lane & 7;
   const uint16_t* src[kLoads];
   int dst[kLoads];
@@ -76,21 +97,21 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
 #pragma unroll
     for (int f = 0; f < TF; ++f) acc[a][f] = f32x4_t{0, 0, 0, 0};
 
-  // This wave's steps are kc = wave, wave + WAVES, ...; a ring of D steps of loads stays in flight:
-  // slot u holds step s0 + u and is refilled with step s0 + u + D right after it is written to LDS.
-  // The loop is branch-free: steps past the wave's last one (and the duplicated half of a 32-column
-  // tail step) contribute through a zeroed A operand, never through masked loads.
-  const int my_steps = (TK - wave + WAVES - 1) / WAVES;
+  // This wave's steps are kc = kb + wave, kb + wave + WAVES, ... < ke; a ring of D steps of loads
+  // stays in flight: slot u holds step s0 + u and is refilled with step s0 + u + D right after it is
+  // written to LDS. The loop is branch-free: steps past the wave's last one (and the duplicated half
+  // of a 32-column tail step) contribute through a zeroed A operand, never through masked loads.
+  const int my_steps = max(0, (ke - kb - wave + WAVES - 1) / WAVES);
   const int n_pad = (my_steps + D - 1) / D * D;
   u32x4_t ring[D][kLoads];
   static_for<D>([&](auto uu) {  // issued in slot order (fenced), as the loop refills them
-    load(wave + decltype(uu)::value * WAVES, ring[decltype(uu)::value]);
+    load(kb + wave + decltype(uu)::value * WAVES, ring[decltype(uu)::value]);
     asm volatile("" ::: "memory");
   });
   for (int s0 = 0; s0 < n_pad; s0 += D) {
     static_for<D>([&](auto uu) {
       constexpr int u = decltype(uu)::value;
-      const int s = s0 + u, kc = wave + s * WAVES;
+      const int s = s0 + u, kc = kb + wave + s * WAVES;
 #pragma unroll
       for (int t = 0; t < kLoads; ++t) st[dst[t]] = ring[u][t];
       load(kc + D * WAVES, ring[u]);
@@ -102,6 +123,12 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
       // these columns are the re-read ones (q >= 2)
       const bool live = s < my_steps && !(half_tail && kc == TK - 1 && quad >= 2);
       const uint32_t keep = live ? ~0u : 0u;
+      bf16x16_t bx[TF];
+#pragma unroll
+      for (int f = 0; f < TF; ++f) {
+        const int xrow = (16 * f + sub) * kPitchU4;
+        bx[f] = cat16(as_bf16x8(st[xrow + quad]), as_bf16x8(st[xrow + 4 + quad]));
+      }
 #pragma unroll
       for (int a = 0; a < RF; ++a) {
         const int vrow = (16 * TF + 16 * a + sub) * kPitchU4;
@@ -110,17 +137,15 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
         const bf16x8_t a23 = as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]});
 #pragma unroll
         for (int f = 0; f < TF; ++f) {
-          const int xrow = (16 * f + sub) * kPitchU4;
-          const bf16x16_t bx = cat16(as_bf16x8(st[xrow + quad]), as_bf16x8(st[xrow + 4 + quad]));
-          acc[a][f] = smfmac16x16x64(a01, bx, acc[a][f], 0x4444);
-          acc[a][f] = smfmac16x16x64(a23, bx, acc[a][f], 0xEEEE);
+          acc[a][f] = smfmac16x16x64(a01, bx[f], acc[a][f], 0x4444);
+          acc[a][f] = smfmac16x16x64(a23, bx[f], acc[a][f], 0xEEEE);
         }
       }
     });
   }
 
-  // combine the waves in order, then T (D rows = ranks j0 + 16 a + 4*(lane/16) + 0..3, column =
-  // token m0 + 16 f + lane%16) as hi / lo bfloat16 planes
+  // combine the waves in order; D rows = ranks j0 + 16 a + 4*(lane/16) + 0..3, column = token
+  // m0 + 16 f + lane%16
   if (wave > 0) {
 #pragma unroll
     for (int a = 0; a < RF; ++a)
@@ -135,6 +160,7 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
     for (int a = 0; a < RF; ++a)
 #pragma unroll
       for (int f = 0; f < TF; ++f) acc[a][f] += red[(((w - 1) * RF + a) * TF + f) * 64 + lane];
+  float* pz = part ? part + (size_t)blockIdx.z * M * r : nullptr;
 #pragma unroll
   for (int a = 0; a < RF; ++a) {
     const int j = j0 + 16 * a + 4 * quad;
@@ -142,16 +168,32 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
     for (int f = 0; f < TF; ++f) {
       const int m = m0 + 16 * f + sub;
       if (m >= M) continue;
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = float_to_bf16_bits(acc[a][f][e]);
-        l[e] = float_to_bf16_bits(acc[a][f][e] - bf16_bits_to_float(h[e]));
-      }
-      *(u32x2_t*)(Thi + (size_t)m * r + j) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *(u32x2_t*)(Tlo + (size_t)m * r + j) = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      const size_t o = (size_t)m * r + j;
+      if (pz)
+        *(f32x4_t*)(pz + o) = acc[a][f];
+      else
+        store_hi_lo(acc[a][f], Thi + o, Tlo + o);
     }
   }
+}
+
+// T = sum over slices z = 0, 1, ... of part[z] (in that order), stored as the bfloat16 pair. All
+// slice loads are issued before the first add (a load-add chain would wait once per slice).
+constexpr int kMaxSlices = 16;
+__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __restrict__ part, int slices,
+                                                            int64_t n4, int64_t stride, uint16_t* __restrict__ Thi,
+                                                            uint16_t* __restrict__ Tlo) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4_t v[kMaxSlices];
+#pragma unroll
+  for (int z = 0; z < kMaxSlices; ++z)
+    v[z] = z < slices ? *(const f32x4_t*)(part + (size_t)z * stride + 4 * i) : f32x4_t{0, 0, 0, 0};
+  f32x4_t t = v[0];
+#pragma unroll
+  for (int z = 1; z < kMaxSlices; ++z)
+    if (z < slices) t += v[z];
+  store_hi_lo(t, Thi + 4 * i, Tlo + 4 * i);
 }
 
 __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restrict__ X, const float* __restrict__ V,
@@ -171,9 +213,43 @@ __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restric
 
 }  // namespace
 
-size_t lowrank_workspace_bytes(int64_t M, int64_t r, bool bf16) {
+namespace {
+
+// bf16 pre-pass shape: ranks per workgroup, and the number of K slices that gives the chip at least
+// ~256 workgroups (at most 16 slices, at most one per K step).
+struct LowrankShape {
+  int tf, rf, slices, steps_per_slice;
+};
+
+LowrankShape lowrank_shape(int64_t M, int64_t n_in, int64_t r) {
+  LowrankShape sh;
+  sh.tf = M <= 16 ? 1 : 2;
+  sh.rf = r % 64 == 0 ? 4 : (r % 32 == 0 ? 2 : 1);
+  const int64_t TK = (n_in + 63) / 64;
+  const int64_t base = ceil_div(M, 16 * sh.tf) * (r / (16 * sh.rf));
+  int64_t slices = std::min<int64_t>(std::min<int64_t>(kMaxSlices, TK), std::max<int64_t>(1, ceil_div(256, base)));
+  sh.steps_per_slice = (int)ceil_div(TK, slices);
+  sh.slices = (int)ceil_div(TK, sh.steps_per_slice);
+  return sh;
+}
+
+template <int TF, int RF>
+void launch_part(const LowrankShape& sh, const void* X, const void* V, int64_t M, int64_t n_in, int64_t r,
+                 uint16_t* Thi, uint16_t* Tlo, float* part, hipStream_t stream) {
+  dim3 grid((unsigned)cdiv(M, 16 * TF), (unsigned)(r / (16 * RF)), (unsigned)sh.slices);
+  lowrank_bf16_kernel<TF, RF, 4, 2><<<grid, dim3(256), 0, stream>>>((const uint16_t*)X, (const uint16_t*)V, (int)M,
+                                                                  (int)n_in, (int)r, sh.steps_per_slice, Thi, Tlo,
+                                                                  part);
+}
+
+}  // namespace
+
+size_t lowrank_workspace_bytes(int64_t M, int64_t n_in, int64_t r, bool bf16) {
   if (r == 0) return 0;
-  return bf16 ? (size_t)M * r * 2 * sizeof(uint16_t) : (size_t)M * r * sizeof(float);
+  if (!bf16) return (size_t)M * r * sizeof(float);
+  const LowrankShape sh = lowrank_shape(M, n_in, r);
+  const size_t planes = (size_t)M * r * 2 * sizeof(uint16_t);
+  return sh.slices > 1 ? planes + (size_t)sh.slices * M * r * sizeof(float) : planes;
 }
 
 hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16,
@@ -182,14 +258,21 @@ hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in,
   if (bf16) {
     uint16_t* Thi = (uint16_t*)workspace;
     uint16_t* Tlo = Thi + (size_t)M * r;
-    if (M <= 16) {  // few tokens: more waves per workgroup stream K
-      dim3 grid((unsigned)cdiv(M, 16), (unsigned)cdiv(r, 16));
-      lowrank_bf16_kernel<1, 1, 16, 4><<<grid, dim3(1024), 0, stream>>>(
-          (const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in, (int)r, Thi, Tlo);
+    const LowrankShape sh = lowrank_shape(M, n_in, r);
+    float* part = sh.slices > 1 ? (float*)(Tlo + (size_t)M * r) : nullptr;
+    if (sh.tf == 1) {
+      if (sh.rf == 4) launch_part<1, 4>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
+      else if (sh.rf == 2) launch_part<1, 2>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
+      else launch_part<1, 1>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
     } else {
-      dim3 grid((unsigned)cdiv(M, 32), (unsigned)cdiv(r, 16));
-      lowrank_bf16_kernel<2, 1, 4, 4><<<grid, dim3(256), 0, stream>>>(
-          (const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in, (int)r, Thi, Tlo);
+      if (sh.rf == 4) launch_part<2, 4>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
+      else if (sh.rf == 2) launch_part<2, 2>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
+      else launch_part<2, 1>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
+    }
+    if (part) {
+      const int64_t n4 = M * r / 4;
+      lowrank_reduce_kernel<<<dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, stream>>>(part, sh.slices, n4, M * r,
+                                                                                         Thi, Tlo);
     }
   } else {
     const int64_t waves = M * r;

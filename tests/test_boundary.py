@@ -94,6 +94,30 @@ def test_linear_validation():
     assert ws(0, 32, 64, 16, 1) == 0
 
 
+def test_stage_validation():
+    lib = binding.lib()
+    s1, s2 = lib.splr_linear_stage1, lib.splr_linear_stage2
+    wsb = lib.splr_linear_workspace_bytes(16, 32, 64, 16, 1)
+    # stage 1: X, V, workspace
+    assert s1(None, 16, 64, A, 16, 1, A, wsb, None) == NULL
+    assert s1(A, 16, 64, None, 16, 1, A, wsb, None) == NULL
+    assert s1(A, 16, 40, A, 16, 1, A, wsb, None) == SHAPE
+    assert s1(A, 0, 64, A, 16, 1, A, wsb, None) == SHAPE
+    assert s1(A, 16, 64, A, 24, 1, A, wsb, None) == SHAPE
+    assert s1(A, 16, 64, A, 16, 3, A, wsb, None) == DTYPE
+    assert s1(A, 16, 64, MIS, 16, 1, A, wsb, None) == ALIGN
+    assert s1(A, 16, 64, A, 16, 1, None, wsb, None) == WORKSPACE
+    assert s1(A, 16, 64, A, 16, 1, A, wsb - 1, None) == WORKSPACE
+    # stage 2: X, values, meta, U, Y, workspace (V is not an argument)
+    assert s2(A, 16, 64, None, A, 32, A, 16, 1, A, A, wsb, None) == NULL
+    assert s2(A, 16, 64, A, A, 32, None, 16, 1, A, A, wsb, None) == NULL
+    assert s2(A, 16, 64, A, A, 32, A, 16, 1, None, A, wsb, None) == NULL
+    assert s2(A, 16, 64, A, A, 0, A, 16, 1, A, A, wsb, None) == SHAPE
+    assert s2(A, 16, 64, A, A, 32, A, 16, 1, A, MIS, wsb, None) == ALIGN
+    assert s2(A, 16, 64, A, A, 32, MIS, 16, 1, A, A, wsb, None) == ALIGN
+    assert s2(A, 16, 64, A, A, 32, A, 16, 1, A, None, wsb, None) == WORKSPACE
+
+
 def test_reconstruct_validation():
     f = binding.lib().splr_dense_reconstruct
     assert f(None, A, A, A, 4, 64, 16, 1, A, None) == NULL

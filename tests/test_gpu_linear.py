@@ -53,6 +53,8 @@ SHAPES = [
     (1, 64, 16, 16), (5, 32, 40, 16), (16, 256, 48, 32), (17, 96, 33, 16), (33, 512, 130, 48),
     (64, 320, 64, 0), (65, 1024, 129, 64), (130, 96, 257, 16), (200, 2080, 300, 64), (257, 512, 513, 128),
     (1024, 1024, 384, 64),
+    # low-rank pre-pass: many K slices (decode), rank counts that are not a multiple of 64
+    (16, 4096, 64, 64), (40, 1056, 100, 80), (128, 4096, 256, 192),
 ]
 
 
@@ -171,3 +173,20 @@ def test_workspace_errors():
     with pytest.raises(binding.SplrError) as e:
         binding.linear(Xd, vd, md, Ud, Vd, workspace=small)
     assert e.value.status == 6
+
+
+@pytest.mark.parametrize("dtype,M,n_in,n_out,r", [("bf16", 200, 2080, 300, 64), ("bf16", 16, 4096, 64, 64),
+                                                  ("bf16", 65, 512, 96, 0), ("fp32", 70, 160, 33, 32)])
+def test_stages_equal_linear(dtype, M, n_in, n_out, r):
+    """splr_linear_stage1 then splr_linear_stage2 give splr_linear's Y bit for bit."""
+    print(f"[stages] dtype={dtype} M={M} n_in={n_in} n_out={n_out} r={r}", flush=True)
+    L = inputs.random_case(M, n_in, n_out, r, dtype, seed=77, n_outliers=2)
+    Xd, Ud, Vd = to_dev(L.X, dtype), to_dev(L.U if r else None, dtype), to_dev(L.V if r else None, dtype)
+    vd, md = binding.prune24_pack(to_dev(L.R, dtype))
+    Y1 = binding.linear(Xd, vd, md, Ud, Vd, n_out=n_out)
+    need = binding.workspace_bytes(M, n_out, n_in, r, Xd.dtype)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=Xd.device) if need else None
+    binding.linear_stage1(Xd, Vd, ws)
+    Y2 = binding.linear_stage2(Xd, vd, md, Ud, ws, n_out=n_out)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
