@@ -103,8 +103,8 @@ splr_status_t run_stage2(const void* X, int64_t M, int64_t n_in, const void* val
                          int64_t n_out, const void* U, int64_t r, splr_dtype_t dtype, float* Y, void* workspace,
                          hipStream_t stream) {
   if (dtype == SPLR_BF16)
-    return from_hip(splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, (const uint16_t*)workspace,
-                                             (const uint16_t*)workspace + (size_t)M * r, Y, stream));
+    return from_hip(splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, (const float*)workspace,
+                                             splr::lowrank_slices(M, n_in, r, true), Y, stream));
   return from_hip(splr::launch_linear_f32((const float*)X, M, n_in, (const float*)values, meta, n_out,
                                           (const float*)U, r, (const float*)workspace, Y, stream));
 }

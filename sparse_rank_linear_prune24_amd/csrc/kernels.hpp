@@ -10,17 +10,21 @@ namespace splr {
 hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
                                uint32_t* meta, hipStream_t stream);
 
-// First low-rank stage T = X V^T, written at the start of the workspace: float32 [M][r] for the
-// fp32 path; for the bf16 path a bfloat16 pair, hi [M][r] then lo [M][r] (T ~= hi + lo), followed by
-// float32 partial sums over K slices when the pre-pass splits K.
+// First low-rank stage T = X V^T, written to the workspace as float32 partial sums over `slices`
+// slices of K: part[z][M][r], z = 0 .. slices-1 (T = sum of the slices in slice order; the fp32 path
+// always uses one slice).
+constexpr int kMaxLowrankSlices = 16;
+int lowrank_slices(int64_t M, int64_t n_in, int64_t r, bool bf16);
 size_t lowrank_workspace_bytes(int64_t M, int64_t n_in, int64_t r, bool bf16);
 hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16,
                           void* workspace, hipStream_t stream);
 
-// Y = X S^T + T U^T with T = Thi + Tlo (bfloat16 planes [M][r]; r == 0: no low-rank term).
+// Y = X S^T + T U^T, T given as `slices` float32 partial sums [slices][M][r] (r == 0: no low-rank
+// term). The partials are added in slice order and T enters the MFMAs as a bfloat16 pair
+// hi = RNE(T), lo = RNE(T - hi).
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                              int64_t n_out, const void* U, int64_t r, const uint16_t* Thi, const uint16_t* Tlo,
-                              float* Y, hipStream_t stream);
+                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, float* Y,
+                              hipStream_t stream);
 hipError_t launch_linear_f32(const float* X, int64_t M, int64_t n_in, const float* values, const uint32_t* meta,
                              int64_t n_out, const float* U, int64_t r, const float* T, float* Y,
                              hipStream_t stream);

@@ -65,51 +65,106 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // ----------------------------------------------------------------------------------- epilogue
 
-// acc[i][j] (rows n = nrow0 + 16 i + ..., tokens m = mrow0 + 16 j + ...) += U[n][:] . T[m][:], with
-// T = Thi + Tlo given as two bfloat16 planes [M][r]. All fragments of a 64-rank block are loaded
-// before its MFMAs.
+// T rows m0 .. m0+ROWS-1, ranks j0 .. j0+63, as the bfloat16 pair (hi = RNE(T), lo = RNE(T - hi))
+// in two LDS planes with the X row pitch; chunk c of a row holds ranks j0 + 8c .. +7. T is the sum of
+// `slices` float32 partials [slices][M][r], added in slice order. All NT threads of the workgroup
+// take part; ranks >= r give zeros, rows past M repeat row M-1 (never stored).
+template <int ROWS, int NT>
+__device__ __forceinline__ void build_t_pair(const float* __restrict__ Tpart, int slices, int M, int r, int m0,
+                                             int j0, u32x4_t* hi, u32x4_t* lo, int tid) {
+  constexpr int kChunks = ROWS * 8;                    // 8 ranks each
+  constexpr int kIters = (kChunks + NT - 1) / NT;
+  constexpr int kGroup = kIters >= 4 ? 4 : 16 / kIters;  // slices in flight per round (<= 16 loads)
+  const size_t stride = (size_t)M * r;
+  const f32x4_t fz = {0, 0, 0, 0};
+  f32x4_t sum[kIters][2];
+  const float* src[kIters];
+  bool ok[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int c = tid + it * NT;
+    const int row = c >> 3, j = j0 + 8 * (c & 7);
+    ok[it] = c < kChunks && j < r;
+    src[it] = Tpart + (size_t)min(m0 + row, M - 1) * r + (ok[it] ? j : 0);
+    sum[it][0] = fz;
+    sum[it][1] = fz;
+  }
+  for (int z0 = 0; z0 < slices; z0 += kGroup) {
+    f32x4_t v[kIters][kGroup][2];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it)
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const bool live = ok[it] && z0 + u < slices;
+        const float* q = src[it] + (size_t)(live ? z0 + u : 0) * stride;
+        v[it][u][0] = live ? *(const f32x4_t*)q : fz;
+        v[it][u][1] = live ? *(const f32x4_t*)(q + 4) : fz;
+      }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it)
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u)
+        if (z0 + u < slices) {
+          sum[it][0] += v[it][u][0];
+          sum[it][1] += v[it][u][1];
+        }
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int c = tid + it * NT;
+    if (c >= kChunks) continue;
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = sum[it][e >> 2][e & 3];
+      h[e] = float_to_bf16_bits(t);
+      l[e] = float_to_bf16_bits(t - bf16_bits_to_float(h[e]));
+    }
+    const int o = (c >> 3) * kXPitchU4 + (c & 7);
+    hi[o] = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    lo[o] = u32x4_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+  }
+}
+
+// acc[i][j] (rows n = nrow0 + 16 i + ..., tokens = LDS rows 16 j + ...) += U[n][j0 .. j0+63] .
+// T[token][j0 .. j0+63], with T as the LDS pair built by build_t_pair. Dense U is the sum of two 2:4
+// operands with fixed patterns (ranks 0,1 and 2,3 of each group of four), and T = hi + lo, so each
+// fragment takes four structured-sparse MFMAs.
 template <int NI, int NJ>
-__device__ __forceinline__ void lowrank_epilogue(f32x4_t (&acc)[NI][NJ], const uint16_t* __restrict__ U,
-                                                 const uint16_t* __restrict__ Thi, const uint16_t* __restrict__ Tlo,
-                                                 int M, int n_out, int r, int nrow0, int mrow0, int lane) {
+__device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint16_t* __restrict__ U,
+                                              const u32x4_t* hi, const u32x4_t* lo, int n_out, int r, int j0,
+                                              int nrow0, int lane) {
   const int sub = lane & 15, quad = lane >> 4;
   const u32x4_t zero = {0, 0, 0, 0};
-  for (int j0 = 0; j0 < r; j0 += 64) {
-    // B operand: T[m][j0 + 8q .. +7] and T[m][j0 + 32 + 8q .. +7]
-    const int ja = j0 + 8 * quad, jb = j0 + 32 + 8 * quad;
-    u32x4_t th[NJ][2], tl[NJ][2];
+  // A operand: U[n][j0 + 16q .. +15] split into the (0,1) and (2,3) positions of each group
+  const int ju = j0 + 16 * quad;
+  u32x4_t ud[NI][2];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = nrow0 + 16 * i + sub;
+    const bool ok = n < n_out && ju < r;
+    const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
+    ud[i][0] = ok ? *(const u32x4_t*)p : zero;
+    ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
+  }
+  // B operand: T[token][j0 + 8q .. +7] and T[token][j0 + 32 + 8q .. +7]
+  bf16x16_t th[NJ], tl[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int row = (16 * j + sub) * kXPitchU4;
+    th[j] = cat16(as_bf16x8(hi[row + quad]), as_bf16x8(hi[row + 4 + quad]));
+    tl[j] = cat16(as_bf16x8(lo[row + quad]), as_bf16x8(lo[row + 4 + quad]));
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bf16x8_t u01 = as_bf16x8(u32x4_t{ud[i][0][0], ud[i][0][2], ud[i][1][0], ud[i][1][2]});
+    const bf16x8_t u23 = as_bf16x8(u32x4_t{ud[i][0][1], ud[i][0][3], ud[i][1][1], ud[i][1][3]});
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const size_t row = (size_t)min(mrow0 + 16 * j + sub, M - 1) * r;
-      th[j][0] = ja < r ? *(const u32x4_t*)(Thi + row + ja) : zero;
-      th[j][1] = jb < r ? *(const u32x4_t*)(Thi + row + jb) : zero;
-      tl[j][0] = ja < r ? *(const u32x4_t*)(Tlo + row + ja) : zero;
-      tl[j][1] = jb < r ? *(const u32x4_t*)(Tlo + row + jb) : zero;
-    }
-    // A operand: U[n][j0 + 16q .. +15] split into the (0,1) and (2,3) positions of each group
-    const int ju = j0 + 16 * quad;
-    u32x4_t ud[NI][2];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int n = nrow0 + 16 * i + sub;
-      const bool ok = n < n_out && ju < r;
-      const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
-      ud[i][0] = ok ? *(const u32x4_t*)p : zero;
-      ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const bf16x8_t u01 = as_bf16x8(u32x4_t{ud[i][0][0], ud[i][0][2], ud[i][1][0], ud[i][1][2]});
-      const bf16x8_t u23 = as_bf16x8(u32x4_t{ud[i][0][1], ud[i][0][3], ud[i][1][1], ud[i][1][3]});
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const bf16x16_t thi = cat16(as_bf16x8(th[j][0]), as_bf16x8(th[j][1]));
-        const bf16x16_t tlo = cat16(as_bf16x8(tl[j][0]), as_bf16x8(tl[j][1]));
-        acc[i][j] = smfmac16x16x64(u01, thi, acc[i][j], 0x4444);
-        acc[i][j] = smfmac16x16x64(u23, thi, acc[i][j], 0xEEEE);
-        acc[i][j] = smfmac16x16x64(u01, tlo, acc[i][j], 0x4444);
-        acc[i][j] = smfmac16x16x64(u23, tlo, acc[i][j], 0xEEEE);
-      }
+      acc[i][j] = smfmac16x16x64(u01, th[j], acc[i][j], 0x4444);
+      acc[i][j] = smfmac16x16x64(u23, th[j], acc[i][j], 0xEEEE);
+      acc[i][j] = smfmac16x16x64(u01, tl[j], acc[i][j], 0x4444);
+      acc[i][j] = smfmac16x16x64(u23, tl[j], acc[i][j], 0xEEEE);
     }
   }
 }
@@ -143,8 +198,8 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], float* 
 template <int NI, int NJ, int P, int PX>
 __global__ __launch_bounds__(256) void linear_prefill_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const uint16_t* __restrict__ Thi, const uint16_t* __restrict__ Tlo,
-    float* __restrict__ Y, int M, int K, int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
+    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, float* __restrict__ Y, int M, int K,
+    int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
   constexpr int WAVES = 4;
   constexpr int BN = 16 * NI * WAVES;
   constexpr int BM = 16 * NJ;
@@ -307,7 +362,15 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
     static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, u, std::true_type{}); });
 
   const int nrow0 = n0 + wave * 16 * NI;
-  if (r > 0) lowrank_epilogue<NI, NJ>(acc, U, Thi, Tlo, M, n_out, r, nrow0, m0, lane);
+  // rank-r term, 64 ranks at a time: the workgroup builds T's bfloat16 pair for its tokens in the
+  // (now free) X slots, then every wave adds its U block times T (the last step's barrier has
+  // retired every read of the X slots)
+  for (int j0 = 0; j0 < r; j0 += 64) {
+    build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs0, xs1, threadIdx.x);
+    lds_barrier();
+    lowrank_block<NI, NJ>(acc, U, xs0, xs1, n_out, r, j0, nrow0, lane);
+    lds_barrier();
+  }
   store_tile<NI, NJ>(acc, Y, M, n_out, nrow0, m0, lane);
 }
 
@@ -316,8 +379,8 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
 template <int MB, int P>
 __global__ __launch_bounds__(256) void linear_decode_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const uint16_t* __restrict__ Thi, const uint16_t* __restrict__ Tlo,
-    float* __restrict__ Y, int M, int K, int n_out, int r) {
+    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, float* __restrict__ Y, int M, int K,
+    int n_out, int r) {
   constexpr int WAVES = 4;
   constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
   __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
@@ -378,30 +441,36 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
     }
   }
 
-  // fixed-order combination of the waves' partial sums
+  // fixed-order combination of the waves' partial sums (into wave 0)
   if (wave > 0) {
 #pragma unroll
     for (int j = 0; j < MB; ++j) red[((wave - 1) * MB + j) * 64 + lane] = acc[0][j];
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave == 0) {
 #pragma unroll
-  for (int w = 1; w < WAVES; ++w)
+    for (int w = 1; w < WAVES; ++w)
 #pragma unroll
-    for (int j = 0; j < MB; ++j) acc[0][j] += red[((w - 1) * MB + j) * 64 + lane];
-
-  if (r > 0) lowrank_epilogue<1, MB>(acc, U, Thi, Tlo, M, n_out, r, tr * 16, m0, lane);
-  store_tile<1, MB>(acc, Y, M, n_out, tr * 16, m0, lane);
+      for (int j = 0; j < MB; ++j) acc[0][j] += red[((w - 1) * MB + j) * 64 + lane];
+  }
+  // rank-r term, 64 ranks at a time: all waves build T's bfloat16 pair in LDS, wave 0 adds U T^T
+  for (int j0 = 0; j0 < r; j0 += 64) {
+    build_t_pair<16 * MB, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs[0], xs[1], threadIdx.x);
+    lds_barrier();
+    if (wave == 0) lowrank_block<1, MB>(acc, U, xs[0], xs[1], n_out, r, j0, tr * 16, lane);
+    lds_barrier();
+  }
+  if (wave == 0) store_tile<1, MB>(acc, Y, M, n_out, tr * 16, m0, lane);
 }
 
 template <int MB>
 hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                         int64_t n_out, const void* U, int64_t r, const uint16_t* Thi, const uint16_t* Tlo,
-                         float* Y, hipStream_t stream) {
+                         int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, float* Y,
+                         hipStream_t stream) {
   constexpr int P = MB == 1 ? 8 : 4;
   dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(M, 16 * MB));
   linear_decode_kernel<MB, P><<<grid, dim3(256), 0, stream>>>(
-      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Thi, Tlo, Y, (int)M, (int)n_in,
+      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, (int)M, (int)n_in,
       (int)n_out, (int)r);
   return hipGetLastError();
 }
@@ -409,11 +478,12 @@ hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* val
 }  // namespace
 
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                              int64_t n_out, const void* U, int64_t r, const uint16_t* Thi, const uint16_t* Tlo,
-                              float* Y, hipStream_t stream) {
-  if (M <= 16) return launch_decode<1>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
-  if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
-  if (M <= kDecodeMaxTokens) return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Thi, Tlo, Y, stream);
+                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, float* Y,
+                              hipStream_t stream) {
+  if (M <= 16) return launch_decode<1>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, stream);
+  if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, stream);
+  if (M <= kDecodeMaxTokens)
+    return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, stream);
 
   constexpr int NI = 4, NJ = 8, P = 4, PX = 2;
   constexpr int BN = 16 * NI * 4, BM = 16 * NJ;
@@ -422,7 +492,7 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   const int per_xcd = (int)ceil_div(n_tiles, 8);
   const int group_m = 4;
   linear_prefill_kernel<NI, NJ, P, PX><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
-      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Thi, Tlo, Y, (int)M, (int)n_in,
+      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, (int)M, (int)n_in,
       (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   return hipGetLastError();
 }

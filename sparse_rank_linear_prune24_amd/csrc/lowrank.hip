@@ -8,10 +8,8 @@
 // operand, dense V being the sum of two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of
 // every group of four columns). Covering all ranks in one workgroup stages each X row once; the K
 // slices give the chip enough workgroups. The waves' partial sums are combined through LDS in wave
-// order; with one slice T is written directly, otherwise each slice writes a float32 partial and a
-// second kernel adds the slices in slice order (deterministic, no atomics). T is stored as a
-// bfloat16 pair: hi = T rounded to nearest even, lo = (T - hi) rounded to nearest even (hi + lo
-// carries about 16 significant bits).
+// order and each slice writes its float32 partial sum of T; the second stage adds the slices in
+// slice order (deterministic, no atomics).
 // fp32: one wave per output, lanes stride over K, fixed-order butterfly reduction.
 #include <algorithm>
 #include <type_traits>
@@ -37,26 +35,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Round T to the bfloat16 pair (hi, lo) for 4 consecutive ranks and store both planes.
-__device__ __forceinline__ void store_hi_lo(const f32x4_t t, uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = float_to_bf16_bits(t[e]);
-    l[e] = float_to_bf16_bits(t[e] - bf16_bits_to_float(h[e]));
-  }
-  *(u32x2_t*)hi = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  *(u32x2_t*)lo = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-}
-
-// Grid (token blocks, rank blocks, K slices); slice z covers K steps [z*steps_per_slice, ...).
-// part == nullptr: one slice, write Thi/Tlo. Otherwise write float32 partial part[z][m][j].
+// Grid (token blocks, rank blocks, K slices); slice z covers K steps [z*steps_per_slice, ...) and
+// writes the float32 partial sum part[z][m][j].
 template <int TF, int RF, int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t* __restrict__ X,
                                                                  const uint16_t* __restrict__ V, int M, int K,
                                                                  int r, int steps_per_slice,
-                                                                 uint16_t* __restrict__ Thi,
-                                                                 uint16_t* __restrict__ Tlo,
                                                                  float* __restrict__ part) {
   constexpr int kRows = 16 * (TF + RF);  // staged rows per wave: X tokens, then V ranks
   constexpr int kLoads = kRows / 8;      // 8 rows x 128 bytes per load instruction
@@ -160,40 +144,16 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
     for (int a = 0; a < RF; ++a)
 #pragma unroll
       for (int f = 0; f < TF; ++f) acc[a][f] += red[(((w - 1) * RF + a) * TF + f) * 64 + lane];
-  float* pz = part ? part + (size_t)blockIdx.z * M * r : nullptr;
+  float* pz = part + (size_t)blockIdx.z * M * r;
 #pragma unroll
   for (int a = 0; a < RF; ++a) {
     const int j = j0 + 16 * a + 4 * quad;
 #pragma unroll
     for (int f = 0; f < TF; ++f) {
       const int m = m0 + 16 * f + sub;
-      if (m >= M) continue;
-      const size_t o = (size_t)m * r + j;
-      if (pz)
-        *(f32x4_t*)(pz + o) = acc[a][f];
-      else
-        store_hi_lo(acc[a][f], Thi + o, Tlo + o);
+      if (m < M) *(f32x4_t*)(pz + (size_t)m * r + j) = acc[a][f];
     }
   }
-}
-
-// T = sum over slices z = 0, 1, ... of part[z] (in that order), stored as the bfloat16 pair. All
-// slice loads are issued before the first add (a load-add chain would wait once per slice).
-constexpr int kMaxSlices = 16;
-__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __restrict__ part, int slices,
-                                                            int64_t n4, int64_t stride, uint16_t* __restrict__ Thi,
-                                                            uint16_t* __restrict__ Tlo) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  f32x4_t v[kMaxSlices];
-#pragma unroll
-  for (int z = 0; z < kMaxSlices; ++z)
-    v[z] = z < slices ? *(const f32x4_t*)(part + (size_t)z * stride + 4 * i) : f32x4_t{0, 0, 0, 0};
-  f32x4_t t = v[0];
-#pragma unroll
-  for (int z = 1; z < kMaxSlices; ++z)
-    if (z < slices) t += v[z];
-  store_hi_lo(t, Thi + 4 * i, Tlo + 4 * i);
 }
 
 __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restrict__ X, const float* __restrict__ V,
@@ -215,8 +175,8 @@ __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restric
 
 namespace {
 
-// bf16 pre-pass shape: ranks per workgroup, and the number of K slices that gives the chip at least
-// ~256 workgroups (at most 16 slices, at most one per K step).
+// bf16 first-stage shape: ranks per workgroup, and the number of K slices that gives the chip at
+// least ~256 workgroups (at most kMaxLowrankSlices, at most one per K step).
 struct LowrankShape {
   int tf, rf, slices, steps_per_slice;
 };
@@ -226,8 +186,9 @@ LowrankShape lowrank_shape(int64_t M, int64_t n_in, int64_t r) {
   sh.tf = M <= 16 ? 1 : 2;
   sh.rf = r % 64 == 0 ? 4 : (r % 32 == 0 ? 2 : 1);
   const int64_t TK = (n_in + 63) / 64;
-  const int64_t base = ceil_div(M, 16 * sh.tf) * (r / (16 * sh.rf));
-  int64_t slices = std::min<int64_t>(std::min<int64_t>(kMaxSlices, TK), std::max<int64_t>(1, ceil_div(256, base)));
+  const int64_t base = ceil_div(M, 16 * sh.tf) * std::max<int64_t>(1, r / (16 * sh.rf));
+  const int64_t slices =
+      std::min<int64_t>(std::min<int64_t>(kMaxLowrankSlices, TK), std::max<int64_t>(1, ceil_div(256, base)));
   sh.steps_per_slice = (int)ceil_div(TK, slices);
   sh.slices = (int)ceil_div(TK, sh.steps_per_slice);
   return sh;
@@ -235,49 +196,42 @@ LowrankShape lowrank_shape(int64_t M, int64_t n_in, int64_t r) {
 
 template <int TF, int RF>
 void launch_part(const LowrankShape& sh, const void* X, const void* V, int64_t M, int64_t n_in, int64_t r,
-                 uint16_t* Thi, uint16_t* Tlo, float* part, hipStream_t stream) {
+                 float* part, hipStream_t stream) {
   dim3 grid((unsigned)cdiv(M, 16 * TF), (unsigned)(r / (16 * RF)), (unsigned)sh.slices);
   lowrank_bf16_kernel<TF, RF, 4, 2><<<grid, dim3(256), 0, stream>>>((const uint16_t*)X, (const uint16_t*)V, (int)M,
-                                                                  (int)n_in, (int)r, sh.steps_per_slice, Thi, Tlo,
-                                                                  part);
+                                                                  (int)n_in, (int)r, sh.steps_per_slice, part);
 }
 
 }  // namespace
 
+int lowrank_slices(int64_t M, int64_t n_in, int64_t r, bool bf16) {
+  return (r == 0 || !bf16) ? 1 : lowrank_shape(M, n_in, r).slices;
+}
+
 size_t lowrank_workspace_bytes(int64_t M, int64_t n_in, int64_t r, bool bf16) {
   if (r == 0) return 0;
-  if (!bf16) return (size_t)M * r * sizeof(float);
-  const LowrankShape sh = lowrank_shape(M, n_in, r);
-  const size_t planes = (size_t)M * r * 2 * sizeof(uint16_t);
-  return sh.slices > 1 ? planes + (size_t)sh.slices * M * r * sizeof(float) : planes;
+  return (size_t)lowrank_slices(M, n_in, r, bf16) * M * r * sizeof(float);
 }
 
 hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16,
                           void* workspace, hipStream_t stream) {
   if (r == 0) return hipSuccess;
+  float* part = (float*)workspace;
   if (bf16) {
-    uint16_t* Thi = (uint16_t*)workspace;
-    uint16_t* Tlo = Thi + (size_t)M * r;
     const LowrankShape sh = lowrank_shape(M, n_in, r);
-    float* part = sh.slices > 1 ? (float*)(Tlo + (size_t)M * r) : nullptr;
     if (sh.tf == 1) {
-      if (sh.rf == 4) launch_part<1, 4>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
-      else if (sh.rf == 2) launch_part<1, 2>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
-      else launch_part<1, 1>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
+      if (sh.rf == 4) launch_part<1, 4>(sh, X, V, M, n_in, r, part, stream);
+      else if (sh.rf == 2) launch_part<1, 2>(sh, X, V, M, n_in, r, part, stream);
+      else launch_part<1, 1>(sh, X, V, M, n_in, r, part, stream);
     } else {
-      if (sh.rf == 4) launch_part<2, 4>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
-      else if (sh.rf == 2) launch_part<2, 2>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
-      else launch_part<2, 1>(sh, X, V, M, n_in, r, Thi, Tlo, part, stream);
-    }
-    if (part) {
-      const int64_t n4 = M * r / 4;
-      lowrank_reduce_kernel<<<dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, stream>>>(part, sh.slices, n4, M * r,
-                                                                                         Thi, Tlo);
+      if (sh.rf == 4) launch_part<2, 4>(sh, X, V, M, n_in, r, part, stream);
+      else if (sh.rf == 2) launch_part<2, 2>(sh, X, V, M, n_in, r, part, stream);
+      else launch_part<2, 1>(sh, X, V, M, n_in, r, part, stream);
     }
   } else {
     const int64_t waves = M * r;
     lowrank_f32_kernel<<<dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, stream>>>(
-        (const float*)X, (const float*)V, (int)M, (int)n_in, (int)r, (float*)workspace);
+        (const float*)X, (const float*)V, (int)M, (int)n_in, (int)r, part);
   }
   return hipGetLastError();
 }
