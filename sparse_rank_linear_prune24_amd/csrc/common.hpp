@@ -24,11 +24,13 @@ __device__ __forceinline__ bf16x16_t cat16(bf16x8_t lo, bf16x8_t hi) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float -> bfloat16 bits, round to nearest even (finite inputs; NaN stays NaN).
+// float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN). Branch-free: both results
+// are formed and one is selected.
 __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? quiet_nan : rounded;
 }
 
 // Split eight float32 values into bfloat16 high parts and bfloat16 corrections:

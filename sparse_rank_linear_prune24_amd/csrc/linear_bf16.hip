@@ -39,6 +39,9 @@ namespace {
 // reads (16 rows x one 16-byte chunk per quarter wave) run at the full ds_read_b128 rate on gfx950;
 // a 16-byte pad leaves them 2-way bank conflicted.
 constexpr int kXPitchU4 = 10;
+// ranks (in blocks of 64) whose T pair the stage-2 kernels build before their main loop; larger r
+// builds it block by block after the loop
+constexpr int kPreRankBlocks = 1;
 
 
 // LDS writes of this wave complete, then workgroup barrier. One asm statement with a memory
@@ -65,75 +68,128 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // ----------------------------------------------------------------------------------- epilogue
 
-// T rows m0 .. m0+ROWS-1, ranks j0 .. j0+63, as the bfloat16 pair (hi = RNE(T), lo = RNE(T - hi))
-// in two LDS planes with the X row pitch; chunk c of a row holds ranks j0 + 8c .. +7. T is the sum of
-// `slices` float32 partials [slices][M][r], added in slice order. All NT threads of the workgroup
-// take part; ranks >= r give zeros, rows past M repeat row M-1 (never stored).
+// Builds T rows m0 .. m0+ROWS-1, ranks j0 .. j0+63, as the bfloat16 pair (hi = RNE(T), lo =
+// RNE(T - hi)) in two LDS planes with the X row pitch (bytes 16c .. 16c+15 of a row hold ranks
+// j0 + 8c .. +7). T is the sum of `slices` float32 partials [slices][M][r], added in slice order.
+// All NT threads take part; thread t handles 4 consecutive ranks of a row per item, so one wave
+// load covers 4 rows x 256 contiguous bytes. Ranks >= r give zeros; rows past M repeat row M-1
+// (never stored). issue() starts the loads of a round of slices, finish() adds them (and any
+// further rounds) and writes the LDS planes, so the first round can overlap other work.
 template <int ROWS, int NT>
-__device__ __forceinline__ void build_t_pair(const float* __restrict__ Tpart, int slices, int M, int r, int m0,
-                                             int j0, u32x4_t* hi, u32x4_t* lo, int tid) {
-  constexpr int kChunks = ROWS * 8;                    // 8 ranks each
-  constexpr int kIters = (kChunks + NT - 1) / NT;
-  constexpr int kGroup = kIters >= 4 ? 4 : 16 / kIters;  // slices in flight per round (<= 16 loads)
-  const size_t stride = (size_t)M * r;
-  const f32x4_t fz = {0, 0, 0, 0};
-  f32x4_t sum[kIters][2];
+struct TPairBuilder {
+  static constexpr int kQuads = ROWS * 16;  // 4 ranks each
+  static constexpr int kIters = (kQuads + NT - 1) / NT;
+  static constexpr int kGroup = kIters >= 8 ? 1 : 16 / kIters;  // slices per round (<= 16 loads in flight)
   const float* src[kIters];
   bool ok[kIters];
+  f32x4_t sum[kIters];
+  f32x4_t v[kIters][kGroup];
+  size_t stride;
+  int slices, tid;
+
+  __device__ __forceinline__ void init(const float* __restrict__ Tpart, int n_slices, int M, int r, int m0, int j0,
+                                       int t) {
+    stride = (size_t)M * r;
+    slices = n_slices;
+    tid = t;
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int c = tid + it * NT;
-    const int row = c >> 3, j = j0 + 8 * (c & 7);
-    ok[it] = c < kChunks && j < r;
-    src[it] = Tpart + (size_t)min(m0 + row, M - 1) * r + (ok[it] ? j : 0);
-    sum[it][0] = fz;
-    sum[it][1] = fz;
+    for (int it = 0; it < kIters; ++it) {
+      const int q = tid + it * NT;
+      const int row = q >> 4, j = j0 + 4 * (q & 15);
+      ok[it] = q < kQuads && j < r;
+      src[it] = Tpart + (size_t)min(m0 + row, M - 1) * r + (ok[it] ? j : 0);
+      sum[it] = f32x4_t{0, 0, 0, 0};
+    }
   }
-  for (int z0 = 0; z0 < slices; z0 += kGroup) {
-    f32x4_t v[kIters][kGroup][2];
-#pragma unroll
-    for (int it = 0; it < kIters; ++it)
-#pragma unroll
-      for (int u = 0; u < kGroup; ++u) {
-        const bool live = ok[it] && z0 + u < slices;
-        const float* q = src[it] + (size_t)(live ? z0 + u : 0) * stride;
-        v[it][u][0] = live ? *(const f32x4_t*)q : fz;
-        v[it][u][1] = live ? *(const f32x4_t*)(q + 4) : fz;
-      }
+  // loads are unconditional (clamped, valid addresses) and masked when added: no lane branches
+  __device__ __forceinline__ void issue(int z0) {
 #pragma unroll
     for (int it = 0; it < kIters; ++it)
 #pragma unroll
       for (int u = 0; u < kGroup; ++u)
-        if (z0 + u < slices) {
-          sum[it][0] += v[it][u][0];
-          sum[it][1] += v[it][u][1];
-        }
+        v[it][u] = *(const f32x4_t*)(src[it] + (size_t)(z0 + u < slices ? z0 + u : 0) * stride);
   }
+  __device__ __forceinline__ void accumulate(int z0) {
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int c = tid + it * NT;
-    if (c >= kChunks) continue;
-    uint32_t h[8], l[8];
+    for (int it = 0; it < kIters; ++it)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = sum[it][e >> 2][e & 3];
-      h[e] = float_to_bf16_bits(t);
-      l[e] = float_to_bf16_bits(t - bf16_bits_to_float(h[e]));
+      for (int u = 0; u < kGroup; ++u) sum[it] += (ok[it] && z0 + u < slices) ? v[it][u] : f32x4_t{0, 0, 0, 0};
+  }
+  __device__ __forceinline__ void finish(u32x4_t* hi, u32x4_t* lo) {
+    accumulate(0);
+    for (int z0 = kGroup; z0 < slices; z0 += kGroup) {
+      issue(z0);
+      // every load of the round is issued before the first use (under register pressure the
+      // scheduler would otherwise pair each load with its use and serialise the latencies)
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(z0);
     }
-    const int o = (c >> 3) * kXPitchU4 + (c & 7);
-    hi[o] = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    lo[o] = u32x4_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int q = tid + it * NT;
+      if (q >= kQuads) continue;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = float_to_bf16_bits(sum[it][e]);
+        l[e] = float_to_bf16_bits(sum[it][e] - bf16_bits_to_float(h[e]));
+      }
+      const int o = (q >> 4) * 2 * kXPitchU4 + (q & 15);  // in 8-byte units
+      ((u32x2_t*)hi)[o] = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      ((u32x2_t*)lo)[o] = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    }
   }
+};
+
+template <int ROWS, int NT>
+__device__ __forceinline__ void build_t_pair(const float* __restrict__ Tpart, int slices, int M, int r, int m0,
+                                             int j0, u32x4_t* hi, u32x4_t* lo, int tid) {
+  TPairBuilder<ROWS, NT> tb;
+  tb.init(Tpart, slices, M, r, m0, j0, tid);
+  tb.issue(0);
+  __builtin_amdgcn_sched_barrier(0);
+  tb.finish(hi, lo);
 }
+
+// Stages U rows n0 .. n0+ROWS-1, ranks j0 .. j0+63 in LDS (X row pitch, bytes 16c .. 16c+15 of a row
+// = ranks j0 + 8c .. +7) with row-contiguous loads (8 rows x 128 bytes per wave load); rows past
+// n_out and ranks >= r are zero. issue() / finish() as for the T pair.
+template <int ROWS, int NT>
+struct UStager {
+  static constexpr int kChunks = ROWS * 8;
+  static constexpr int kIters = (kChunks + NT - 1) / NT;
+  u32x4_t v[kIters];
+  bool ok[kIters];
+  int tid;
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ U, int n_out, int r, int n0, int j0, int t) {
+    tid = t;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int c = tid + it * NT;
+      const int row = c >> 3, j = j0 + 8 * (c & 7);
+      ok[it] = c < kChunks && n0 + row < n_out && j < r;
+      v[it] = *(const u32x4_t*)(U + (size_t)min(n0 + row, n_out - 1) * r + (j < r ? j : 0));
+    }
+  }
+  __device__ __forceinline__ void finish(u32x4_t* dst) {
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int c = tid + it * NT;
+      if (c < kChunks) dst[(c >> 3) * kXPitchU4 + (c & 7)] = ok[it] ? v[it] : u32x4_t{0, 0, 0, 0};
+    }
+  }
+};
 
 // acc[i][j] (rows n = nrow0 + 16 i + ..., tokens = LDS rows 16 j + ...) += U[n][j0 .. j0+63] .
 // T[token][j0 .. j0+63], with T as the LDS pair built by build_t_pair. Dense U is the sum of two 2:4
 // operands with fixed patterns (ranks 0,1 and 2,3 of each group of four), and T = hi + lo, so each
 // fragment takes four structured-sparse MFMAs.
+// U comes from `ulds` when given (rows of the block staged by UStager, this wave's first row at
+// `urow0`), else from global memory.
 template <int NI, int NJ>
 __device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint16_t* __restrict__ U,
                                               const u32x4_t* hi, const u32x4_t* lo, int n_out, int r, int j0,
-                                              int nrow0, int lane) {
+                                              int nrow0, int lane, const u32x4_t* ulds = nullptr, int urow0 = 0) {
   const int sub = lane & 15, quad = lane >> 4;
   const u32x4_t zero = {0, 0, 0, 0};
   // A operand: U[n][j0 + 16q .. +15] split into the (0,1) and (2,3) positions of each group
@@ -141,11 +197,17 @@ __device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint
   u32x4_t ud[NI][2];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int n = nrow0 + 16 * i + sub;
-    const bool ok = n < n_out && ju < r;
-    const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
-    ud[i][0] = ok ? *(const u32x4_t*)p : zero;
-    ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
+    if (ulds) {
+      const int row = (urow0 + 16 * i + sub) * kXPitchU4 + 2 * quad;
+      ud[i][0] = ulds[row];
+      ud[i][1] = ulds[row + 1];
+    } else {
+      const int n = nrow0 + 16 * i + sub;
+      const bool ok = n < n_out && ju < r;
+      const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
+      ud[i][0] = ok ? *(const u32x4_t*)p : zero;
+      ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
+    }
   }
   // B operand: T[token][j0 + 8q .. +7] and T[token][j0 + 32 + 8q .. +7]
   bf16x16_t th[NJ], tl[NJ];
@@ -211,6 +273,11 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   // the other
   __shared__ u32x4_t xs0[BM * kXPitchU4];
   __shared__ u32x4_t xs1[BM * kXPitchU4];
+  // T's bfloat16 pair for this tile's tokens (hi, lo planes per 64 ranks), built before the main
+  // loop when r <= 64 * kPreRankBlocks (registers are free then and the loads overlap the start),
+  // and this tile's U rows when r <= 64
+  __shared__ u32x4_t tpair[2 * kPreRankBlocks][BM * kXPitchU4];
+  __shared__ u32x4_t ulds[BN * kXPitchU4];
 
   // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a contiguous range of
   // logical tiles, walked in groups of `group_m` token tiles, so its tiles share X and S rows.
@@ -341,6 +408,21 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // rank-r operands staged before the main loop: loads issued here, finished after the loop's
+  // prologue has issued its own loads (published by the prologue's barriers)
+  const bool t_pre = r <= 64 * kPreRankBlocks, u_pre = r <= 64;
+  TPairBuilder<BM, 64 * WAVES> tb[kPreRankBlocks];
+  UStager<BN, 64 * WAVES> us;
+  if (t_pre) {
+#pragma unroll
+    for (int b = 0; b < kPreRankBlocks; ++b)
+      if (64 * b < r) {
+        tb[b].init(Tpart, slices, M, r, m0, 64 * b, threadIdx.x);
+        tb[b].issue(0);
+      }
+  }
+  if (u_pre && r > 0) us.issue(U, n_out, r, n0, 0, threadIdx.x);
+
   // Prologue: virtual steps v = -VS .. -1 issue exactly what a step would (X of step v+2 into LDS,
   // S of step v+P-1, X of step v+2+PX), so the loop is entered with the loads in flight in the same
   // order as in the steady state and the wait counts the compiler derives need no extra waits.
@@ -351,6 +433,12 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
     if constexpr (v + P - 1 >= 0) load_s(v + P - 1, sa[(v + P - 1) % P], sw[(v + P - 1) % P]);
     if constexpr (v + 2 + PX >= 0) load_x(v + 2 + PX, xr[(v + 2 + PX) % PX]);
   });
+  if (t_pre) {
+#pragma unroll
+    for (int b = 0; b < kPreRankBlocks; ++b)
+      if (64 * b < r) tb[b].finish(tpair[2 * b], tpair[2 * b + 1]);
+  }
+  if (u_pre && r > 0) us.finish(ulds);
   lds_barrier();
   read_b(xs0, bx[0]);
   lds_barrier();  // every wave's reads of slot 0 are done before step 0 overwrites it
@@ -362,14 +450,23 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
     static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, u, std::true_type{}); });
 
   const int nrow0 = n0 + wave * 16 * NI;
-  // rank-r term, 64 ranks at a time: the workgroup builds T's bfloat16 pair for its tokens in the
-  // (now free) X slots, then every wave adds its U block times T (the last step's barrier has
-  // retired every read of the X slots)
-  for (int j0 = 0; j0 < r; j0 += 64) {
-    build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs0, xs1, threadIdx.x);
-    lds_barrier();
-    lowrank_block<NI, NJ>(acc, U, xs0, xs1, n_out, r, j0, nrow0, lane);
-    lds_barrier();
+  // rank-r term, 64 ranks at a time: every wave adds its U block times T. T's pair is already in
+  // LDS (built before the loop, published by the prologue's barriers), or, for larger r, the
+  // workgroup builds it block by block in the now free X slots (the last step's barrier has retired
+  // every read of them)
+  if (t_pre) {
+#pragma unroll
+    for (int b = 0; b < kPreRankBlocks; ++b)
+      if (64 * b < r)
+        lowrank_block<NI, NJ>(acc, U, tpair[2 * b], tpair[2 * b + 1], n_out, r, 64 * b, nrow0, lane,
+                              u_pre ? ulds : nullptr, wave * 16 * NI);
+  } else {
+    for (int j0 = 0; j0 < r; j0 += 64) {
+      build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs0, xs1, threadIdx.x);
+      lds_barrier();
+      lowrank_block<NI, NJ>(acc, U, xs0, xs1, n_out, r, j0, nrow0, lane);
+      lds_barrier();
+    }
   }
   store_tile<NI, NJ>(acc, Y, M, n_out, nrow0, m0, lane);
 }
@@ -385,12 +482,21 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
   constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
   __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
   __shared__ f32x4_t red[(WAVES - 1) * MB * 64];
+  __shared__ u32x4_t tpair[2 * kPreRankBlocks][16 * MB * kXPitchU4];  // as in the prefill kernel
   // the wave index is uniform across the wave; readfirstlane lets the compiler see that (scalar
   // loop control instead of exec-mask loops)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane & 15, quad = lane >> 4;
   const int tr = blockIdx.x, m0 = blockIdx.y * 16 * MB;
   const int TK = (K + 63) / 64;
+
+  const bool t_pre = r <= 64 * kPreRankBlocks;
+  if (t_pre) {  // T's pair first, while registers are free (published by the barrier after the loop)
+#pragma unroll
+    for (int b = 0; b < kPreRankBlocks; ++b)
+      if (64 * b < r) build_t_pair<16 * MB, 64 * WAVES>(Tpart, slices, M, r, m0, 64 * b, tpair[2 * b],
+                                                         tpair[2 * b + 1], threadIdx.x);
+  }
 
   const u32x4_t* vsrc = values + (size_t)tr * TK * 64 + lane;
   const uint16_t* msrc = (const uint16_t*)(meta + (size_t)tr * TK * 32 + sub + 16 * (quad >> 1)) + (quad & 1);
@@ -453,12 +559,21 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
 #pragma unroll
       for (int j = 0; j < MB; ++j) acc[0][j] += red[((w - 1) * MB + j) * 64 + lane];
   }
-  // rank-r term, 64 ranks at a time: all waves build T's bfloat16 pair in LDS, wave 0 adds U T^T
-  for (int j0 = 0; j0 < r; j0 += 64) {
-    build_t_pair<16 * MB, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs[0], xs[1], threadIdx.x);
-    lds_barrier();
-    if (wave == 0) lowrank_block<1, MB>(acc, U, xs[0], xs[1], n_out, r, j0, tr * 16, lane);
-    lds_barrier();
+  // rank-r term, 64 ranks at a time: wave 0 adds U T^T, with T's pair from before the loop or, for
+  // larger r, built block by block by all waves
+  if (t_pre) {
+    if (wave == 0) {
+#pragma unroll
+      for (int b = 0; b < kPreRankBlocks; ++b)
+        if (64 * b < r) lowrank_block<1, MB>(acc, U, tpair[2 * b], tpair[2 * b + 1], n_out, r, 64 * b, tr * 16, lane);
+    }
+  } else {
+    for (int j0 = 0; j0 < r; j0 += 64) {
+      build_t_pair<16 * MB, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs[0], xs[1], threadIdx.x);
+      lds_barrier();
+      if (wave == 0) lowrank_block<1, MB>(acc, U, xs[0], xs[1], n_out, r, j0, tr * 16, lane);
+      lds_barrier();
+    }
   }
   if (wave == 0) store_tile<1, MB>(acc, Y, M, n_out, tr * 16, m0, lane);
 }

@@ -175,20 +175,29 @@ __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restric
 
 namespace {
 
-// bf16 first-stage shape: ranks per workgroup, and the number of K slices that gives the chip at
-// least ~256 workgroups (at most kMaxLowrankSlices, at most one per K step).
+// bf16 first-stage shape. Enough workgroups (~256) come first from splitting the ranks (32 tokens x
+// 64, 32 or 16 ranks per workgroup, the widest split that suffices), so that T needs no K slices
+// and stage 2 reads it once; only when even 16 ranks per workgroup leave the chip short does the
+// stage split K into slices (at most kMaxLowrankSlices, at most one per K step), with 64 ranks per
+// workgroup to stage each X row once.
 struct LowrankShape {
   int tf, rf, slices, steps_per_slice;
 };
 
 LowrankShape lowrank_shape(int64_t M, int64_t n_in, int64_t r) {
+  constexpr int64_t kWant = 256;
   LowrankShape sh;
   sh.tf = M <= 16 ? 1 : 2;
-  sh.rf = r % 64 == 0 ? 4 : (r % 32 == 0 ? 2 : 1);
-  const int64_t TK = (n_in + 63) / 64;
-  const int64_t base = ceil_div(M, 16 * sh.tf) * std::max<int64_t>(1, r / (16 * sh.rf));
-  const int64_t slices =
-      std::min<int64_t>(std::min<int64_t>(kMaxLowrankSlices, TK), std::max<int64_t>(1, ceil_div(256, base)));
+  const int64_t TK = (n_in + 63) / 64, token_blocks = ceil_div(M, 16 * sh.tf);
+  sh.rf = 0;
+  for (int rf : {4, 2, 1})
+    if (sh.rf == 0 && r % (16 * rf) == 0 && token_blocks * (r / (16 * rf)) >= kWant) sh.rf = rf;
+  int64_t slices = 1;
+  if (sh.rf == 0) {
+    sh.rf = r % 64 == 0 ? 4 : (r % 32 == 0 ? 2 : 1);
+    const int64_t base = token_blocks * (r / (16 * sh.rf));
+    slices = std::min<int64_t>(std::min<int64_t>(kMaxLowrankSlices, TK), std::max<int64_t>(1, ceil_div(kWant, base)));
+  }
   sh.steps_per_slice = (int)ceil_div(TK, slices);
   sh.slices = (int)ceil_div(TK, sh.steps_per_slice);
   return sh;
@@ -198,8 +207,12 @@ template <int TF, int RF>
 void launch_part(const LowrankShape& sh, const void* X, const void* V, int64_t M, int64_t n_in, int64_t r,
                  float* part, hipStream_t stream) {
   dim3 grid((unsigned)cdiv(M, 16 * TF), (unsigned)(r / (16 * RF)), (unsigned)sh.slices);
-  lowrank_bf16_kernel<TF, RF, 4, 2><<<grid, dim3(256), 0, stream>>>((const uint16_t*)X, (const uint16_t*)V, (int)M,
-                                                                  (int)n_in, (int)r, sh.steps_per_slice, part);
+  if (sh.steps_per_slice >= 16)
+    lowrank_bf16_kernel<TF, RF, 4, 4><<<grid, dim3(256), 0, stream>>>((const uint16_t*)X, (const uint16_t*)V, (int)M,
+                                                                    (int)n_in, (int)r, sh.steps_per_slice, part);
+  else
+    lowrank_bf16_kernel<TF, RF, 4, 2><<<grid, dim3(256), 0, stream>>>((const uint16_t*)X, (const uint16_t*)V, (int)M,
+                                                                    (int)n_in, (int)r, sh.steps_per_slice, part);
 }
 
 }  // namespace
