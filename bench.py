@@ -12,7 +12,9 @@ Timed region (value): exactly K steps issued on one stream between two events. A
 before the start event keeps the GPU busy while the host enqueues all K steps, so the region
 measures back-to-back GPU execution of the steps, not host launch gaps (measured here, replaying
 HIP graphs of the steps was slower than plain stream launches; --graph times that variant).
-Per-kernel region: the same K steps again, with an event after every library call.
+Per-kernel region: the same K steps again, every library call issued 8 times back to back with an
+event after each group (the calls are idempotent), so a call's average duration carries 1/8 of
+the cost of an event.
 
 Prints one JSON line. `value` is dense-equivalent TFLOP/s (2 M n_out n_in per layer) of the whole
 step for the prefill workloads, or GB/s of the weight-side bytes (packed values, metadata, U, V)
@@ -43,6 +45,7 @@ PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 (vector / MFMA)
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 MALL_DEFEAT_BYTES = 640 << 20  # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+REPEAT = 8                    # back-to-back launches per timed group in the per-kernel region
 
 # library call -> source file of the kernel it launches (the traffic figures are tied to it)
 KERNEL_SOURCE = {"pack": "pack.hip", "stage2": "linear_bf16.hip"}
@@ -167,19 +170,23 @@ def main():
     n_layers = len(layers)
     calls = ("pack", "stage1", "stage2")
 
-    def step(i, ev=None):
-        """One step on `stream`; ev[c][li] is recorded after call c of layer li when given."""
+    def step(i, ev=None, repeat=1):
+        """One step on `stream`. With `ev`, every library call is issued `repeat` times back to back
+        and ev[c][li] is recorded after the repeats of call c of layer li (the calls are idempotent)."""
         s = sets[i % copies]
         for li, d in enumerate(s):
-            binding.prune24_pack(d["R"], d["values"], d["meta"], stream=stream)
+            for _ in range(repeat):
+                binding.prune24_pack(d["R"], d["values"], d["meta"], stream=stream)
             if ev is not None:
                 ev[0][li].record(stream)
         for li, d in enumerate(s):
-            binding.linear_stage1(d["X"], d["V"], d["ws"], stream=stream)
+            for _ in range(repeat):
+                binding.linear_stage1(d["X"], d["V"], d["ws"], stream=stream)
             if ev is not None:
                 ev[1][li].record(stream)
-            binding.linear_stage2(d["X"], d["values"], d["meta"], d["U"], d["ws"], n_out=d["Y"].shape[1],
-                                  out=d["Y"], stream=stream)
+            for _ in range(repeat):
+                binding.linear_stage2(d["X"], d["values"], d["meta"], d["U"], d["ws"], n_out=d["Y"].shape[1],
+                                      out=d["Y"], stream=stream)
             if ev is not None:
                 ev[2][li].record(stream)
 
@@ -215,20 +222,16 @@ def main():
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
 
-        # per-kernel region: the same K steps, an event after every call; then pairs of events with
-        # nothing between them, whose interval (the cost of an event itself) is taken off each call
+        # per-kernel region: the same K steps with every library call issued REPEAT times back to back
+        # and an event after each group, so the cost of an event is spread over REPEAT launches
         evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(n_layers)] for _ in calls]
                for _ in range(args.steps)]
         first = torch.cuda.Event(enable_timing=True)
-        empty = [torch.cuda.Event(enable_timing=True) for _ in range(41)]
-        torch.cuda._sleep(spin_cycles)
+        torch.cuda._sleep(spin_cycles * REPEAT)
         first.record(stream)
         for i in range(args.steps):
-            step(i, evs[i])
-        for e in empty:
-            e.record(stream)
+            step(i, evs[i], repeat=REPEAT)
         torch.cuda.synchronize()
-        event_ms = float(np.median([empty[j].elapsed_time(empty[j + 1]) for j in range(len(empty) - 1)]))
 
     # per-call durations (ms), averaged over the steps: the interval since the previous event
     call_ms = {c: np.zeros(n_layers) for c in calls}
@@ -239,7 +242,7 @@ def main():
             call_ms[calls[c]][li] += prev.elapsed_time(ev[c][li])
             prev = ev[c][li]
     for c in calls:
-        call_ms[c] = call_ms[c] / args.steps - event_ms
+        call_ms[c] = call_ms[c] / (args.steps * REPEAT)
 
     ms_per_step = total_ms / args.steps
     flop_step = sum(2 * L.M * L.n_out * L.n_in for L in layers)
@@ -299,7 +302,6 @@ def main():
                      pack_GBps=round(pbytes_step / pack_s / 1e9, 1),
                      linear_dense_equiv_TFLOPs=round(
                          flop_step / ((call_ms["stage1"].sum() + call_ms["stage2"].sum()) * 1e-3) / 1e12, 1)),
-        event_overhead_us=round(event_ms * 1e3, 3),
         input_generation_s=round(gen_s, 1),
     )
 
