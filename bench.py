@@ -162,7 +162,7 @@ def main():
                 values=torch.empty((*binding.tiles(L.n_out, L.n_in), 64, 8), dtype=tdt, device=dev),
                 meta=torch.empty((*binding.tiles(L.n_out, L.n_in), 2, 16), dtype=torch.int32, device=dev),
                 Y=torch.empty((L.M, L.n_out), dtype=torch.float32, device=dev),
-                ws=torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)))
+                ws=torch.zeros(max(ws_n, 256), dtype=torch.uint8, device=dev)))
         sets.append(s)
     torch.cuda.synchronize()
 

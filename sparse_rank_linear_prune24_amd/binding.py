@@ -126,6 +126,14 @@ def workspace_bytes(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype) -
     return int(lib().splr_linear_workspace_bytes(M, n_out, n_in, r, code))
 
 
+def new_workspace(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype, device="cuda") -> Optional[torch.Tensor]:
+    """A workspace for splr_linear with these sizes (None when none is needed). Any workspace of at
+    least workspace_bytes() serves any call; this one is zero-filled so that nothing depends on
+    leftover contents."""
+    need = workspace_bytes(M, n_out, n_in, r, dtype)
+    return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
+
+
 def _linear_args(X, values, U, n_out, out, workspace, with_workspace=True):
     M, n_in = X.shape
     if n_out is None:
@@ -133,9 +141,8 @@ def _linear_args(X, values, U, n_out, out, workspace, with_workspace=True):
     r = 0 if U is None else U.shape[1]
     if out is None:
         out = torch.empty((M, n_out), dtype=torch.float32, device=X.device)
-    need = workspace_bytes(M, n_out, n_in, r, X.dtype)
-    if workspace is None and need and with_workspace:
-        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    if workspace is None and with_workspace:
+        workspace = new_workspace(M, n_out, n_in, r, X.dtype, X.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return M, n_in, n_out, r, out, workspace, ws_bytes
 

@@ -10,9 +10,10 @@
 // The packed layout stores each 16-row x 64-column tile in exactly this A order, so a wave reads
 // its S fragment as 1 KiB of contiguous memory and its metadata as 128 contiguous bytes. X is
 // row-major: it is loaded with row-contiguous (coalesced) 16-byte loads and staged in LDS with a
-// padded 144-byte row pitch, from which the B fragments are read without bank conflicts.
+// padded 160-byte row pitch, from which the B fragments are read without bank conflicts.
 //
-// The rank-r term is folded into the same accumulators in the epilogue with the same instruction:
+// The rank-r term is folded into the same accumulators with the same instruction (before the main
+// loop when r <= 64, so that it overlaps the loop's first loads; block by block after it otherwise):
 // dense U is the sum of two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of every group
 // of four ranks), so acc += U_tile T_tile^T is two structured-sparse MFMAs per 64 ranks with
 // constant index operands. T (float32) enters as a bfloat16 high part plus a bfloat16 correction.
@@ -440,6 +441,17 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   }
   if (u_pre && r > 0) us.finish(ulds);
   lds_barrier();
+  const int nrow0 = n0 + wave * 16 * NI;
+  // rank-r term first when T's pair is already in LDS: its MFMAs run while the main loop's first
+  // loads are in flight (the accumulators start from U T^T instead of zero)
+  if (t_pre) {
+#pragma unroll
+    for (int b = 0; b < kPreRankBlocks; ++b)
+      if (64 * b < r)
+        lowrank_block<NI, NJ>(acc, U, tpair[2 * b], tpair[2 * b + 1], n_out, r, 64 * b, nrow0, lane,
+                              u_pre ? ulds : nullptr, wave * 16 * NI);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   read_b(xs0, bx[0]);
   lds_barrier();  // every wave's reads of slot 0 are done before step 0 overwrites it
   __builtin_amdgcn_sched_barrier(0);
@@ -449,18 +461,9 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   for (int kc0 = nk_full; kc0 < nk_pad; kc0 += kUnroll)
     static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, u, std::true_type{}); });
 
-  const int nrow0 = n0 + wave * 16 * NI;
-  // rank-r term, 64 ranks at a time: every wave adds its U block times T. T's pair is already in
-  // LDS (built before the loop, published by the prologue's barriers), or, for larger r, the
-  // workgroup builds it block by block in the now free X slots (the last step's barrier has retired
-  // every read of them)
-  if (t_pre) {
-#pragma unroll
-    for (int b = 0; b < kPreRankBlocks; ++b)
-      if (64 * b < r)
-        lowrank_block<NI, NJ>(acc, U, tpair[2 * b], tpair[2 * b + 1], n_out, r, 64 * b, nrow0, lane,
-                              u_pre ? ulds : nullptr, wave * 16 * NI);
-  } else {
+  // larger r: the rank-r term, 64 ranks at a time, after the loop; the workgroup builds T's pair
+  // block by block in the now free X slots (the last step's barrier has retired every read of them)
+  if (!t_pre) {
     for (int j0 = 0; j0 < r; j0 += 64) {
       build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs0, xs1, threadIdx.x);
       lds_barrier();

@@ -1,15 +1,13 @@
 // First stage of the low-rank product, T = X V^T (LoSparse page, §3.2: the input is multiplied by
 // the thin factors; in the orientation used here X [M x n_in] times V^T [n_in x r]).
 //
-// bf16: a workgroup owns 16*TF tokens x 16*RF ranks (all of r when r is a multiple of 64) over one
-// slice of K; its waves take interleaved 64-column K steps of the slice, each wave staging its own X
-// and V rows in a private LDS region (row-contiguous loads, padded pitch) with several steps of
-// loads in flight, and feed gfx950's structured-sparse MFMA: X is the dense B operand; V is the A
-// operand, dense V being the sum of two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of
-// every group of four columns). Covering all ranks in one workgroup stages each X row once; the K
-// slices give the chip enough workgroups. The waves' partial sums are combined through LDS in wave
-// order and each slice writes its float32 partial sum of T; the second stage adds the slices in
-// slice order (deterministic, no atomics).
+// bf16: a workgroup owns 16*TF tokens x 16*RF ranks over one slice of K; its waves take interleaved
+// 64-column K steps of the slice, each wave staging its own X and V rows in a private LDS region
+// (row-contiguous loads, padded pitch) with several steps of loads in flight, and feed gfx950's
+// structured-sparse MFMA: X is the dense B operand; V is the A operand, dense V being the sum of two
+// 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of every group of four columns). The
+// waves' partial sums are combined through LDS in wave order and each slice writes its float32
+// partial sum of T; the second stage adds the slices in slice order (deterministic, no atomics).
 // fp32: one wave per output, lanes stride over K, fixed-order butterfly reduction.
 #include <algorithm>
 #include <type_traits>
@@ -175,11 +173,11 @@ __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restric
 
 namespace {
 
-// bf16 first-stage shape. Enough workgroups (~256) come first from splitting the ranks (32 tokens x
-// 64, 32 or 16 ranks per workgroup, the widest split that suffices), so that T needs no K slices
-// and stage 2 reads it once; only when even 16 ranks per workgroup leave the chip short does the
-// stage split K into slices (at most kMaxLowrankSlices, at most one per K step), with 64 ranks per
-// workgroup to stage each X row once.
+// bf16 first-stage shape. Measured on MI355X, the stage runs fastest as about 256 small workgroups:
+// 16 ranks per workgroup for decode-sized inputs (M <= 16) and 32 ranks otherwise (when 32 divides
+// r), with K split into slices only as far as needed to reach ~256 workgroups (at most
+// kMaxLowrankSlices, at most one per K step). Wider rank blocks stage each X row fewer times but
+// leave too few workgroups, or need more slices for the second stage to add.
 struct LowrankShape {
   int tf, rf, slices, steps_per_slice;
 };
@@ -188,16 +186,11 @@ LowrankShape lowrank_shape(int64_t M, int64_t n_in, int64_t r) {
   constexpr int64_t kWant = 256;
   LowrankShape sh;
   sh.tf = M <= 16 ? 1 : 2;
+  sh.rf = (M > 16 && r % 32 == 0) ? 2 : 1;
   const int64_t TK = (n_in + 63) / 64, token_blocks = ceil_div(M, 16 * sh.tf);
-  sh.rf = 0;
-  for (int rf : {4, 2, 1})
-    if (sh.rf == 0 && r % (16 * rf) == 0 && token_blocks * (r / (16 * rf)) >= kWant) sh.rf = rf;
-  int64_t slices = 1;
-  if (sh.rf == 0) {
-    sh.rf = r % 64 == 0 ? 4 : (r % 32 == 0 ? 2 : 1);
-    const int64_t base = token_blocks * (r / (16 * sh.rf));
-    slices = std::min<int64_t>(std::min<int64_t>(kMaxLowrankSlices, TK), std::max<int64_t>(1, ceil_div(kWant, base)));
-  }
+  const int64_t base = token_blocks * (r / (16 * sh.rf));
+  const int64_t slices =
+      std::min<int64_t>(std::min<int64_t>(kMaxLowrankSlices, TK), std::max<int64_t>(1, ceil_div(kWant, base)));
   sh.steps_per_slice = (int)ceil_div(TK, slices);
   sh.slices = (int)ceil_div(TK, sh.steps_per_slice);
   return sh;
@@ -232,15 +225,9 @@ hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in,
   float* part = (float*)workspace;
   if (bf16) {
     const LowrankShape sh = lowrank_shape(M, n_in, r);
-    if (sh.tf == 1) {
-      if (sh.rf == 4) launch_part<1, 4>(sh, X, V, M, n_in, r, part, stream);
-      else if (sh.rf == 2) launch_part<1, 2>(sh, X, V, M, n_in, r, part, stream);
-      else launch_part<1, 1>(sh, X, V, M, n_in, r, part, stream);
-    } else {
-      if (sh.rf == 4) launch_part<2, 4>(sh, X, V, M, n_in, r, part, stream);
-      else if (sh.rf == 2) launch_part<2, 2>(sh, X, V, M, n_in, r, part, stream);
-      else launch_part<2, 1>(sh, X, V, M, n_in, r, part, stream);
-    }
+    if (sh.tf == 1) launch_part<1, 1>(sh, X, V, M, n_in, r, part, stream);
+    else if (sh.rf == 2) launch_part<2, 2>(sh, X, V, M, n_in, r, part, stream);
+    else launch_part<2, 1>(sh, X, V, M, n_in, r, part, stream);
   } else {
     const int64_t waves = M * r;
     lowrank_f32_kernel<<<dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, stream>>>(

@@ -15,7 +15,7 @@ def test_graph_replays_match_eager(M, r):
     L = inputs.random_case(M, 1024, 512, r, "bf16", seed=5, n_outliers=4)
     R, X, U, V = (to_dev(a, "bf16") for a in (L.R, L.X, L.U, L.V))
     values, meta = binding.prune24_pack(R)
-    ws = torch.empty(binding.workspace_bytes(M, 512, 1024, r, torch.bfloat16), dtype=torch.uint8, device=X.device)
+    ws = binding.new_workspace(M, 512, 1024, r, torch.bfloat16, X.device)
     Y = torch.empty((M, 512), dtype=torch.float32, device=X.device)
 
     def step(stream):

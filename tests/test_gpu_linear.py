@@ -184,9 +184,27 @@ def test_stages_equal_linear(dtype, M, n_in, n_out, r):
     Xd, Ud, Vd = to_dev(L.X, dtype), to_dev(L.U if r else None, dtype), to_dev(L.V if r else None, dtype)
     vd, md = binding.prune24_pack(to_dev(L.R, dtype))
     Y1 = binding.linear(Xd, vd, md, Ud, Vd, n_out=n_out)
-    need = binding.workspace_bytes(M, n_out, n_in, r, Xd.dtype)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=Xd.device) if need else None
+    ws = binding.new_workspace(M, n_out, n_in, r, Xd.dtype, Xd.device)
     binding.linear_stage1(Xd, Vd, ws)
     Y2 = binding.linear_stage2(Xd, vd, md, Ud, ws, n_out=n_out)
     torch.cuda.synchronize()
     assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves calls of different shapes in a row (K split into slices or not, ragged
+    token counts): each gives the same Y, bit for bit, as a call with a fresh workspace, whatever
+    the previous call left in it."""
+    shapes = [(2048, 4096, 256, 64), (16, 4096, 128, 64), (40, 1056, 100, 80), (300, 2080, 96, 128),
+              (128, 4096, 256, 192), (16, 4096, 128, 64)]
+    need = max(binding.workspace_bytes(M, n_out, n_in, r, torch.bfloat16) for M, n_in, n_out, r in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage: NaN-like floats
+    for i, (M, n_in, n_out, r) in enumerate(shapes):
+        print(f"[reuse] call {i}: M={M} n_in={n_in} n_out={n_out} r={r}", flush=True)
+        L = inputs.random_case(M, n_in, n_out, r, "bf16", seed=100 + i, n_outliers=2)
+        Xd, Ud, Vd = to_dev(L.X, "bf16"), to_dev(L.U, "bf16"), to_dev(L.V, "bf16")
+        vd, md = binding.prune24_pack(to_dev(L.R, "bf16"))
+        Y_shared = binding.linear(Xd, vd, md, Ud, Vd, n_out=n_out, workspace=ws)
+        Y_fresh = binding.linear(Xd, vd, md, Ud, Vd, n_out=n_out)
+        torch.cuda.synchronize()
+        assert torch.equal(Y_shared.view(torch.int32), Y_fresh.view(torch.int32))
