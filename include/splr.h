@@ -93,8 +93,9 @@ splr_status_t splr_packed_bytes(int64_t n_out, int64_t n_in, splr_dtype_t dtype,
 
 /*
  * splr_linear_workspace_bytes -- device workspace that splr_linear needs for these sizes
- * (0 when none).  It holds the first low-rank stage T = X V^T and, for larger problems, float32
- * partial sums of T over slices of n_in (at most 16 slices).
+ * (0 when none).  It holds the first low-rank stage T = X V^T as float32 partial sums over at most
+ * 16 slices of n_in (one slice for fp32).  Everything a call reads from it is written by the same
+ * call, so it needs no initialisation and may be reused by calls of any shape that fit.
  */
 size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64_t r,
                                    splr_dtype_t dtype);
