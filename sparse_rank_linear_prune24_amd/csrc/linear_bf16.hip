@@ -476,12 +476,11 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
 
 // ----------------------------------------------------------------------------------- decode
 
-template <int MB, int P>
-__global__ __launch_bounds__(256) void linear_decode_kernel(
+template <int MB, int P, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
     const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, float* __restrict__ Y, int M, int K,
     int n_out, int r) {
-  constexpr int WAVES = 4;
   constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
   __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
   __shared__ f32x4_t red[(WAVES - 1) * MB * 64];
@@ -492,14 +491,6 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
   const int sub = lane & 15, quad = lane >> 4;
   const int tr = blockIdx.x, m0 = blockIdx.y * 16 * MB;
   const int TK = (K + 63) / 64;
-
-  const bool t_pre = r <= 64 * kPreRankBlocks;
-  if (t_pre) {  // T's pair first, while registers are free (published by the barrier after the loop)
-#pragma unroll
-    for (int b = 0; b < kPreRankBlocks; ++b)
-      if (64 * b < r) build_t_pair<16 * MB, 64 * WAVES>(Tpart, slices, M, r, m0, 64 * b, tpair[2 * b],
-                                                         tpair[2 * b + 1], threadIdx.x);
-  }
 
   const u32x4_t* vsrc = values + (size_t)tr * TK * 64 + lane;
   const uint16_t* msrc = (const uint16_t*)(meta + (size_t)tr * TK * 32 + sub + 16 * (quad >> 1)) + (quad & 1);
@@ -518,37 +509,61 @@ __global__ __launch_bounds__(256) void linear_decode_kernel(
 #pragma unroll
   for (int j = 0; j < MB; ++j) acc[0][j] = f32x4_t{0, 0, 0, 0};
 
-  // this wave's steps: kc = wave, wave + 4, ... ; P of them in flight
+  // This wave's steps are kc = wave, wave + 4, ...; a ring of P steps of loads stays in flight:
+  // slot u holds step s0 + u and is refilled with step s0 + u + P as soon as it has been consumed.
+  // Branch-free: steps past the wave's last one load a clamped step and contribute through a
+  // zeroed S operand.
   const int my_steps = (TK - wave + WAVES - 1) / WAVES;
-  for (int s0 = 0; s0 < my_steps; s0 += P) {
-    u32x4_t sa[P], xr[P][kXLoads];
-    uint32_t sw[P];
+  const int n_pad = max(1, (my_steps + P - 1) / P) * P;  // at least the final round (a wave may have no steps)
+  u32x4_t sa[P], xr[P][kXLoads];
+  uint32_t sw[P];
+  auto load = [&](int s, u32x4_t& va, uint32_t& wa, u32x4_t (&xv)[kXLoads]) {
+    const int kc = min(wave + s * WAVES, TK - 1);
+    va = vsrc[(size_t)kc * 64];
+    wa = msrc[(size_t)kc * 64];
+    int col = kc * 64;
+    if (col + 8 * xchunk >= K) col -= 32;  // half tail step: re-read valid columns (S is zero there)
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int kc = min(wave + (s0 + u) * WAVES, TK - 1);
-      sa[u] = vsrc[(size_t)kc * 64];
-      sw[u] = msrc[(size_t)kc * 64];
-      int col = kc * 64;
-      if (col + 8 * xchunk >= K) col -= 32;
-#pragma unroll
-      for (int t = 0; t < kXLoads; ++t) xr[u][t] = *(const u32x4_t*)(xsrc[t] + col);
-    }
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const bool live = s0 + u < my_steps;  // wave-uniform
-#pragma unroll
-      for (int t = 0; t < kXLoads; ++t) st[xdst[t]] = xr[u][t];
-      const uint32_t keep = live ? ~0u : 0u;
-      const bf16x8_t a = as_bf16x8(sa[u] & keep);
-      const int idx = (int)(sw[u] & keep);
-#pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        const int row = (16 * j + sub) * kXPitchU4;
-        const bf16x16_t bx = cat16(as_bf16x8(st[row + quad]), as_bf16x8(st[row + 4 + quad]));
-        acc[0][j] = smfmac16x16x64(a, bx, acc[0][j], idx);
-      }
-    }
+    for (int t = 0; t < kXLoads; ++t) xv[t] = *(const u32x4_t*)(xsrc[t] + col);
+  };
+
+  // T's pair: its loads go out first, the ring's next, and the pair is written to LDS while the
+  // ring's loads are in flight (published by the barrier after the loop)
+  const bool t_pre = r <= 64 * kPreRankBlocks;
+  TPairBuilder<16 * MB, 64 * WAVES> tb;
+  if (t_pre && r > 0) {
+    tb.init(Tpart, slices, M, r, m0, 0, threadIdx.x);
+    tb.issue(0);
   }
+  static_for<P>([&](auto uu) {  // issued in slot order (fenced), as the loop refills them
+    constexpr int u = decltype(uu)::value;
+    load(u, sa[u], sw[u], xr[u]);
+    asm volatile("" ::: "memory");
+  });
+  if (t_pre && r > 0) tb.finish(tpair[0], tpair[1]);
+
+  auto step = [&](int s, auto uu, auto refill) {
+    constexpr int u = decltype(uu)::value;
+#pragma unroll
+    for (int t = 0; t < kXLoads; ++t) st[xdst[t]] = xr[u][t];
+    const uint32_t keep = s < my_steps ? ~0u : 0u;  // wave-uniform
+    const bf16x8_t a = as_bf16x8(sa[u] & keep);
+    const int idx = (int)(sw[u] & keep);
+    if constexpr (decltype(refill)::value) load(s + P, sa[u], sw[u], xr[u]);
+    // compiler-only fence: the refill stays in this step (not rotated into the next iteration,
+    // which would shorten the prefetch distance of this slot)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int row = (16 * j + sub) * kXPitchU4;
+      const bf16x16_t bx = cat16(as_bf16x8(st[row + quad]), as_bf16x8(st[row + 4 + quad]));
+      acc[0][j] = smfmac16x16x64(a, bx, acc[0][j], idx);
+    }
+  };
+  // every round but the last refills its slots; the last round loads nothing past the end
+  for (int s0 = 0; s0 + P < n_pad; s0 += P)
+    static_for<P>([&](auto uu) { step(s0 + decltype(uu)::value, uu, std::true_type{}); });
+  static_for<P>([&](auto uu) { step(n_pad - P + decltype(uu)::value, uu, std::false_type{}); });
 
   // fixed-order combination of the waves' partial sums (into wave 0)
   if (wave > 0) {
@@ -585,9 +600,9 @@ template <int MB>
 hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                          int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, float* Y,
                          hipStream_t stream) {
-  constexpr int P = MB == 1 ? 8 : 4;
+  constexpr int P = MB == 1 ? 8 : 4, W = 4;
   dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(M, 16 * MB));
-  linear_decode_kernel<MB, P><<<grid, dim3(256), 0, stream>>>(
+  linear_decode_kernel<MB, P, W><<<grid, dim3(64 * W), 0, stream>>>(
       (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, (int)M, (int)n_in,
       (int)n_out, (int)r);
   return hipGetLastError();

@@ -81,50 +81,53 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
 
   // This wave's steps are kc = kb + wave, kb + wave + WAVES, ... < ke; a ring of D steps of loads
   // stays in flight: slot u holds step s0 + u and is refilled with step s0 + u + D right after it is
-  // written to LDS. The loop is branch-free: steps past the wave's last one (and the duplicated half
-  // of a 32-column tail step) contribute through a zeroed A operand, never through masked loads.
+  // written to LDS; the final round refills nothing. The loop is branch-free: steps past the wave's
+  // last one (and the duplicated half of a 32-column tail step) contribute through a zeroed A
+  // operand, never through masked loads.
   const int my_steps = max(0, (ke - kb - wave + WAVES - 1) / WAVES);
-  const int n_pad = (my_steps + D - 1) / D * D;
+  const int n_pad = max(1, (my_steps + D - 1) / D) * D;  // at least the final round (a wave may have no steps)
   u32x4_t ring[D][kLoads];
   static_for<D>([&](auto uu) {  // issued in slot order (fenced), as the loop refills them
     load(kb + wave + decltype(uu)::value * WAVES, ring[decltype(uu)::value]);
     asm volatile("" ::: "memory");
   });
-  for (int s0 = 0; s0 < n_pad; s0 += D) {
-    static_for<D>([&](auto uu) {
-      constexpr int u = decltype(uu)::value;
-      const int s = s0 + u, kc = kb + wave + s * WAVES;
+  auto step = [&](int s, auto uu, auto refill) {
+    constexpr int u = decltype(uu)::value;
+    const int kc = kb + wave + s * WAVES;
 #pragma unroll
-      for (int t = 0; t < kLoads; ++t) st[dst[t]] = ring[u][t];
-      load(kc + D * WAVES, ring[u]);
-      // compiler-only fence: the refill stays in this step (not rotated into the next iteration,
-      // which would shorten the prefetch distance of this slot)
-      asm volatile("" ::: "memory");
-      // A operand (V rows j0 + 16 a + sub, dense columns 16 q .. 16 q + 15) as two fixed-pattern
-      // 2:4 halves; zero when the step is past this wave's last, or when it is the tail step and
-      // these columns are the re-read ones (q >= 2)
-      const bool live = s < my_steps && !(half_tail && kc == TK - 1 && quad >= 2);
-      const uint32_t keep = live ? ~0u : 0u;
-      bf16x16_t bx[TF];
+    for (int t = 0; t < kLoads; ++t) st[dst[t]] = ring[u][t];
+    if constexpr (decltype(refill)::value) load(kc + D * WAVES, ring[u]);
+    // compiler-only fence: the refill stays in this step (not rotated into the next iteration,
+    // which would shorten the prefetch distance of this slot)
+    asm volatile("" ::: "memory");
+    // A operand (V rows j0 + 16 a + sub, dense columns 16 q .. 16 q + 15) as two fixed-pattern
+    // 2:4 halves; zero when the step is past this wave's last, or when it is the tail step and
+    // these columns are the re-read ones (q >= 2)
+    const bool live = s < my_steps && !(half_tail && kc == TK - 1 && quad >= 2);
+    const uint32_t keep = live ? ~0u : 0u;
+    bf16x16_t bx[TF];
+#pragma unroll
+    for (int f = 0; f < TF; ++f) {
+      const int xrow = (16 * f + sub) * kPitchU4;
+      bx[f] = cat16(as_bf16x8(st[xrow + quad]), as_bf16x8(st[xrow + 4 + quad]));
+    }
+#pragma unroll
+    for (int a = 0; a < RF; ++a) {
+      const int vrow = (16 * TF + 16 * a + sub) * kPitchU4;
+      const u32x4_t d0 = st[vrow + 2 * quad] & keep, d1 = st[vrow + 2 * quad + 1] & keep;
+      const bf16x8_t a01 = as_bf16x8(u32x4_t{d0[0], d0[2], d1[0], d1[2]});
+      const bf16x8_t a23 = as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]});
 #pragma unroll
       for (int f = 0; f < TF; ++f) {
-        const int xrow = (16 * f + sub) * kPitchU4;
-        bx[f] = cat16(as_bf16x8(st[xrow + quad]), as_bf16x8(st[xrow + 4 + quad]));
+        acc[a][f] = smfmac16x16x64(a01, bx[f], acc[a][f], 0x4444);
+        acc[a][f] = smfmac16x16x64(a23, bx[f], acc[a][f], 0xEEEE);
       }
-#pragma unroll
-      for (int a = 0; a < RF; ++a) {
-        const int vrow = (16 * TF + 16 * a + sub) * kPitchU4;
-        const u32x4_t d0 = st[vrow + 2 * quad] & keep, d1 = st[vrow + 2 * quad + 1] & keep;
-        const bf16x8_t a01 = as_bf16x8(u32x4_t{d0[0], d0[2], d1[0], d1[2]});
-        const bf16x8_t a23 = as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]});
-#pragma unroll
-        for (int f = 0; f < TF; ++f) {
-          acc[a][f] = smfmac16x16x64(a01, bx[f], acc[a][f], 0x4444);
-          acc[a][f] = smfmac16x16x64(a23, bx[f], acc[a][f], 0xEEEE);
-        }
-      }
-    });
-  }
+    }
+  };
+  // every round but the last refills its slots; the last round loads nothing past the end
+  for (int s0 = 0; s0 + D < n_pad; s0 += D)
+    static_for<D>([&](auto uu) { step(s0 + decltype(uu)::value, uu, std::true_type{}); });
+  static_for<D>([&](auto uu) { step(n_pad - D + decltype(uu)::value, uu, std::false_type{}); });
 
   // combine the waves in order; D rows = ranks j0 + 16 a + 4*(lane/16) + 0..3, column = token
   // m0 + 16 f + lane%16
