@@ -46,11 +46,13 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         lib.splr_ref_prune24_pack.argtypes = [P, I64, I64, ctypes.c_int, P, P]
+        lib.splr_ref_prune24_pack_scaled.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
         lib.splr_ref_unpack.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
         lib.splr_ref_unpack.restype = ctypes.c_int
         lib.splr_ref_linear.argtypes = [P, I64, I64, P, P, I64, P, P, I64, ctypes.c_int, P, I64, P]
         lib.splr_ref_dense_reconstruct.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P]
-        for f in (lib.splr_ref_prune24_pack, lib.splr_ref_linear, lib.splr_ref_dense_reconstruct):
+        for f in (lib.splr_ref_prune24_pack, lib.splr_ref_prune24_pack_scaled, lib.splr_ref_linear,
+                  lib.splr_ref_dense_reconstruct):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -82,6 +84,25 @@ def prune24_pack(R: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
     rc = _load().splr_ref_prune24_pack(_ptr(R), n_out, n_in, _DT[dtype], _ptr(values), _ptr(meta))
     if rc:
         raise ValueError(f"splr_ref_prune24_pack failed ({rc}) for shape {R.shape}")
+    return values, meta
+
+
+def prune24_pack_scaled(R: np.ndarray, d: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Activation-aware 2:4 projection of R [n_out x n_in] with per-column scales d (float32
+    [n_in]): keeps the two entries of largest |R[n][k]| * |d[k]| per group (exact score, ties to the
+    lower column, NaN scores above every number), storing R's own entries. Same layout as
+    prune24_pack."""
+    R = _check(R, dtype, 2, "R")
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    n_out, n_in = R.shape
+    if d.shape != (n_in,):
+        raise ValueError(f"d: expected shape ({n_in},), got {d.shape}")
+    TR, TK = tiles(n_out, n_in)
+    values = np.empty((TR, TK, 64, 8), dtype=_NP[dtype])
+    meta = np.empty((TR, TK, 2, 16), dtype=np.uint32)
+    rc = _load().splr_ref_prune24_pack_scaled(_ptr(R), _ptr(d), n_out, n_in, _DT[dtype], _ptr(values), _ptr(meta))
+    if rc:
+        raise ValueError(f"splr_ref_prune24_pack_scaled failed ({rc}) for shape {R.shape}")
     return values, meta
 
 

@@ -27,6 +27,11 @@
  *                                nonzero (3BASiL article, "A three-block ADMM replaces alternating
  *                                minimization").  Hard thresholding per group = keep the two
  *                                largest magnitudes unchanged, zero the rest.
+ *   splr_ref_prune24_pack_scaled
+ *                             -- the sparse subproblem with a diagonal Hessian: hard thresholding is
+ *                                applied to the residual scaled column by column by D, which gives
+ *                                Wanda's score |W_ij| * ||X_j|| (HASSLE-free page, §4.1.2); the kept
+ *                                entries are the unscaled residual (scaling, thresholding, unscaling).
  *   splr_ref_linear           -- the compressed forward pass sums the sparse product and the
  *                                low-rank product, computed side by side (LoSparse page, §3 and
  *                                §3.2), here as Y = X S^T + (X V^T) U^T.
@@ -35,6 +40,7 @@
  * Readings where the pages are silent (ties, special values, layout) are the ones listed at the
  * top of each function.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -71,8 +77,21 @@ static void copy_elem(void *dst, size_t di, const void *src, size_t si, int dtyp
     ((uint32_t *)dst)[di] = ((const uint32_t *)src)[si];
 }
 
-/* Position i of a group outranks position j when its magnitude is larger, or equal with i < j. */
-static int outranks(const uint32_t key[4], int i, int j) {
+/* Activation-aware key of entry i (column k): |R| * |d_k| as a binary64 value.  Both factors have
+   at most 24 significant bits and binary32 range, so the product is exact (no rounding, no
+   overflow, no underflow) and keys order entries by the exact score.  NaN scores (a NaN entry or
+   scale, or infinity times zero) are all equal and rank above every number.  Keys are compared as
+   unsigned integers: for non-negative binary64 values that is the numeric order. */
+static uint64_t scaled_key(const void *base, int dtype, size_t i, float dk) {
+  const double p = fabs(load_f64(base, dtype, i)) * fabs((double)dk);
+  if (p != p) return 0x7FF8000000000000ull;
+  uint64_t u;
+  memcpy(&u, &p, 8);
+  return u;
+}
+
+/* Position i of a group outranks position j when its key is larger, or equal with i < j. */
+static int outranks(const uint64_t key[4], int i, int j) {
   return key[i] > key[j] || (key[i] == key[j] && i < j);
 }
 
@@ -103,14 +122,15 @@ size_t splr_ref_packed_meta(int64_t n_out, int64_t n_in) {
 }
 
 /*
- * 2:4 projection and pack.  For every row and every group of four consecutive input columns:
+ * Shared selection of both packs: for every row and every group of four consecutive input columns,
  * keep the entry that outranks the other three and the entry that outranks the remaining two,
- * unchanged (bit copies); store them in ascending position order and record their positions.
+ * unchanged (bit copies); store them in ascending position order and record their positions.  The
+ * key is the magnitude (d == NULL) or the activation-aware score (d = per-column scales).
  * Readings: ties go to the lower position; groups with fewer than two nonzeros still store two
  * slots (zeros included), so the output layout is fixed.
  */
-int splr_ref_prune24_pack(const void *R, int64_t n_out, int64_t n_in, int dtype, void *values,
-                          uint32_t *meta) {
+static int pack_by_keys(const void *R, const float *d, int64_t n_out, int64_t n_in, int dtype, void *values,
+                        uint32_t *meta) {
   if (!R || !values || !meta) return SPLR_REF_EINVAL;
   if (n_out < 0 || n_in < 0 || n_in % 32 != 0) return SPLR_REF_EINVAL;
   if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
@@ -122,8 +142,9 @@ int splr_ref_prune24_pack(const void *R, int64_t n_out, int64_t n_in, int dtype,
   for (int64_t n = 0; n < n_out; ++n) {
     for (int64_t g = 0; g < groups; ++g) {
       const size_t base = (size_t)n * (size_t)n_in + 4 * (size_t)g;
-      uint32_t key[4];
-      for (int i = 0; i < 4; ++i) key[i] = magnitude_key(R, dtype, base + i);
+      uint64_t key[4];
+      for (int i = 0; i < 4; ++i)
+        key[i] = d ? scaled_key(R, dtype, base + i, d[4 * g + i]) : (uint64_t)magnitude_key(R, dtype, base + i);
       int first = 0;
       for (int i = 1; i < 4; ++i)
         if (outranks(key, i, first)) first = i;
@@ -140,6 +161,20 @@ int splr_ref_prune24_pack(const void *R, int64_t n_out, int64_t n_in, int dtype,
     }
   }
   return SPLR_REF_OK;
+}
+
+/* 2:4 projection and pack (identity Hessian): keys are the magnitudes. */
+int splr_ref_prune24_pack(const void *R, int64_t n_out, int64_t n_in, int dtype, void *values,
+                          uint32_t *meta) {
+  return pack_by_keys(R, NULL, n_out, n_in, dtype, values, meta);
+}
+
+/* Activation-aware 2:4 projection and pack (diagonal Hessian): keys are |R[n][k]| * |d[k]|; the
+   stored entries are R's own.  d: float32 [n_in]. */
+int splr_ref_prune24_pack_scaled(const void *R, const float *d, int64_t n_out, int64_t n_in, int dtype,
+                                 void *values, uint32_t *meta) {
+  if (!d) return SPLR_REF_EINVAL;
+  return pack_by_keys(R, d, n_out, n_in, dtype, values, meta);
 }
 
 static void decode_nibble(const uint32_t *meta, int64_t n, int64_t g, int64_t n_in, int *a, int *b) {

@@ -103,6 +103,14 @@ def residual(W, U, V, dtype: str) -> np.ndarray:
     return from_f64(w - to_f64(U, dtype) @ to_f64(V, dtype), dtype)
 
 
+def column_scales(X, dtype: str) -> np.ndarray:
+    """Per-input-column scales for the activation-aware pack: the 2-norms of the calibration
+    activations' columns, sqrt(sum_m X[m][k]^2), in float64 from the stored X, rounded to float32.
+    (Set-up, like `residual`: the pack takes d as an input.)"""
+    x = to_f64(X, dtype)
+    return np.sqrt(np.einsum("mk,mk->k", x, x)).astype(np.float32)
+
+
 @dataclass
 class Layer:
     name: str
