@@ -305,9 +305,56 @@ def main():
         input_generation_s=round(gen_s, 1),
     )
 
+    out["next"] = measure_next(binding, inputs, layers, sets, copies, stream, dev, args)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, layers, dtype, flop_step, wbytes_step, decode, args.cpu_rows)
     print(json.dumps(out), flush=True)
+
+
+def time_per_call(issue, n, stream, spin_cycles):
+    """Average GPU time (ms) of one call: `issue(i)` enqueues call i on `stream`; n calls, each
+    issued REPEAT times back to back, between two events behind a queue-filling spin."""
+    import torch
+    for i in range(3):
+        issue(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(spin_cycles)
+        e0.record(stream)
+        for i in range(n):
+            for _ in range(REPEAT):
+                issue(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (n * REPEAT)
+
+
+def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
+    """The parts built beyond the hot path, each timed per call on every layer of the workload
+    (outside the timed step): the activation-aware pack (keys |R| |d|, d = column norms of the
+    layer's activations)."""
+    import torch
+    n = max(8, args.steps // 2)
+    spin = int(4e4 * n * REPEAT)
+    res = {}
+    per_layer = []
+    for li, L in enumerate(layers):
+        d = torch.from_numpy(inputs.column_scales(L.X, L.dtype)).to(dev)
+        isz = inputs.itemsize(L.dtype)
+        nbytes = pack_bytes(L.n_in, L.n_out, isz) + L.n_in * 4
+
+        def issue(i, li=li, d=d):
+            s = sets[i % copies][li]
+            binding.prune24_pack_scaled(s["R"], d, s["values"], s["meta"], stream=stream)
+
+        ms = time_per_call(issue, n, stream, spin)
+        per_layer.append(dict(layer=L.name, us=round(ms * 1e3, 2), GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                              frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)))
+    res["pack_scaled"] = dict(entry="splr_prune24_pack_scaled", bound="hbm",
+                              work="bytes: R + d + packed values + metadata", per_layer=per_layer)
+    return res
 
 
 def cpu_baseline(cfg, layers, dtype, flop_step, wbytes_step, decode, rows_arg):

@@ -85,6 +85,29 @@ splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr
                                 void* values, uint32_t* meta, hipStream_t stream);
 
 /*
+ * splr_prune24_pack_scaled -- activation-aware (diagonal-Hessian) 2:4 projection, then packing.
+ *
+ * With a diagonal Hessian the sparse step hard-thresholds the residual after scaling input column
+ * k by d_k, which gives Wanda's score |W_ij| * ||X_j|| (HASSLE-free page, §4.1.2); the entries kept
+ * are the residual's own.  Typically d_k is the 2-norm of column k of the calibration activations.
+ *
+ * For each row and each group of four consecutive columns the two entries of largest score
+ * |R[n][k]| * |d[k]| are kept as bit copies.  The score is the exact product (formed in binary64,
+ * which holds the product of two binary32 values exactly), so no rounding decides a choice; equal
+ * scores go to the lower column; NaN scores (NaN entry or scale, infinity times zero) all tie and
+ * outrank every number.  With d == 1 everywhere the result equals splr_prune24_pack's for inputs
+ * with at most one NaN per group.  Bit-exact and deterministic.
+ *
+ *   R      [n_out][n_in] dtype, row-major       input
+ *   d      [n_in] float32                        per-column scales (any sign; |d| is used)
+ *   values, meta                                output, packed layout above
+ * Errors: as splr_prune24_pack; d NULL -> SPLR_ERR_NULL, misaligned d -> SPLR_ERR_ALIGN.
+ */
+splr_status_t splr_prune24_pack_scaled(const void* R, const float* d, int64_t n_out, int64_t n_in,
+                                       splr_dtype_t dtype, void* values, uint32_t* meta,
+                                       hipStream_t stream);
+
+/*
  * splr_packed_bytes -- sizes of the packed values and metadata buffers for an n_out x n_in S.
  * Returns SPLR_ERR_SHAPE / SPLR_ERR_DTYPE / SPLR_ERR_NULL like the other entry points.
  */

@@ -34,7 +34,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
-                               "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC])
+                               "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -47,11 +47,14 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.splr_ref_prune24_pack.argtypes = [P, I64, I64, ctypes.c_int, P, P]
         lib.splr_ref_prune24_pack_scaled.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
+        lib.splr_ref_residual.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P]
+        lib.splr_ref_prune24_pack_residual.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P, P]
         lib.splr_ref_unpack.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
         lib.splr_ref_unpack.restype = ctypes.c_int
         lib.splr_ref_linear.argtypes = [P, I64, I64, P, P, I64, P, P, I64, ctypes.c_int, P, I64, P]
         lib.splr_ref_dense_reconstruct.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int, P]
-        for f in (lib.splr_ref_prune24_pack, lib.splr_ref_prune24_pack_scaled, lib.splr_ref_linear,
+        for f in (lib.splr_ref_prune24_pack, lib.splr_ref_prune24_pack_scaled, lib.splr_ref_residual,
+                  lib.splr_ref_prune24_pack_residual, lib.splr_ref_linear,
                   lib.splr_ref_dense_reconstruct):
             f.restype = ctypes.c_int
         _lib = lib
@@ -103,6 +106,43 @@ def prune24_pack_scaled(R: np.ndarray, d: np.ndarray, dtype: str) -> Tuple[np.nd
     rc = _load().splr_ref_prune24_pack_scaled(_ptr(R), _ptr(d), n_out, n_in, _DT[dtype], _ptr(values), _ptr(meta))
     if rc:
         raise ValueError(f"splr_ref_prune24_pack_scaled failed ({rc}) for shape {R.shape}")
+    return values, meta
+
+
+def residual(W: np.ndarray, U: Optional[np.ndarray], V: Optional[np.ndarray], dtype: str) -> np.ndarray:
+    """R = W - U V with the fused pack's pinned arithmetic: per entry acc = W, then
+    acc = fmaf(-U[n][j], V[j][k], acc) for j = 0..r-1 in binary32, stored in the storage type
+    (bfloat16: round to nearest even)."""
+    W = _check(W, dtype, 2, "W")
+    n_out, n_in = W.shape
+    r = 0 if U is None else U.shape[1]
+    if r:
+        U, V = _check(U, dtype, 2, "U"), _check(V, dtype, 2, "V")
+        if U.shape != (n_out, r) or V.shape != (r, n_in):
+            raise ValueError(f"U {U.shape} / V {V.shape} do not match W {W.shape}")
+    R = np.empty_like(W)
+    rc = _load().splr_ref_residual(_ptr(W), _ptr(U if r else None), _ptr(V if r else None), n_out, n_in, r,
+                                   _DT[dtype], _ptr(R))
+    if rc:
+        raise ValueError(f"splr_ref_residual failed ({rc})")
+    return R
+
+
+def prune24_pack_residual(W: np.ndarray, U: Optional[np.ndarray], V: Optional[np.ndarray],
+                          dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Fused residual + 2:4 projection + pack: prune24_pack(residual(W, U, V))."""
+    W = _check(W, dtype, 2, "W")
+    n_out, n_in = W.shape
+    r = 0 if U is None else U.shape[1]
+    if r:
+        U, V = _check(U, dtype, 2, "U"), _check(V, dtype, 2, "V")
+    TR, TK = tiles(n_out, n_in)
+    values = np.empty((TR, TK, 64, 8), dtype=_NP[dtype])
+    meta = np.empty((TR, TK, 2, 16), dtype=np.uint32)
+    rc = _load().splr_ref_prune24_pack_residual(_ptr(W), _ptr(U if r else None), _ptr(V if r else None), n_out, n_in,
+                                                r, _DT[dtype], _ptr(values), _ptr(meta))
+    if rc:
+        raise ValueError(f"splr_ref_prune24_pack_residual failed ({rc})")
     return values, meta
 
 

@@ -32,6 +32,11 @@
  *                                applied to the residual scaled column by column by D, which gives
  *                                Wanda's score |W_ij| * ||X_j|| (HASSLE-free page, §4.1.2); the kept
  *                                entries are the unscaled residual (scaling, thresholding, unscaling).
+ *   splr_ref_residual, splr_ref_prune24_pack_residual
+ *                             -- the sparse step of the alternating-minimisation / ADMM
+ *                                decompositions acts on the weight minus the current low-rank part,
+ *                                R = W - U V (HASSLE-free page, §4 and §4.1.1, the sparse subproblem
+ *                                (P1)); the fused pack forms R entry by entry and projects it.
  *   splr_ref_linear           -- the compressed forward pass sums the sparse product and the
  *                                low-rank product, computed side by side (LoSparse page, §3 and
  *                                §3.2), here as Y = X S^T + (X V^T) U^T.
@@ -175,6 +180,64 @@ int splr_ref_prune24_pack_scaled(const void *R, const float *d, int64_t n_out, i
                                  void *values, uint32_t *meta) {
   if (!d) return SPLR_REF_EINVAL;
   return pack_by_keys(R, d, n_out, n_in, dtype, values, meta);
+}
+
+/* binary32 (not NaN) -> bfloat16 bits, round to nearest even. */
+static uint16_t to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+static float load_f32(const void *base, int dtype, size_t i) { return (float)load_f64(base, dtype, i); }
+
+/*
+ * Residual with the pinned arithmetic of the fused pack.  For every entry: acc = W[n][k] (binary32),
+ * then for j = 0, 1, ..., r-1 in that order acc = fmaf(-U[n][j], V[j][k], acc) -- one rounding per
+ * step -- and R[n][k] = acc stored in the storage type (bfloat16: round to nearest even).  A NaN
+ * result is stored as the canonical quiet NaN (binary32 0x7FC00000, bfloat16 0x7FC0): processors
+ * differ in the sign and payload of the NaNs they produce.  Reading: the pages define R = W - U V
+ * but fix no arithmetic; this order is the plainest one a bit-exact kernel can follow.
+ */
+int splr_ref_residual(const void *W, const void *U, const void *V, int64_t n_out, int64_t n_in, int64_t r, int dtype,
+                      void *R) {
+  if (!W || !R || (r > 0 && (!U || !V))) return SPLR_REF_EINVAL;
+  if (n_out < 0 || n_in < 0 || r < 0) return SPLR_REF_EINVAL;
+  if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < n_out; ++n) {
+    for (int64_t k = 0; k < n_in; ++k) {
+      float acc = load_f32(W, dtype, (size_t)n * (size_t)n_in + (size_t)k);
+      for (int64_t j = 0; j < r; ++j)
+        acc = fmaf(-load_f32(U, dtype, (size_t)n * (size_t)r + (size_t)j),
+                   load_f32(V, dtype, (size_t)j * (size_t)n_in + (size_t)k), acc);
+      const size_t i = (size_t)n * (size_t)n_in + (size_t)k;
+      if (acc != acc) {
+        if (dtype == SPLR_REF_BF16)
+          ((uint16_t *)R)[i] = 0x7FC0u;
+        else
+          ((uint32_t *)R)[i] = 0x7FC00000u;
+      } else if (dtype == SPLR_REF_BF16) {
+        ((uint16_t *)R)[i] = to_bf16_rne(acc);
+      } else {
+        ((float *)R)[i] = acc;
+      }
+    }
+  }
+  return SPLR_REF_OK;
+}
+
+/* Fused residual + 2:4 projection + pack: the plain pack of splr_ref_residual's R. */
+int splr_ref_prune24_pack_residual(const void *W, const void *U, const void *V, int64_t n_out, int64_t n_in, int64_t r,
+                                   int dtype, void *values, uint32_t *meta) {
+  if (n_out < 0 || n_in < 0) return SPLR_REF_EINVAL;
+  const size_t esz = dtype == SPLR_REF_BF16 ? 2 : 4;
+  void *R = malloc((size_t)n_out * (size_t)n_in * esz + 1);
+  if (!R) return SPLR_REF_ENOMEM;
+  int rc = splr_ref_residual(W, U, V, n_out, n_in, r, dtype, R);
+  if (rc == SPLR_REF_OK) rc = splr_ref_prune24_pack(R, n_out, n_in, dtype, values, meta);
+  free(R);
+  return rc;
 }
 
 static void decode_nibble(const uint32_t *meta, int64_t n, int64_t g, int64_t n_in, int *a, int *b) {

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libsplr.so")
 SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
-EXPORTS = ("splr_prune24_pack", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
+EXPORTS = ("splr_prune24_pack", "splr_prune24_pack_scaled", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
            "splr_linear_stage1", "splr_linear_stage2", "splr_dense_reconstruct", "splr_status_string",
            "splr_version")
 
@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.splr_prune24_pack.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P]
         L.splr_prune24_pack.restype = _I32
+        L.splr_prune24_pack_scaled.argtypes = [_P, _P, _I64, _I64, _I32, _P, _P, _P]
+        L.splr_prune24_pack_scaled.restype = _I32
         L.splr_packed_bytes.argtypes = [_I64, _I64, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
         L.splr_packed_bytes.restype = _I32
         L.splr_linear_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32]
@@ -118,6 +120,25 @@ def prune24_pack(R: torch.Tensor, values: Optional[torch.Tensor] = None, meta: O
         meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
     _check("splr_prune24_pack", lib().splr_prune24_pack(_dev(R, "R"), n_out, n_in, _dtype_code(R),
                                                         _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
+    return values, meta
+
+
+def prune24_pack_scaled(R: torch.Tensor, d: torch.Tensor, values: Optional[torch.Tensor] = None,
+                        meta: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Activation-aware 2:4 projection + pack of R [n_out, n_in] with per-column scales d (float32
+    [n_in]): keeps the two entries of largest |R[n][k]| * |d[k]| per group. Same outputs as
+    prune24_pack."""
+    n_out, n_in = R.shape
+    if d.dtype != torch.float32 or tuple(d.shape) != (n_in,):
+        raise ValueError(f"d must be float32 of shape ({n_in},), got {d.dtype} {tuple(d.shape)}")
+    TR, TK = tiles(n_out, n_in)
+    if values is None:
+        values = torch.empty((TR, TK, 64, 8), dtype=R.dtype, device=R.device)
+    if meta is None:
+        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
+    _check("splr_prune24_pack_scaled",
+           lib().splr_prune24_pack_scaled(_dev(R, "R"), _dev(d, "d"), n_out, n_in, _dtype_code(R),
+                                          _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
     return values, meta
 
 

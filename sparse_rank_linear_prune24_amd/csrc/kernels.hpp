@@ -9,6 +9,9 @@ namespace splr {
 
 hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
                                uint32_t* meta, hipStream_t stream);
+// The same with keys |R[n][k]| * |d[k]| (d: float32 [n_in]).
+hipError_t launch_prune24_pack_scaled(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16,
+                                      void* values, uint32_t* meta, hipStream_t stream);
 
 // First low-rank stage T = X V^T, written to the workspace as float32 partial sums over `slices`
 // slices of K: part[z][M][r], z = 0 .. slices-1 (T = sum of the slices in slice order; the fp32 path

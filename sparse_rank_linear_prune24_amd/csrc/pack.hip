@@ -4,10 +4,15 @@
 // 3BASiL article, "A three-block ADMM replaces alternating minimization"): keep the two entries of
 // largest magnitude as bit copies, ties to the lower column.
 //
+// Activation-aware variant (HASSLE-free page, §4.1.2: with a diagonal Hessian the residual is
+// hard-thresholded after scaling column k by d_k, Wanda's score): the keys are |x| * |d_k|, formed
+// as a binary64 product, which is exact for binary32 (and bfloat16) factors; NaN scores are made
+// one canonical value, so they tie and outrank every number. The kept entries are R's own.
+//
 // HBM streaming kernel. A workgroup owns 16 rows x 512 bytes of R (four bf16 tiles or two fp32
 // tiles of the packed layout). Each lane reads 16-byte chunks with row-contiguous, fully
-// coalesced loads, ranks the four entries of each group with integer compares of the sign-cleared
-// bit patterns (six compares, no floating point: bit-exact and independent of denormal modes),
+// coalesced loads, ranks the four entries of each group with six integer compares of keys (the
+// sign-cleared bit patterns, or the bit patterns of the exact binary64 scores: bit-exact either way),
 // and scatters its kept pair into the tile image in LDS; the lanes that share a metadata word
 // merge their nibbles with cross-lane shuffles. The finished tiles leave LDS as contiguous
 // 16-byte stores.
@@ -22,8 +27,9 @@ constexpr int kPackThreads = 256;
 // Keep positions of four magnitude keys: i outranks j <=> k_i > k_j, or k_i == k_j and i < j. An
 // entry is kept iff it outranks at least two of the other three (ranks of four entries in a
 // strict order are 3, 2, 1, 0). Returns the nibble (a | b << 2) and the kept bit patterns.
-__device__ __forceinline__ uint32_t top2_of_4(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3, uint32_t e0,
-                                              uint32_t e1, uint32_t e2, uint32_t e3, uint32_t& va, uint32_t& vb) {
+template <typename Key>
+__device__ __forceinline__ uint32_t top2_of_4(Key k0, Key k1, Key k2, Key k3, uint32_t e0, uint32_t e1, uint32_t e2,
+                                              uint32_t e3, uint32_t& va, uint32_t& vb) {
   const int w0 = (k0 >= k1) + (k0 >= k2) + (k0 >= k3);
   const int w1 = (k1 > k0) + (k1 >= k2) + (k1 >= k3);
   const int w2 = (k2 > k0) + (k2 > k1) + (k2 >= k3);
@@ -36,8 +42,15 @@ __device__ __forceinline__ uint32_t top2_of_4(uint32_t k0, uint32_t k1, uint32_t
   return (uint32_t)(a | (b << 2));
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_t* __restrict__ R, int n_out, int K,
+// Activation-aware key: |x| * |d| exactly (binary64), NaN canonical; compared as unsigned integers.
+__device__ __forceinline__ uint64_t scaled_key(float x, float d) {
+  const double p = (double)fabsf(x) * (double)fabsf(d);
+  return p != p ? 0x7FF8000000000000ull : (uint64_t)__double_as_longlong(p);
+}
+
+template <bool BF16, bool SCALED>
+__global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_t* __restrict__ R,
+                                                                    const float* __restrict__ dscale, int n_out, int K,
                                                                     int TK, u32x4_t* __restrict__ values,
                                                                     uint32_t* __restrict__ meta) {
   constexpr int kEsz = BF16 ? 2 : 4;            // bytes per entry
@@ -53,6 +66,7 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   const int tid = threadIdx.x;
 
   u32x4_t x[2];
+  f32x4_t ds[2][kPerChunk / 4];  // this chunk's column scales (SCALED only)
   bool valid[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -63,6 +77,11 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
     valid[c] = n < n_out && k < K;
     x[c] = valid[c] ? __builtin_nontemporal_load((const u32x4_t*)(R + ((size_t)n * K + k) * kEsz))
                     : u32x4_t{0, 0, 0, 0};
+    if constexpr (SCALED) {
+#pragma unroll
+      for (int h = 0; h < kPerChunk / 4; ++h)
+        ds[c][h] = k < K ? *(const f32x4_t*)(dscale + k + 4 * h) : f32x4_t{0, 0, 0, 0};
+    }
   }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -74,10 +93,20 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
       const int tkl = ch >> 3, gi0 = 2 * (ch & 7);
       uint32_t v[4];
       const uint32_t d0 = x[c][0], d1 = x[c][1], d2 = x[c][2], d3 = x[c][3];
-      uint32_t n0 = top2_of_4(d0 & 0x7FFFu, (d0 >> 16) & 0x7FFFu, d1 & 0x7FFFu, (d1 >> 16) & 0x7FFFu, d0 & 0xFFFFu,
-                              d0 >> 16, d1 & 0xFFFFu, d1 >> 16, v[0], v[1]);
-      uint32_t n1 = top2_of_4(d2 & 0x7FFFu, (d2 >> 16) & 0x7FFFu, d3 & 0x7FFFu, (d3 >> 16) & 0x7FFFu, d2 & 0xFFFFu,
-                              d2 >> 16, d3 & 0xFFFFu, d3 >> 16, v[2], v[3]);
+      uint32_t n0, n1;
+      if constexpr (SCALED) {
+        auto key = [](uint32_t bits16, float s) { return scaled_key(__uint_as_float(bits16 << 16), s); };
+        const f32x4_t s0 = ds[c][0], s1 = ds[c][1];
+        n0 = top2_of_4(key(d0 & 0xFFFFu, s0[0]), key(d0 >> 16, s0[1]), key(d1 & 0xFFFFu, s0[2]), key(d1 >> 16, s0[3]),
+                       d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16, v[0], v[1]);
+        n1 = top2_of_4(key(d2 & 0xFFFFu, s1[0]), key(d2 >> 16, s1[1]), key(d3 & 0xFFFFu, s1[2]), key(d3 >> 16, s1[3]),
+                       d2 & 0xFFFFu, d2 >> 16, d3 & 0xFFFFu, d3 >> 16, v[2], v[3]);
+      } else {
+        n0 = top2_of_4(d0 & 0x7FFFu, (d0 >> 16) & 0x7FFFu, d1 & 0x7FFFu, (d1 >> 16) & 0x7FFFu, d0 & 0xFFFFu, d0 >> 16,
+                       d1 & 0xFFFFu, d1 >> 16, v[0], v[1]);
+        n1 = top2_of_4(d2 & 0x7FFFu, (d2 >> 16) & 0x7FFFu, d3 & 0x7FFFu, (d3 >> 16) & 0x7FFFu, d2 & 0xFFFFu, d2 >> 16,
+                       d3 & 0xFFFFu, d3 >> 16, v[2], v[3]);
+      }
       if (!valid[c]) n0 = n1 = 0;  // padding: zero entries (already zero) and zero nibbles
       const int slot = r + 16 * (gi0 >> 2);
       // 4 entries (8 bytes) at entry 2*(gi0 % 4) of the slot: half (gi0 % 4) / 2 of its 16 bytes
@@ -92,9 +121,15 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
       // chunk = group gi of tile tkl
       const int tkl = ch >> 4, gi = ch & 15;
       const uint32_t e0 = x[c][0], e1 = x[c][1], e2 = x[c][2], e3 = x[c][3];
-      uint32_t va, vb;
-      uint32_t nb = top2_of_4(e0 & 0x7FFFFFFFu, e1 & 0x7FFFFFFFu, e2 & 0x7FFFFFFFu, e3 & 0x7FFFFFFFu, e0, e1, e2, e3,
-                              va, vb);
+      uint32_t va, vb, nb;
+      if constexpr (SCALED) {
+        const f32x4_t sc = ds[c][0];
+        nb = top2_of_4(scaled_key(__uint_as_float(e0), sc[0]), scaled_key(__uint_as_float(e1), sc[1]),
+                       scaled_key(__uint_as_float(e2), sc[2]), scaled_key(__uint_as_float(e3), sc[3]), e0, e1, e2, e3,
+                       va, vb);
+      } else {
+        nb = top2_of_4(e0 & 0x7FFFFFFFu, e1 & 0x7FFFFFFFu, e2 & 0x7FFFFFFFu, e3 & 0x7FFFFFFFu, e0, e1, e2, e3, va, vb);
+      }
       if (!valid[c]) nb = 0;
       const int slot = r + 16 * (gi >> 2);
       u32x2_t* dst = (u32x2_t*)&sv[tkl * kTileU4 + 2 * slot] + (gi & 3);
@@ -115,20 +150,31 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   if (tid < n_tiles * 8) ((u32x4_t*)meta)[t0 * 8 + tid] = ((const u32x4_t*)sm)[tid];
 }
 
-}  // namespace
-
-hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
-                               uint32_t* meta, hipStream_t stream) {
+template <bool SCALED>
+hipError_t launch_pack(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16, void* values,
+                       uint32_t* meta, hipStream_t stream) {
   const int TK = (int)ceil_div(n_in, 64);
   const int cols = bf16 ? 256 : 128;
   dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(n_in, cols));
   if (bf16)
-    prune24_pack_kernel<true><<<grid, dim3(kPackThreads), 0, stream>>>((const uint8_t*)R, (int)n_out, (int)n_in, TK,
-                                                                      (u32x4_t*)values, meta);
+    prune24_pack_kernel<true, SCALED><<<grid, dim3(kPackThreads), 0, stream>>>(
+        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta);
   else
-    prune24_pack_kernel<false><<<grid, dim3(kPackThreads), 0, stream>>>((const uint8_t*)R, (int)n_out, (int)n_in, TK,
-                                                                       (u32x4_t*)values, meta);
+    prune24_pack_kernel<false, SCALED><<<grid, dim3(kPackThreads), 0, stream>>>(
+        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
+                               uint32_t* meta, hipStream_t stream) {
+  return launch_pack<false>(R, nullptr, n_out, n_in, bf16, values, meta, stream);
+}
+
+hipError_t launch_prune24_pack_scaled(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16,
+                                      void* values, uint32_t* meta, hipStream_t stream) {
+  return launch_pack<true>(R, d, n_out, n_in, bf16, values, meta, stream);
 }
 
 }  // namespace splr

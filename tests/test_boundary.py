@@ -49,6 +49,18 @@ def test_pack_validation():
     assert f(A, 4, 64, 0, A, MIS, None) == ALIGN
 
 
+def test_pack_scaled_validation():
+    f = binding.lib().splr_prune24_pack_scaled
+    assert f(None, A, 4, 64, 1, A, A, None) == NULL
+    assert f(A, None, 4, 64, 1, A, A, None) == NULL
+    assert f(A, A, 4, 64, 1, None, A, None) == NULL
+    assert f(A, A, 0, 64, 1, A, A, None) == SHAPE
+    assert f(A, A, 4, 48, 1, A, A, None) == SHAPE
+    assert f(A, A, 4, 64, 2, A, A, None) == DTYPE
+    assert f(A, MIS, 4, 64, 1, A, A, None) == ALIGN
+    assert f(MIS, A, 4, 64, 1, A, A, None) == ALIGN
+
+
 def test_packed_bytes():
     import ctypes
     f = binding.lib().splr_packed_bytes
