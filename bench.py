@@ -42,6 +42,10 @@ sys.path.insert(0, ROOT)
 METRIC = "2:4+rank-r linear: dense-equiv TFLOP/s & HBM GB/s vs roofline, Llama3-8B shapes"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 (vector / MFMA)
+# fp32 fused multiply-add on the vector ALUs without packed (two-wide) instructions, which this
+# library does not use: 256 CUs x 4 SIMDs x 16 lanes per clock x 2 FLOP x 2.4 GHz = 78.6 TFLOP/s (the
+# vendor's 157.3 TFLOP/s fp32 vector figure counts two-wide packed fused multiply-adds)
+PEAK_FP32_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 MALL_DEFEAT_BYTES = 640 << 20  # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -158,7 +162,7 @@ def main():
         for L in layers:
             ws_n = binding.workspace_bytes(L.M, L.n_out, L.n_in, L.r, tdt)
             s.append(dict(
-                R=to_dev(L.R), X=to_dev(L.X), U=to_dev(L.U), V=to_dev(L.V),
+                R=to_dev(L.R), W=to_dev(L.W), X=to_dev(L.X), U=to_dev(L.U), V=to_dev(L.V),
                 values=torch.empty((*binding.tiles(L.n_out, L.n_in), 64, 8), dtype=tdt, device=dev),
                 meta=torch.empty((*binding.tiles(L.n_out, L.n_in), 2, 16), dtype=torch.int32, device=dev),
                 Y=torch.empty((L.M, L.n_out), dtype=torch.float32, device=dev),
@@ -334,7 +338,7 @@ def time_per_call(issue, n, stream, spin_cycles):
 def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
     """The parts built beyond the hot path, each timed per call on every layer of the workload
     (outside the timed step): the activation-aware pack (keys |R| |d|, d = column norms of the
-    layer's activations)."""
+    layer's activations) and the fused residual + pack (R = W - U V formed in the kernel)."""
     import torch
     n = max(8, args.steps // 2)
     spin = int(4e4 * n * REPEAT)
@@ -354,6 +358,27 @@ def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
                               frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)))
     res["pack_scaled"] = dict(entry="splr_prune24_pack_scaled", bound="hbm",
                               work="bytes: R + d + packed values + metadata", per_layer=per_layer)
+
+    # fused residual + pack: vector-ALU bound (r fused multiply-adds per weight, binary32, not packed)
+    per_layer = []
+    for li, L in enumerate(layers):
+        isz = inputs.itemsize(L.dtype)
+        nbytes = pack_bytes(L.n_in, L.n_out, isz) + (L.n_out + L.n_in) * L.r * isz
+        fmas = L.n_out * L.n_in * L.r
+
+        def issue(i, li=li):
+            s = sets[i % copies][li]
+            binding.prune24_pack_residual(s["W"], s["U"], s["V"], s["values"], s["meta"], stream=stream)
+
+        ms = time_per_call(issue, n, stream, spin)
+        tflops = 2 * fmas / (ms * 1e-3) / 1e12
+        per_layer.append(dict(layer=L.name, us=round(ms * 1e3, 2), fp32_TFLOPs=round(tflops, 1),
+                              frac_alu=round(tflops / PEAK_FP32_VALU_TFLOPS, 4),
+                              GBps=round(nbytes / (ms * 1e-3) / 1e9, 1)))
+    res["pack_residual"] = dict(entry="splr_prune24_pack_residual", bound="alu",
+                                peak_TFLOPs=PEAK_FP32_VALU_TFLOPS,
+                                work="2 n_out n_in r FLOP (the residual's fused multiply-adds); bytes W + U + V + "
+                                     "packed values + metadata", per_layer=per_layer)
     return res
 
 

@@ -85,6 +85,27 @@ splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr
                                 void* values, uint32_t* meta, hipStream_t stream);
 
 /*
+ * splr_prune24_pack_residual -- residual R = W - U V formed in the kernel, then projected and packed
+ * exactly as splr_prune24_pack does (R never goes to memory).
+ *
+ * The sparse step of the alternating-minimisation / ADMM decompositions acts on the weight minus
+ * the current low-rank part (HASSLE-free page, §4 and §4.1.1), and repeats at every iteration.
+ * Pinned arithmetic (bit-exact): per entry acc = W[n][k] as binary32, then for j = 0, 1, ..., r-1
+ * in that order acc = fma(-U[n][j], V[j][k], acc) (one rounding per step), then the storage type
+ * (bfloat16: round to nearest even).  A NaN result is stored as the canonical quiet NaN
+ * (0x7FC00000 / 0x7FC0).  r == 0 packs W itself.
+ *
+ *   W      [n_out][n_in] dtype    U [n_out][r] dtype    V [r][n_in] dtype (U, V NULL iff r == 0)
+ *   values, meta                  output, packed layout above
+ * Vector-ALU bound: r fused multiply-adds per weight.
+ * Errors: NULL pointer -> SPLR_ERR_NULL; n_out < 1, n_in < 32, n_in % 32 != 0, r < 0 or r > 1024 ->
+ *         SPLR_ERR_SHAPE; bad dtype -> SPLR_ERR_DTYPE; misaligned pointer -> SPLR_ERR_ALIGN.
+ */
+splr_status_t splr_prune24_pack_residual(const void* W, const void* U, const void* V, int64_t n_out,
+                                         int64_t n_in, int64_t r, splr_dtype_t dtype, void* values,
+                                         uint32_t* meta, hipStream_t stream);
+
+/*
  * splr_prune24_pack_scaled -- activation-aware (diagonal-Hessian) 2:4 projection, then packing.
  *
  * With a diagonal Hessian the sparse step hard-thresholds the residual after scaling input column

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libsplr.so")
 SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
-EXPORTS = ("splr_prune24_pack", "splr_prune24_pack_scaled", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
+EXPORTS = ("splr_prune24_pack", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
            "splr_linear_stage1", "splr_linear_stage2", "splr_dense_reconstruct", "splr_status_string",
            "splr_version")
 
@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.splr_prune24_pack.restype = _I32
         L.splr_prune24_pack_scaled.argtypes = [_P, _P, _I64, _I64, _I32, _P, _P, _P]
         L.splr_prune24_pack_scaled.restype = _I32
+        L.splr_prune24_pack_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
+        L.splr_prune24_pack_residual.restype = _I32
         L.splr_packed_bytes.argtypes = [_I64, _I64, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
         L.splr_packed_bytes.restype = _I32
         L.splr_linear_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32]
@@ -120,6 +122,23 @@ def prune24_pack(R: torch.Tensor, values: Optional[torch.Tensor] = None, meta: O
         meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
     _check("splr_prune24_pack", lib().splr_prune24_pack(_dev(R, "R"), n_out, n_in, _dtype_code(R),
                                                         _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
+    return values, meta
+
+
+def prune24_pack_residual(W: torch.Tensor, U: Optional[torch.Tensor], V: Optional[torch.Tensor],
+                          values: Optional[torch.Tensor] = None, meta: Optional[torch.Tensor] = None,
+                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """2:4 projection + pack of R = W - U V, formed in the kernel (pinned fused multiply-add order)."""
+    n_out, n_in = W.shape
+    r = 0 if U is None else U.shape[1]
+    TR, TK = tiles(n_out, n_in)
+    if values is None:
+        values = torch.empty((TR, TK, 64, 8), dtype=W.dtype, device=W.device)
+    if meta is None:
+        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=W.device)
+    _check("splr_prune24_pack_residual",
+           lib().splr_prune24_pack_residual(_dev(W, "W"), _dev(U, "U"), _dev(V, "V"), n_out, n_in, r, _dtype_code(W),
+                                            _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
     return values, meta
 
 

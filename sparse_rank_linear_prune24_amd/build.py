@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libsplr.so")
-SOURCES = ["api.hip", "pack.hip", "lowrank.hip", "linear_bf16.hip", "linear_f32.hip", "reconstruct.hip"]
+SOURCES = ["api.hip", "pack.hip", "residual.hip", "lowrank.hip", "linear_bf16.hip", "linear_f32.hip", "reconstruct.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -54,6 +54,22 @@ splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr
   return from_hip(splr::launch_prune24_pack(R, n_out, n_in, dtype == SPLR_BF16, values, meta, stream));
 }
 
+splr_status_t splr_prune24_pack_residual(const void* W, const void* U, const void* V, int64_t n_out, int64_t n_in,
+                                         int64_t r, splr_dtype_t dtype, void* values, uint32_t* meta,
+                                         hipStream_t stream) {
+  if (!W || !values || !meta) return SPLR_ERR_NULL;
+  if (r > 0 && (!U || !V)) return SPLR_ERR_NULL;
+  splr_status_t s = check_in(n_in);
+  if (s == SPLR_OK) s = check_rows(n_out, n_in);
+  if (s == SPLR_OK && (r < 0 || r > kMaxRank)) s = SPLR_ERR_SHAPE;
+  if (s != SPLR_OK) return s;
+  if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
+  if (r > 0 && (!aligned16(U) || !aligned16(V))) return SPLR_ERR_ALIGN;
+  return from_hip(
+      splr::launch_prune24_pack_residual(W, U, V, n_out, n_in, r, dtype == SPLR_BF16, values, meta, stream));
+}
+
 splr_status_t splr_prune24_pack_scaled(const void* R, const float* d, int64_t n_out, int64_t n_in, splr_dtype_t dtype,
                                        void* values, uint32_t* meta, hipStream_t stream) {
   if (!R || !d || !values || !meta) return SPLR_ERR_NULL;

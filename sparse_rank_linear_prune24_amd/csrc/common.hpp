@@ -59,6 +59,24 @@ __device__ __forceinline__ f32x4_t smfmac16x16x64(bf16x8_t a, bf16x16_t b, f32x4
   return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, 0);
 }
 
+// Keep positions of four keys (2:4 projection): i outranks j <=> k_i > k_j, or k_i == k_j and i < j. An
+// entry is kept iff it outranks at least two of the other three (ranks of four entries in a
+// strict order are 3, 2, 1, 0). Returns the nibble (a | b << 2) and the kept bit patterns.
+template <typename Key>
+__device__ __forceinline__ uint32_t top2_of_4(Key k0, Key k1, Key k2, Key k3, uint32_t e0, uint32_t e1, uint32_t e2,
+                                              uint32_t e3, uint32_t& va, uint32_t& vb) {
+  const int w0 = (k0 >= k1) + (k0 >= k2) + (k0 >= k3);
+  const int w1 = (k1 > k0) + (k1 >= k2) + (k1 >= k3);
+  const int w2 = (k2 > k0) + (k2 > k1) + (k2 >= k3);
+  const int w3 = (k3 > k0) + (k3 > k1) + (k3 > k2);
+  const bool keep0 = w0 >= 2, keep1 = w1 >= 2, keep2 = w2 >= 2, keep3 = w3 >= 2;
+  const int a = keep0 ? 0 : (keep1 ? 1 : 2);
+  const int b = keep3 ? 3 : (keep2 ? 2 : 1);
+  va = keep0 ? e0 : (keep1 ? e1 : e2);
+  vb = keep3 ? e3 : (keep2 ? e2 : e1);
+  return (uint32_t)(a | (b << 2));
+}
+
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace splr

@@ -24,24 +24,6 @@ namespace {
 
 constexpr int kPackThreads = 256;
 
-// Keep positions of four magnitude keys: i outranks j <=> k_i > k_j, or k_i == k_j and i < j. An
-// entry is kept iff it outranks at least two of the other three (ranks of four entries in a
-// strict order are 3, 2, 1, 0). Returns the nibble (a | b << 2) and the kept bit patterns.
-template <typename Key>
-__device__ __forceinline__ uint32_t top2_of_4(Key k0, Key k1, Key k2, Key k3, uint32_t e0, uint32_t e1, uint32_t e2,
-                                              uint32_t e3, uint32_t& va, uint32_t& vb) {
-  const int w0 = (k0 >= k1) + (k0 >= k2) + (k0 >= k3);
-  const int w1 = (k1 > k0) + (k1 >= k2) + (k1 >= k3);
-  const int w2 = (k2 > k0) + (k2 > k1) + (k2 >= k3);
-  const int w3 = (k3 > k0) + (k3 > k1) + (k3 > k2);
-  const bool keep0 = w0 >= 2, keep1 = w1 >= 2, keep2 = w2 >= 2, keep3 = w3 >= 2;
-  const int a = keep0 ? 0 : (keep1 ? 1 : 2);
-  const int b = keep3 ? 3 : (keep2 ? 2 : 1);
-  va = keep0 ? e0 : (keep1 ? e1 : e2);
-  vb = keep3 ? e3 : (keep2 ? e2 : e1);
-  return (uint32_t)(a | (b << 2));
-}
-
 // Activation-aware key: |x| * |d| exactly (binary64), NaN canonical; compared as unsigned integers.
 __device__ __forceinline__ uint64_t scaled_key(float x, float d) {
   const double p = (double)fabsf(x) * (double)fabsf(d);

@@ -61,6 +61,22 @@ def test_pack_scaled_validation():
     assert f(MIS, A, 4, 64, 1, A, A, None) == ALIGN
 
 
+def test_pack_residual_validation():
+    f = binding.lib().splr_prune24_pack_residual
+    assert f(None, A, A, 4, 64, 16, 1, A, A, None) == NULL
+    assert f(A, None, A, 4, 64, 16, 1, A, A, None) == NULL
+    assert f(A, A, None, 4, 64, 16, 1, A, A, None) == NULL
+    assert f(A, A, A, 4, 64, 16, 1, None, A, None) == NULL
+    assert f(A, A, A, 4, 64, -1, 1, A, A, None) == SHAPE
+    assert f(A, A, A, 4, 64, 1025, 1, A, A, None) == SHAPE
+    assert f(A, A, A, 4, 48, 16, 1, A, A, None) == SHAPE
+    assert f(A, A, A, 0, 64, 16, 1, A, A, None) == SHAPE
+    assert f(A, A, A, 4, 64, 16, 3, A, A, None) == DTYPE
+    assert f(MIS, A, A, 4, 64, 16, 1, A, A, None) == ALIGN
+    assert f(A, MIS, A, 4, 64, 16, 1, A, A, None) == ALIGN
+    assert f(A, None, None, 4, 64, 0, 1, MIS, A, None) == ALIGN
+
+
 def test_packed_bytes():
     import ctypes
     f = binding.lib().splr_packed_bytes
