@@ -338,7 +338,8 @@ def time_per_call(issue, n, stream, spin_cycles):
 def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
     """The parts built beyond the hot path, each timed per call on every layer of the workload
     (outside the timed step): the activation-aware pack (keys |R| |d|, d = column norms of the
-    layer's activations) and the fused residual + pack (R = W - U V formed in the kernel)."""
+    layer's activations), the fused residual + pack (R = W - U V formed in the kernel) and the layer
+    product with a bfloat16 Y (splr_linear_ex)."""
     import torch
     n = max(8, args.steps // 2)
     spin = int(4e4 * n * REPEAT)
@@ -379,6 +380,24 @@ def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
                                 peak_TFLOPs=PEAK_FP32_VALU_TFLOPS,
                                 work="2 n_out n_in r FLOP (the residual's fused multiply-adds); bytes W + U + V + "
                                      "packed values + metadata", per_layer=per_layer)
+
+    # bfloat16 Y: the same layer product with the output rounded to bfloat16 (half the Y bytes)
+    per_layer = []
+    for li, L in enumerate(layers):
+        if L.dtype != "bf16":
+            continue
+        y16 = torch.empty((L.M, L.n_out), dtype=torch.bfloat16, device=dev)
+
+        def issue(i, li=li, y16=y16):
+            s = sets[i % copies][li]
+            binding.linear_ex(s["X"], s["values"], s["meta"], s["U"], s["V"], y_dtype=torch.bfloat16,
+                              n_out=L.n_out, out=y16, workspace=s["ws"], stream=stream)
+
+        ms = time_per_call(issue, n, stream, spin)
+        per_layer.append(dict(layer=L.name, us=round(ms * 1e3, 2),
+                              dense_equiv_TFLOPs=round(2 * L.M * L.n_out * L.n_in / (ms * 1e-3) / 1e12, 1)))
+    res["linear_bf16_y"] = dict(entry="splr_linear_ex (y_dtype bfloat16)", bound="mfma",
+                                work="dense-equivalent FLOP 2 M n_out n_in", per_layer=per_layer)
     return res
 
 

@@ -169,6 +169,19 @@ splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* va
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * splr_linear_ex -- splr_linear with a choice of output type: y_dtype SPLR_FP32 gives splr_linear's
+ * Y; SPLR_BF16 stores each float32 result rounded to bfloat16 (to nearest even; NaN stays a quiet
+ * NaN), so Y [M][n_out] is 2-byte entries and half the bytes to write.  The rounding is the only
+ * difference: a bfloat16 Y is, bit for bit, the round-to-nearest-even of the float32 Y of the same
+ * call.
+ * Errors: as splr_linear; unknown y_dtype -> SPLR_ERR_DTYPE.
+ */
+splr_status_t splr_linear_ex(const void* X, int64_t M, int64_t n_in, const void* values,
+                             const uint32_t* meta, int64_t n_out, const void* U, const void* V,
+                             int64_t r, splr_dtype_t dtype, splr_dtype_t y_dtype, void* Y,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * splr_linear_stage1 / splr_linear_stage2 -- the two stages of splr_linear, for callers that want
  * to schedule them apart (for example stage 1 on another stream while the residual is packed).
  * splr_linear(...) is exactly stage1 followed by stage2 on one stream with one workspace.

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libsplr.so")
 SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
-EXPORTS = ("splr_prune24_pack", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
+EXPORTS = ("splr_prune24_pack", "splr_linear_ex", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
            "splr_linear_stage1", "splr_linear_stage2", "splr_dense_reconstruct", "splr_status_string",
            "splr_version")
 
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.splr_linear_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32]
         L.splr_linear_workspace_bytes.restype = _SZ
         L.splr_linear.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P, _SZ, _P]
+        L.splr_linear_ex.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P]
+        L.splr_linear_ex.restype = _I32
         L.splr_linear.restype = _I32
         L.splr_linear_stage1.argtypes = [_P, _I64, _I64, _P, _I64, _I32, _P, _SZ, _P]
         L.splr_linear_stage1.restype = _I32
@@ -195,6 +197,30 @@ def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optiona
     _check("splr_linear", lib().splr_linear(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
                                             _dev(U, "U"), _dev(V, "V"), r, _dtype_code(X), _dev(out, "out"),
                                             _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return out
+
+
+def linear_ex(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
+              V: Optional[torch.Tensor], y_dtype: torch.dtype = torch.float32, n_out: Optional[int] = None,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """splr_linear with the output type chosen: float32, or bfloat16 (each result rounded to nearest
+    even)."""
+    if y_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"y_dtype must be float32 or bfloat16, got {y_dtype}")
+    M = X.shape[0]
+    if n_out is None:
+        n_out = U.shape[0] if U is not None else values.shape[0] * 16
+    if out is None:
+        out = torch.empty((M, n_out), dtype=y_dtype, device=X.device)
+    if out.dtype != y_dtype:
+        raise ValueError(f"out is {out.dtype}, expected {y_dtype}")
+    M, n_in, n_out, r, _, workspace, ws_bytes = _linear_args(X, values, U, n_out, out, workspace)
+    ycode = SPLR_BF16 if y_dtype == torch.bfloat16 else SPLR_FP32
+    _check("splr_linear_ex", lib().splr_linear_ex(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"),
+                                                  n_out, _dev(U, "U"), _dev(V, "V"), r, _dtype_code(X), ycode,
+                                                  _dev(out, "out"), _dev(workspace, "workspace"), ws_bytes,
+                                                  _stream(stream)))
     return out
 
 

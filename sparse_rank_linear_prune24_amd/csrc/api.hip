@@ -105,7 +105,7 @@ namespace {
 
 // Argument checks shared by splr_linear and its two stages. V is checked only when need_v.
 splr_status_t check_linear(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                           int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, const float* Y,
+                           int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, const void* Y,
                            const void* workspace, size_t ws_bytes, bool need_sparse, bool need_v) {
   if (!X) return SPLR_ERR_NULL;
   if (need_sparse && (!values || !meta || !Y || (r > 0 && !U))) return SPLR_ERR_NULL;
@@ -128,13 +128,13 @@ splr_status_t check_linear(const void* X, int64_t M, int64_t n_in, const void* v
 }
 
 splr_status_t run_stage2(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                         int64_t n_out, const void* U, int64_t r, splr_dtype_t dtype, float* Y, void* workspace,
-                         hipStream_t stream) {
+                         int64_t n_out, const void* U, int64_t r, splr_dtype_t dtype, void* Y, bool y_bf16,
+                         void* workspace, hipStream_t stream) {
   if (dtype == SPLR_BF16)
     return from_hip(splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, (const float*)workspace,
-                                             splr::lowrank_slices(M, n_in, r, true), Y, stream));
+                                             splr::lowrank_slices(M, n_in, r, true), Y, y_bf16, stream));
   return from_hip(splr::launch_linear_f32((const float*)X, M, n_in, (const float*)values, meta, n_out,
-                                          (const float*)U, r, (const float*)workspace, Y, stream));
+                                          (const float*)U, r, (const float*)workspace, Y, y_bf16, stream));
 }
 
 }  // namespace
@@ -147,7 +147,19 @@ splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* va
   if (s != SPLR_OK) return s;
   if (splr::launch_lowrank(X, V, M, n_in, r, dtype == SPLR_BF16, workspace, stream) != hipSuccess)
     return SPLR_ERR_HIP;
-  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, workspace, stream);
+  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, false, workspace, stream);
+}
+
+splr_status_t splr_linear_ex(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                             int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype,
+                             splr_dtype_t y_dtype, void* Y, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const splr_status_t s =
+      check_linear(X, M, n_in, values, meta, n_out, U, V, r, dtype, Y, workspace, ws_bytes, true, true);
+  if (s != SPLR_OK) return s;
+  if (!dtype_ok(y_dtype)) return SPLR_ERR_DTYPE;
+  if (splr::launch_lowrank(X, V, M, n_in, r, dtype == SPLR_BF16, workspace, stream) != hipSuccess)
+    return SPLR_ERR_HIP;
+  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, y_dtype == SPLR_BF16, workspace, stream);
 }
 
 splr_status_t splr_linear_stage1(const void* X, int64_t M, int64_t n_in, const void* V, int64_t r,
@@ -164,7 +176,7 @@ splr_status_t splr_linear_stage2(const void* X, int64_t M, int64_t n_in, const v
   const splr_status_t s =
       check_linear(X, M, n_in, values, meta, n_out, U, nullptr, r, dtype, Y, workspace, ws_bytes, true, false);
   if (s != SPLR_OK) return s;
-  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, const_cast<void*>(workspace), stream);
+  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, false, const_cast<void*>(workspace), stream);
 }
 
 splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, const void* U, const void* V,

@@ -25,14 +25,14 @@ size_t lowrank_workspace_bytes(int64_t M, int64_t n_in, int64_t r, bool bf16);
 hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in, int64_t r, bool bf16,
                           void* workspace, hipStream_t stream);
 
-// Y = X S^T + T U^T, T given as `slices` float32 partial sums [slices][M][r] (r == 0: no low-rank
-// term). The partials are added in slice order and T enters the MFMAs as a bfloat16 pair
-// hi = RNE(T), lo = RNE(T - hi).
+// Y (float32, or bfloat16 when y_bf16, rounded to nearest even) = X S^T + T U^T, T given as
+// `slices` float32 partial sums [slices][M][r] (r == 0: no low-rank term). The partials are added
+// in slice order and T enters the MFMAs as a bfloat16 pair hi = RNE(T), lo = RNE(T - hi).
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, float* Y,
-                              hipStream_t stream);
+                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
+                              bool y_bf16, hipStream_t stream);
 hipError_t launch_linear_f32(const float* X, int64_t M, int64_t n_in, const float* values, const uint32_t* meta,
-                             int64_t n_out, const float* U, int64_t r, const float* T, float* Y,
+                             int64_t n_out, const float* U, int64_t r, const float* T, void* Y, bool y_bf16,
                              hipStream_t stream);
 
 hipError_t launch_dense_reconstruct(const void* values, const uint32_t* meta, const void* U, const void* V,

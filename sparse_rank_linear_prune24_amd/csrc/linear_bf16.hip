@@ -232,11 +232,36 @@ __device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint
   }
 }
 
-// Store acc[i][j] (rows n = nrow0 + 16 i + 4*(lane/16) + 0..3, token m = mrow0 + 16 j + lane%16).
+// Store acc[i][j] (rows n = nrow0 + 16 i + 4*(lane/16) + 0..3, token m = mrow0 + 16 j + lane%16), as
+// float32, or (y_bf16) rounded to bfloat16 (to nearest even).
 template <int NI, int NJ>
-__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], float* __restrict__ Y, int M, int n_out,
-                                           int nrow0, int mrow0, int lane) {
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* __restrict__ Yv, int y_bf16, int M,
+                                           int n_out, int nrow0, int mrow0, int lane) {
   const bool vec_ok = (n_out & 3) == 0;
+  if (y_bf16) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int m = mrow0 + 16 * j + (lane & 15);
+      if (m >= M) continue;
+      uint16_t* yrow = (uint16_t*)Yv + (size_t)m * n_out;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = nrow0 + 16 * i + 4 * (lane >> 4);
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(acc[i][j][e]);
+        if (vec_ok && n + 3 < n_out) {
+          *(u32x2_t*)(yrow + n) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < n_out) yrow[n + e] = (uint16_t)h[e];
+        }
+      }
+    }
+    return;
+  }
+  float* __restrict__ Y = (float*)Yv;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int m = mrow0 + 16 * j + (lane & 15);
@@ -261,7 +286,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], float* 
 template <int NI, int NJ, int P, int PX>
 __global__ __launch_bounds__(256) void linear_prefill_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, float* __restrict__ Y, int M, int K,
+    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16, int M, int K,
     int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
   constexpr int WAVES = 4;
   constexpr int BN = 16 * NI * WAVES;
@@ -471,7 +496,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
       lds_barrier();
     }
   }
-  store_tile<NI, NJ>(acc, Y, M, n_out, nrow0, m0, lane);
+  store_tile<NI, NJ>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
 }
 
 // ----------------------------------------------------------------------------------- decode
@@ -479,7 +504,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
 template <int MB, int P, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, float* __restrict__ Y, int M, int K,
+    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16, int M, int K,
     int n_out, int r) {
   constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
   __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
@@ -593,30 +618,31 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
       lds_barrier();
     }
   }
-  if (wave == 0) store_tile<1, MB>(acc, Y, M, n_out, tr * 16, m0, lane);
+  if (wave == 0) store_tile<1, MB>(acc, Y, y_bf16, M, n_out, tr * 16, m0, lane);
 }
 
 template <int MB>
 hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                         int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, float* Y,
-                         hipStream_t stream) {
+                         int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
+                         int y_bf16, hipStream_t stream) {
   constexpr int P = MB == 1 ? 8 : 4, W = 4;
   dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(M, 16 * MB));
   linear_decode_kernel<MB, P, W><<<grid, dim3(64 * W), 0, stream>>>(
-      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, (int)M, (int)n_in,
-      (int)n_out, (int)r);
+      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, y_bf16, (int)M,
+      (int)n_in, (int)n_out, (int)r);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, float* Y,
-                              hipStream_t stream) {
-  if (M <= 16) return launch_decode<1>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, stream);
-  if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, stream);
+                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
+                              bool y_bf16, hipStream_t stream) {
+  const int yb = y_bf16 ? 1 : 0;
+  if (M <= 16) return launch_decode<1>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, yb, stream);
+  if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, yb, stream);
   if (M <= kDecodeMaxTokens)
-    return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, stream);
+    return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, yb, stream);
 
   constexpr int NI = 4, NJ = 8, P = 4, PX = 2;
   constexpr int BN = 16 * NI * 4, BM = 16 * NJ;
@@ -625,8 +651,8 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   const int per_xcd = (int)ceil_div(n_tiles, 8);
   const int group_m = 4;
   linear_prefill_kernel<NI, NJ, P, PX><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
-      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, (int)M, (int)n_in,
-      (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
+      (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   return hipGetLastError();
 }
 

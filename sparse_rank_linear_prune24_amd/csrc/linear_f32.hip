@@ -12,7 +12,8 @@ namespace {
 __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict__ X, const float* __restrict__ values,
                                                         const uint32_t* __restrict__ meta,
                                                         const float* __restrict__ U, const float* __restrict__ T,
-                                                        float* __restrict__ Y, int M, int K, int n_out, int r) {
+                                                        void* __restrict__ Y, int y_bf16, int M, int K, int n_out,
+                                                        int r) {
   const int n = blockIdx.x * 64 + (threadIdx.x & 63);
   const int m = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (n >= n_out || m >= M) return;
@@ -30,16 +31,19 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict
   }
   float lr = 0.0f;
   for (int j = 0; j < r; ++j) lr = fmaf(T[(size_t)m * r + j], U[(size_t)n * r + j], lr);
-  Y[(size_t)m * n_out + n] = acc + lr;
+  const float y = acc + lr;
+  if (y_bf16) ((uint16_t*)Y)[(size_t)m * n_out + n] = (uint16_t)float_to_bf16_bits(y);
+  else ((float*)Y)[(size_t)m * n_out + n] = y;
 }
 
 }  // namespace
 
 hipError_t launch_linear_f32(const float* X, int64_t M, int64_t n_in, const float* values, const uint32_t* meta,
-                             int64_t n_out, const float* U, int64_t r, const float* T, float* Y,
+                             int64_t n_out, const float* U, int64_t r, const float* T, void* Y, bool y_bf16,
                              hipStream_t stream) {
   dim3 grid((unsigned)ceil_div(n_out, 64), (unsigned)ceil_div(M, 4));
-  linear_f32_kernel<<<grid, dim3(256), 0, stream>>>(X, values, meta, U, T, Y, (int)M, (int)n_in, (int)n_out, (int)r);
+  linear_f32_kernel<<<grid, dim3(256), 0, stream>>>(X, values, meta, U, T, Y, y_bf16 ? 1 : 0, (int)M, (int)n_in,
+                                                    (int)n_out, (int)r);
   return hipGetLastError();
 }
 

@@ -77,6 +77,18 @@ def test_pack_residual_validation():
     assert f(A, None, None, 4, 64, 0, 1, MIS, A, None) == ALIGN
 
 
+def test_linear_ex_validation():
+    import ctypes
+    f = binding.lib().splr_linear_ex
+    wsb = binding.lib().splr_linear_workspace_bytes(16, 32, 64, 16, 1)
+    args = lambda yd, Y=A: (A, 16, 64, A, A, 32, A, A, 16, 1, yd, Y, A, wsb, None)
+    assert f(*args(2)) == DTYPE
+    assert f(*args(-1)) == DTYPE
+    assert f(*args(1, None)) == NULL
+    assert f(*args(1, MIS)) == ALIGN
+    assert f(A, 16, 64, A, A, 32, A, A, 16, 1, 1, A, A, ctypes.c_size_t(0), None) == 6  # workspace too small
+
+
 def test_packed_bytes():
     import ctypes
     f = binding.lib().splr_packed_bytes
