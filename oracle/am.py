@@ -1,0 +1,70 @@
+"""Data-free alternating minimisation of W ~ S + U V -- TEST INFRASTRUCTURE ONLY (oracle).
+
+The decomposition alternates an exact sparse update and an exact low-rank update (HASSLE-free page,
+§4): with an identity Hessian the sparse subproblem is solved by hard thresholding onto the 2:4 set
+(§4.1.1) and the low-rank subproblem by the rank-r truncated SVD C_r (§4.2.1; C_r is the best
+rank-r approximation by the Eckart-Young theorem, §3). The pages run 80 steps at rank 64 (§5.2,
+§5.3). Readings where the pages are silent:
+  * start: L_0 = C_r(W), the leading singular components of the weight (LoSparse page, §3.2);
+  * storage: L is kept as thin factors in the storage type, balanced as U = U_r sqrt(Sigma_r),
+    V = sqrt(Sigma_r) V_r^T, each rounded to nearest; every sparse step projects the residual
+    W - U V of the stored factors with the fused pack's pinned arithmetic
+    (oracle.prune24_pack_residual);
+  * objective: ||W - S - U V||_F of the stored S, U, V, in float64.
+The truncated SVD is numpy's (LAPACK, float64).
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+from . import prune24_pack_residual, unpack
+from sparse_rank_linear_prune24_amd import inputs
+
+
+def truncated_svd(Z: np.ndarray, r: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """C_r(Z) as (U_r, s_r, V_r^T): the r leading singular triplets of the float64 matrix Z."""
+    u, s, vt = np.linalg.svd(Z, full_matrices=False)
+    return u[:, :r], s[:r], vt[:r]
+
+
+def balanced_factors(Z: np.ndarray, r: int, dtype: str) -> Tuple[Optional[np.ndarray], Optional[np.ndarray]]:
+    """Stored thin factors of C_r(Z): U = U_r sqrt(s), V = sqrt(s) V_r^T, rounded to the storage type."""
+    if r == 0:
+        return None, None
+    u, s, vt = truncated_svd(Z, r)
+    root = np.sqrt(s)
+    return inputs.from_f64(u * root, dtype), inputs.from_f64(root[:, None] * vt, dtype)
+
+
+def dense_sparse(values, meta, n_out: int, n_in: int, dtype: str) -> np.ndarray:
+    """The packed S as a dense float64 matrix (stored entries at their columns, zeros elsewhere)."""
+    kept, nib = unpack(values, meta, n_out, n_in, dtype)
+    k = inputs.to_f64(kept, dtype)
+    S = np.zeros((n_out, n_in))
+    groups = n_in // 4
+    a = (nib & 3).astype(np.int64)
+    b = (nib >> 2).astype(np.int64)
+    rows = np.arange(n_out)[:, None]
+    base = 4 * np.arange(groups)[None, :]
+    S[rows, base + a] = k[:, 0::2]
+    S[rows, base + b] = k[:, 1::2]
+    return S
+
+
+def alternating_minimization(W: np.ndarray, r: int, iters: int, dtype: str):
+    """Returns (values, meta, U, V, objectives) after `iters` steps; objectives[t] is
+    ||W - S_t - U_t V_t||_F after step t (each step: S from the current factors, then new factors)."""
+    n_out, n_in = W.shape
+    w = inputs.to_f64(W, dtype)
+    U, V = balanced_factors(w, r, dtype)
+    objectives: List[float] = []
+    values = meta = None
+    for _ in range(iters):
+        values, meta = prune24_pack_residual(W, U, V, dtype)
+        S = dense_sparse(values, meta, n_out, n_in, dtype)
+        U, V = balanced_factors(w - S, r, dtype)
+        L = 0.0 if U is None else inputs.to_f64(U, dtype) @ inputs.to_f64(V, dtype)
+        objectives.append(float(np.linalg.norm(w - S - L)))
+    return values, meta, U, V, objectives
