@@ -338,8 +338,8 @@ def time_per_call(issue, n, stream, spin_cycles):
 def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
     """The parts built beyond the hot path, each timed per call on every layer of the workload
     (outside the timed step): the activation-aware pack (keys |R| |d|, d = column norms of the
-    layer's activations), the fused residual + pack (R = W - U V formed in the kernel) and the layer
-    product with a bfloat16 Y (splr_linear_ex)."""
+    layer's activations), the fused residual + pack (R = W - U V formed in the kernel), the layer
+    product with a bfloat16 Y (splr_linear_ex) and steps of the data-free alternating minimisation."""
     import torch
     n = max(8, args.steps // 2)
     spin = int(4e4 * n * REPEAT)
@@ -398,6 +398,24 @@ def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
                               dense_equiv_TFLOPs=round(2 * L.M * L.n_out * L.n_in / (ms * 1e-3) / 1e12, 1)))
     res["linear_bf16_y"] = dict(entry="splr_linear_ex (y_dtype bfloat16)", bound="mfma",
                                 work="dense-equivalent FLOP 2 M n_out n_in", per_layer=per_layer)
+
+    # data-free alternating minimisation on the first layer: per-step time (untracked) and the
+    # objective / layer error over a few steps (tracked)
+    from sparse_rank_linear_prune24_amd import am
+    L = layers[0]
+    s0 = sets[0][0]
+    if L.r > 0:
+        steps = 6
+        am.alternating_minimization(s0["W"], L.r, 1, track=False)  # warm-up (library initialisation)
+        t = am.alternating_minimization(s0["W"], L.r, steps, track=False)
+        tracked = am.alternating_minimization(s0["W"], L.r, steps, X=s0["X"])
+        wnorm = float(torch.linalg.norm(s0["W"].float()))
+        res["am_loop"] = dict(layer=L.name, steps=steps, ms_per_step=round(t["seconds"] / steps * 1e3, 3),
+                              est_80_steps_s=round(t["seconds"] / steps * 80, 3),
+                              rel_objective=[round(o / wnorm, 5) for o in tracked["objective"]],
+                              layer_rel_error=[round(e, 5) for e in tracked["layer_rel_error"]],
+                              step="splr_prune24_pack_residual + dense reconstruct of S + rank-r subspace "
+                                   "iteration (torch matmul / QR / small SVD)")
     return res
 
 

@@ -1,0 +1,88 @@
+"""Data-free alternating minimisation W ~ S + U V on the GPU (HASSLE-free page, §4).
+
+Each step solves the two subproblems in turn: the sparse update is the 2:4 projection of the
+residual W - U V (hard thresholding, §4.1.1), run by the fused residual + pack kernel
+(splr_prune24_pack_residual); the low-rank update is the rank-r truncated SVD C_r(W - S) (§4.2.1).
+The pages run 80 steps at rank 64 (§5.2, §5.3).
+
+Readings where the pages are silent (the same as the CPU oracle's): the loop starts from
+L_0 = C_r(W), the weight's leading singular components (LoSparse page, §3.2); L is kept as balanced
+thin factors U = U_r sqrt(Sigma_r), V = sqrt(Sigma_r) V_r^T in the storage type (rounded to
+nearest); the objective is ||W - S - U V||_F of the stored S, U, V.
+
+C_r is computed by subspace iteration (float32 matrix products and thin QR factorisations from
+torch, then an SVD of the small projected matrix), warm-started from the previous step's right
+singular basis: after a few steps of the loop it agrees with the exact truncated SVD to the
+working precision on matrices whose r-th and (r+1)-th singular values are separated. The matrix
+products, QR and SVD are library calls (torch); the projection and the reconstruction of S are
+this library's kernels.
+"""
+from __future__ import annotations
+
+import time
+from typing import Dict, List, Optional
+
+import torch
+
+from . import binding
+
+
+def _low_rank(Z: torch.Tensor, r: int, basis: Optional[torch.Tensor], power_iters: int, oversample: int,
+              gen: torch.Generator):
+    """Approximate C_r(Z) for float32 Z [n_out, n_in]: (U, V) balanced float32 factors and the right
+    basis [n_in, k] to warm-start the next call."""
+    n_out, n_in = Z.shape
+    k = min(r + oversample, n_out, n_in)
+    B = basis if basis is not None else torch.randn(n_in, k, generator=gen, device=Z.device, dtype=torch.float32)
+    B, _ = torch.linalg.qr(B)
+    for _ in range(power_iters):
+        Q, _ = torch.linalg.qr(Z @ B)
+        B, _ = torch.linalg.qr(Z.T @ Q)
+    Q, _ = torch.linalg.qr(Z @ B)
+    small = Q.T @ Z                                   # [k, n_in]
+    ub, s, vh = torch.linalg.svd(small, full_matrices=False)
+    root = torch.sqrt(s[:r])
+    U = (Q @ ub[:, :r]) * root[None, :]
+    V = root[:, None] * vh[:r]
+    return U, V, vh.T.contiguous()
+
+
+def alternating_minimization(W: torch.Tensor, r: int, iters: int, *, power_iters: int = 2, start_iters: int = 6,
+                             oversample: int = 16, seed: int = 0, X: Optional[torch.Tensor] = None,
+                             track: bool = True) -> Dict:
+    """Run `iters` steps on W [n_out, n_in] (bfloat16 or float32, on the GPU).
+
+    Returns dict(values, meta, U, V, objective, layer_rel_error, seconds): the packed S and factors
+    after the last step; objective[t] = ||W - S_t - U_t V_t||_F after step t (when `track`); with
+    activations X [M, n_in], layer_rel_error[t] = ||X W^T - splr_linear(X)||_F / ||X W^T||_F."""
+    n_out, n_in = W.shape
+    dtype = W.dtype
+    gen = torch.Generator(device=W.device)
+    gen.manual_seed(seed)
+    W32 = W.float()
+    basis = None
+    U = V = None
+    t0 = time.perf_counter()
+    if r > 0:
+        U32, V32, basis = _low_rank(W32, r, None, start_iters, oversample, gen)
+        U, V = U32.to(dtype).contiguous(), V32.to(dtype).contiguous()
+    objective: List[float] = []
+    layer_err: List[float] = []
+    ref = X.float() @ W32.T if X is not None else None
+    values = meta = None
+    for _ in range(iters):
+        values, meta = binding.prune24_pack_residual(W, U, V, values, meta)
+        S = binding.dense_reconstruct(values, meta, None, None, n_out=n_out, n_in=n_in)
+        Z = W32 - S
+        if r > 0:
+            U32, V32, basis = _low_rank(Z, r, basis, power_iters, oversample, gen)
+            U, V = U32.to(dtype).contiguous(), V32.to(dtype).contiguous()
+        if track:
+            L = U.float() @ V.float() if r > 0 else 0.0
+            objective.append(float(torch.linalg.norm(Z - L)))
+        if ref is not None:
+            Y = binding.linear(X, values, meta, U, V, n_out=n_out)
+            layer_err.append(float(torch.linalg.norm(Y - ref) / torch.linalg.norm(ref)))
+    torch.cuda.synchronize()
+    return dict(values=values, meta=meta, U=U, V=V, objective=objective, layer_rel_error=layer_err,
+                seconds=time.perf_counter() - t0)
