@@ -62,6 +62,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="C2", help="C1..C5 (default: C2, the prefill q_proj layer)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    p.add_argument("--no-next", action="store_true", help="skip the measurements of the parts beyond the hot path")
     p.add_argument("--cpu-rows", type=int, default=0, help="token rows of the oracle sample (0 = auto)")
     p.add_argument("--graph", action="store_true", help="replay the steps from HIP graphs (for comparison)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -309,7 +310,8 @@ def main():
         input_generation_s=round(gen_s, 1),
     )
 
-    out["next"] = measure_next(binding, inputs, layers, sets, copies, stream, dev, args)
+    if not args.no_next:
+        out["next"] = measure_next(binding, inputs, layers, sets, copies, stream, dev, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, layers, dtype, flop_step, wbytes_step, decode, args.cpu_rows)

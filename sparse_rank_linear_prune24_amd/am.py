@@ -10,11 +10,12 @@ L_0 = C_r(W), the weight's leading singular components (LoSparse page, §3.2); L
 thin factors U = U_r sqrt(Sigma_r), V = sqrt(Sigma_r) V_r^T in the storage type (rounded to
 nearest); the objective is ||W - S - U V||_F of the stored S, U, V.
 
-C_r is computed by subspace iteration (float32 matrix products and thin QR factorisations from
-torch, then an SVD of the small projected matrix), warm-started from the previous step's right
-singular basis: after a few steps of the loop it agrees with the exact truncated SVD to the
-working precision on matrices whose r-th and (r+1)-th singular values are separated. The matrix
-products, QR and SVD are library calls (torch); the projection and the reconstruction of S are
+C_r is computed by subspace iteration (float32 matrix products from torch; Cholesky QR with the
+k x k factors in float64 on the host; the small projected matrix decomposed through a k x k
+symmetric eigenproblem, float64, host), warm-started from the previous step's right singular basis:
+after a few steps of the loop it agrees with the exact truncated SVD to the working precision on
+matrices whose r-th and (r+1)-th singular values are separated. The matrix products and the small
+factorisations are library calls (torch, numpy); the projection and the reconstruction of S are
 this library's kernels.
 """
 from __future__ import annotations
@@ -22,29 +23,47 @@ from __future__ import annotations
 import time
 from typing import Dict, List, Optional
 
+import numpy as np
 import torch
 
 from . import binding
 
 
+def _orthonormalize(Y: torch.Tensor) -> torch.Tensor:
+    """Orthonormal basis of the columns of Y [n, k] (k small) by Cholesky QR, twice: the Gram
+    matrix is formed in float64 on the GPU, its k x k Cholesky factor inverted in float64 on the
+    host, and Y multiplied by the inverse."""
+    for _ in range(2):
+        G = (Y.double().T @ Y.double()).cpu().numpy()
+        Rinv = np.linalg.inv(np.linalg.cholesky(G).T)
+        Y = Y @ torch.from_numpy(Rinv).to(device=Y.device, dtype=torch.float32)
+    return Y
+
+
 def _low_rank(Z: torch.Tensor, r: int, basis: Optional[torch.Tensor], power_iters: int, oversample: int,
               gen: torch.Generator):
     """Approximate C_r(Z) for float32 Z [n_out, n_in]: (U, V) balanced float32 factors and the right
-    basis [n_in, k] to warm-start the next call."""
+    basis [n_in, k] to warm-start the next call. Subspace iteration; the projected k x n_in matrix
+    B = Q^T Z is decomposed through the eigenvectors of B B^T (float64, on the host)."""
     n_out, n_in = Z.shape
     k = min(r + oversample, n_out, n_in)
     B = basis if basis is not None else torch.randn(n_in, k, generator=gen, device=Z.device, dtype=torch.float32)
-    B, _ = torch.linalg.qr(B)
+    B = _orthonormalize(B)
     for _ in range(power_iters):
-        Q, _ = torch.linalg.qr(Z @ B)
-        B, _ = torch.linalg.qr(Z.T @ Q)
-    Q, _ = torch.linalg.qr(Z @ B)
+        Q = _orthonormalize(Z @ B)
+        B = _orthonormalize(Z.T @ Q)
+    Q = _orthonormalize(Z @ B)
     small = Q.T @ Z                                   # [k, n_in]
-    ub, s, vh = torch.linalg.svd(small, full_matrices=False)
-    root = torch.sqrt(s[:r])
-    U = (Q @ ub[:, :r]) * root[None, :]
-    V = root[:, None] * vh[:r]
-    return U, V, vh.T.contiguous()
+    lam, vec = np.linalg.eigh((small.double() @ small.double().T).cpu().numpy())
+    order = np.argsort(lam)[::-1][:k]
+    lam, vec = np.maximum(lam[order], 0.0), vec[:, order]
+    s = np.sqrt(lam)
+    Wv = torch.from_numpy(vec).to(device=Z.device, dtype=torch.float64)
+    right = (small.double().T @ Wv) / torch.from_numpy(np.where(s > 0, s, 1.0)).to(Z.device)[None, :]  # [n_in, k]
+    root = torch.from_numpy(np.sqrt(s[:r])).to(device=Z.device, dtype=torch.float64)
+    U = ((Q.double() @ Wv[:, :r]) * root[None, :]).float()
+    V = (root[:, None] * right[:, :r].T).float()
+    return U, V, right.float().contiguous()
 
 
 def alternating_minimization(W: torch.Tensor, r: int, iters: int, *, power_iters: int = 2, start_iters: int = 6,
