@@ -488,11 +488,20 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
 
   // larger r: the rank-r term, 64 ranks at a time, after the loop; the workgroup builds T's pair
   // block by block in the now free X slots (the last step's barrier has retired every read of them)
+  // and stages the block's U rows in the U slot (unused before the loop when r > 64), the loads of
+  // both in flight together
   if (!t_pre) {
     for (int j0 = 0; j0 < r; j0 += 64) {
-      build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs0, xs1, threadIdx.x);
+      TPairBuilder<BM, 64 * WAVES> tbp;
+      UStager<BN, 64 * WAVES> usp;
+      tbp.init(Tpart, slices, M, r, m0, j0, threadIdx.x);
+      tbp.issue(0);
+      usp.issue(U, n_out, r, n0, j0, threadIdx.x);
+      __builtin_amdgcn_sched_barrier(0);
+      tbp.finish(xs0, xs1);
+      usp.finish(ulds);
       lds_barrier();
-      lowrank_block<NI, NJ>(acc, U, xs0, xs1, n_out, r, j0, nrow0, lane);
+      lowrank_block<NI, NJ>(acc, U, xs0, xs1, n_out, r, j0, nrow0, lane, ulds, wave * 16 * NI);
       lds_barrier();
     }
   }

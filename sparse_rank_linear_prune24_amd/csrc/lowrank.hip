@@ -157,6 +157,148 @@ __global__ __launch_bounds__(64 * WAVES) void lowrank_bf16_kernel(const uint16_t
   }
 }
 
+// LDS writes of this wave complete, then workgroup barrier (one asm statement with a memory
+// clobber, so that register prefetches stay in flight across it; the builtin wait after it tells
+// the compiler's wait-count tracking that no LDS access is outstanding).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+}
+
+// Tile kernel for many tokens: a workgroup owns BM = 16*TMW*WM tokens x BR = 16*TRW*WR ranks over
+// one K slice (grid: rank blocks, token blocks, K slices), so that X is read from memory once when
+// BR covers r. Per 64-column K step the four waves stage the step's X rows into one slot of a
+// two-slot LDS ring (row-contiguous 16-byte loads, one barrier per step) and wave w computes its
+// 16*TMW tokens x 16*TRW ranks: X fragments come from the slot, V fragments (small, L2-resident)
+// straight from global memory into registers. Loads of both run P steps ahead in registers. V is
+// the A operand (two fixed 2:4 halves, as above), X the B operand. Rows past M and ranks past r
+// repeat the last valid row and are never stored.
+template <int TMW, int TRW, int WM, int WR, int P>
+__global__ __launch_bounds__(256) void lowrank_tile_kernel(const uint16_t* __restrict__ X,
+                                                          const uint16_t* __restrict__ V, int M, int K, int r,
+                                                          int steps_per_slice, float* __restrict__ part) {
+  static_assert(WM * WR == 4, "four waves");
+  constexpr int BM = 16 * TMW * WM, BR = 16 * TRW * WR;
+  constexpr int kChunks = BM * 8;                  // 16-byte chunks of X per step
+  constexpr int kLoads = (kChunks + 255) / 256;    // per thread per step
+  __shared__ u32x4_t slot[2][BM * kPitchU4];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane & 15, quad = lane >> 4;
+  const int wm = wave % WM, wr = wave / WM;
+  const int j0 = blockIdx.x * BR, m0 = blockIdx.y * BM;
+  const int TK = (K + 63) / 64;
+  const int kb = blockIdx.z * steps_per_slice;
+  const int n_steps = min(TK, kb + steps_per_slice) - kb;  // >= 1 by the choice of slices
+  const bool half_tail = (K & 63) != 0;                      // the last step holds 32 valid columns
+
+  // X: thread chunk c -> token row c / 8, 16-byte chunk c % 8 of the step
+  const uint16_t* xsrc[kLoads];
+  int xdst[kLoads], xch[kLoads];
+#pragma unroll
+  for (int t = 0; t < kLoads; ++t) {
+    const int c = min((int)threadIdx.x + 256 * t, kChunks - 1);
+    xch[t] = c & 7;
+    xdst[t] = threadIdx.x + 256 * t < kChunks ? (c >> 3) * kPitchU4 + xch[t] : -1;
+    xsrc[t] = X + (size_t)min(m0 + (c >> 3), M - 1) * K + 8 * xch[t];
+  }
+  // V: A fragment of rank block a -> row j0 + 16 (wr TRW + a) + lane%16, dense columns 16 q .. 16 q + 15
+  const uint16_t* vsrc[TRW];
+#pragma unroll
+  for (int a = 0; a < TRW; ++a) vsrc[a] = V + (size_t)min(j0 + 16 * (wr * TRW + a) + sub, r - 1) * K + 16 * quad;
+
+  auto loadx = [&](int kc, u32x4_t (&v)[kLoads]) {
+#pragma unroll
+    for (int t = 0; t < kLoads; ++t) {
+      int col = kc * 64;
+      if (col + 8 * xch[t] >= K) col -= 32;  // 32-column tail step: re-read valid columns (zeroed below)
+      v[t] = *(const u32x4_t*)(xsrc[t] + col);
+    }
+  };
+  auto loadv = [&](int kc, u32x4_t (&v)[TRW][2]) {
+    int col = kc * 64;
+    if (col + 16 * quad >= K) col -= 32;  // as above
+#pragma unroll
+    for (int a = 0; a < TRW; ++a) {
+      v[a][0] = *(const u32x4_t*)(vsrc[a] + col);
+      v[a][1] = *(const u32x4_t*)(vsrc[a] + col + 8);
+    }
+  };
+
+  f32x4_t acc[TRW][TMW];
+#pragma unroll
+  for (int a = 0; a < TRW; ++a)
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) acc[a][i] = f32x4_t{0, 0, 0, 0};
+
+  // A ring of P steps of loads stays in flight: register slot u holds step s0 + u and is refilled
+  // with step s0 + u + P as soon as it has been consumed. Branch-free (conditional loads would make
+  // the compiler wait for every outstanding load): steps are padded to a multiple of P, loads past
+  // the slice's last step re-read that step, and padded steps contribute through a zeroed A operand.
+  const int n_pad = (n_steps + P - 1) / P * P;
+  u32x4_t xring[P][kLoads], vring[P][TRW][2];
+  static_for<P>([&](auto uu) {  // issued in slot order (fenced), as the loop refills them
+    constexpr int u = decltype(uu)::value;
+    loadx(kb + min(u, n_steps - 1), xring[u]);
+    loadv(kb + min(u, n_steps - 1), vring[u]);
+    asm volatile("" ::: "memory");
+  });
+  auto step = [&](int s, auto uu, auto refill) {
+    constexpr int u = decltype(uu)::value;
+    constexpr bool kRefill = decltype(refill)::value;
+    const int next = kb + min(s + P, n_steps - 1);
+    u32x4_t* sl = slot[s & 1];
+#pragma unroll
+    for (int t = 0; t < kLoads; ++t)
+      if (xdst[t] >= 0) sl[xdst[t]] = xring[u][t];
+    if constexpr (kRefill) loadx(next, xring[u]);
+    asm volatile("" ::: "memory");  // compiler-only fence: the refill stays in this step
+    lds_barrier();
+    const int kc = kb + s;
+    // A operand zero past the slice's last step, and for the re-read upper half of a 32-column tail
+    // step (dense columns 32..63)
+    const bool live = s < n_steps && !(half_tail && kc == TK - 1 && quad >= 2);
+    const uint32_t keep = live ? ~0u : 0u;
+    bf16x8_t a01[TRW], a23[TRW];
+#pragma unroll
+    for (int a = 0; a < TRW; ++a) {
+      const u32x4_t d0 = vring[u][a][0] & keep, d1 = vring[u][a][1] & keep;
+      a01[a] = as_bf16x8(u32x4_t{d0[0], d0[2], d1[0], d1[2]});
+      a23[a] = as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]});
+    }
+    if constexpr (kRefill) loadv(next, vring[u]);
+    asm volatile("" ::: "memory");
+    bf16x16_t bx[TMW];
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) {
+      const int xrow = (16 * (wm * TMW + i) + sub) * kPitchU4;
+      bx[i] = cat16(as_bf16x8(sl[xrow + quad]), as_bf16x8(sl[xrow + 4 + quad]));
+    }
+#pragma unroll
+    for (int a = 0; a < TRW; ++a)
+#pragma unroll
+      for (int i = 0; i < TMW; ++i) {
+        acc[a][i] = smfmac16x16x64(a01[a], bx[i], acc[a][i], 0x4444);
+        acc[a][i] = smfmac16x16x64(a23[a], bx[i], acc[a][i], 0xEEEE);
+      }
+  };
+  // every round but the last refills its slots; the last round loads nothing more
+  for (int s0 = 0; s0 + P < n_pad; s0 += P)
+    static_for<P>([&](auto uu) { step(s0 + decltype(uu)::value, uu, std::true_type{}); });
+  static_for<P>([&](auto uu) { step(n_pad - P + decltype(uu)::value, uu, std::false_type{}); });
+
+  // D rows = ranks j0 + 16 (wr TRW + a) + 4*(lane/16) + 0..3, column = token m0 + 16 (wm TMW + i) + lane%16
+  float* pz = part + (size_t)blockIdx.z * M * r;
+#pragma unroll
+  for (int a = 0; a < TRW; ++a) {
+    const int j = j0 + 16 * (wr * TRW + a) + 4 * quad;
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) {
+      const int m = m0 + 16 * (wm * TMW + i) + sub;
+      if (m < M && j < r) *(f32x4_t*)(pz + (size_t)m * r + j) = acc[a][i];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restrict__ X, const float* __restrict__ V,
                                                          int M, int K, int r, float* __restrict__ T) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -176,22 +318,34 @@ __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restric
 
 namespace {
 
-// bf16 first-stage shape. Measured on MI355X, the stage runs fastest as about 256 small workgroups:
-// 16 ranks per workgroup for decode-sized inputs (M <= 16) and 32 ranks otherwise (when 32 divides
-// r), with K split into slices only as far as needed to reach ~256 workgroups (at most
-// kMaxLowrankSlices, at most one per K step). Wider rank blocks stage each X row fewer times but
-// leave too few workgroups, or need more slices for the second stage to add.
+// bf16 first-stage shape, chosen by measurement on MI355X. For r <= 64, lowrank_bf16_kernel: ~256
+// small workgroups, 16 ranks each for decode-sized inputs (M <= 16) and 32 otherwise (when 32
+// divides r), K split into slices only as far as needed to reach ~256 workgroups (at most
+// kMaxLowrankSlices); each X row is staged at most twice, by concurrently running workgroups.
+// For r > 64 the rank blocks of that kernel would stream X from memory r/32 times: the tile kernel
+// takes 128 ranks per workgroup (X read once for r <= 128) and 16, 32 or 64 tokens by M.
 struct LowrankShape {
-  int tf, rf, slices, steps_per_slice;
+  bool tile;
+  int tf, rf;   // lowrank_bf16_kernel: 16*tf tokens x 16*rf ranks
+  int bm;       // tile kernel: bm tokens x 128 ranks
+  int slices, steps_per_slice;
 };
 
 LowrankShape lowrank_shape(int64_t M, int64_t n_in, int64_t r) {
   constexpr int64_t kWant = 256;
-  LowrankShape sh;
-  sh.tf = M <= 16 ? 1 : 2;
-  sh.rf = (M > 16 && r % 32 == 0) ? 2 : 1;
-  const int64_t TK = (n_in + 63) / 64, token_blocks = ceil_div(M, 16 * sh.tf);
-  const int64_t base = token_blocks * (r / (16 * sh.rf));
+  LowrankShape sh{};
+  const int64_t TK = (n_in + 63) / 64;
+  int64_t base;
+  if (M <= 16 || r <= 64) {
+    sh.tile = false;
+    sh.tf = M <= 16 ? 1 : 2;
+    sh.rf = (M > 16 && r % 32 == 0) ? 2 : 1;
+    base = ceil_div(M, 16 * sh.tf) * (r / (16 * sh.rf));
+  } else {
+    sh.tile = true;
+    sh.bm = M >= 4096 ? 64 : (M >= 1024 ? 32 : 16);
+    base = ceil_div(M, sh.bm) * ceil_div(r, 128);
+  }
   const int64_t slices =
       std::min<int64_t>(std::min<int64_t>(kMaxLowrankSlices, TK), std::max<int64_t>(1, ceil_div(kWant, base)));
   sh.steps_per_slice = (int)ceil_div(TK, slices);
@@ -211,6 +365,14 @@ void launch_part(const LowrankShape& sh, const void* X, const void* V, int64_t M
                                                                     (int)n_in, (int)r, sh.steps_per_slice, part);
 }
 
+template <int TMW>
+void launch_tile(const LowrankShape& sh, const void* X, const void* V, int64_t M, int64_t n_in, int64_t r,
+                 float* part, hipStream_t stream) {
+  dim3 grid((unsigned)cdiv(r, 128), (unsigned)cdiv(M, 16 * TMW), (unsigned)sh.slices);
+  lowrank_tile_kernel<TMW, 2, 1, 4, 4><<<grid, dim3(256), 0, stream>>>(
+      (const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in, (int)r, sh.steps_per_slice, part);
+}
+
 }  // namespace
 
 int lowrank_slices(int64_t M, int64_t n_in, int64_t r, bool bf16) {
@@ -228,9 +390,17 @@ hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in,
   float* part = (float*)workspace;
   if (bf16) {
     const LowrankShape sh = lowrank_shape(M, n_in, r);
-    if (sh.tf == 1) launch_part<1, 1>(sh, X, V, M, n_in, r, part, stream);
-    else if (sh.rf == 2) launch_part<2, 2>(sh, X, V, M, n_in, r, part, stream);
-    else launch_part<2, 1>(sh, X, V, M, n_in, r, part, stream);
+    if (!sh.tile) {
+      if (sh.tf == 1) launch_part<1, 1>(sh, X, V, M, n_in, r, part, stream);
+      else if (sh.rf == 2) launch_part<2, 2>(sh, X, V, M, n_in, r, part, stream);
+      else launch_part<2, 1>(sh, X, V, M, n_in, r, part, stream);
+    } else if (sh.bm == 16) {
+      launch_tile<1>(sh, X, V, M, n_in, r, part, stream);
+    } else if (sh.bm == 32) {
+      launch_tile<2>(sh, X, V, M, n_in, r, part, stream);
+    } else {
+      launch_tile<4>(sh, X, V, M, n_in, r, part, stream);
+    }
   } else {
     const int64_t waves = M * r;
     lowrank_f32_kernel<<<dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, stream>>>(
