@@ -76,11 +76,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 // load covers 4 rows x 256 contiguous bytes. Ranks >= r give zeros; rows past M repeat row M-1
 // (never stored). issue() starts the loads of a round of slices, finish() adds them (and any
 // further rounds) and writes the LDS planes, so the first round can overlap other work.
-template <int ROWS, int NT>
+template <int ROWS, int NT, int G = 0>
 struct TPairBuilder {
   static constexpr int kQuads = ROWS * 16;  // 4 ranks each
   static constexpr int kIters = (kQuads + NT - 1) / NT;
-  static constexpr int kGroup = kIters >= 8 ? 1 : 16 / kIters;  // slices per round (<= 16 loads in flight)
+  // slices per round: G, else as many as keep <= 16 loads in flight per thread
+  static constexpr int kGroup = G > 0 ? G : (kIters >= 8 ? 1 : 16 / kIters);
   const float* src[kIters];
   bool ok[kIters];
   f32x4_t sum[kIters];
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   // rank-r operands staged before the main loop: loads issued here, finished after the loop's
   // prologue has issued its own loads (published by the prologue's barriers)
   const bool t_pre = r <= 64 * kPreRankBlocks, u_pre = r <= 64;
-  TPairBuilder<BM, 64 * WAVES> tb[kPreRankBlocks];
+  TPairBuilder<BM, 64 * WAVES, 2> tb[kPreRankBlocks];
   UStager<BN, 64 * WAVES> us;
   if (t_pre) {
 #pragma unroll
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   // both in flight together
   if (!t_pre) {
     for (int j0 = 0; j0 < r; j0 += 64) {
-      TPairBuilder<BM, 64 * WAVES> tbp;
+      TPairBuilder<BM, 64 * WAVES, 2> tbp;
       UStager<BN, 64 * WAVES> usp;
       tbp.init(Tpart, slices, M, r, m0, j0, threadIdx.x);
       tbp.issue(0);
