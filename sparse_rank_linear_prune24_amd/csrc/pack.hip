@@ -23,6 +23,7 @@ namespace splr {
 namespace {
 
 constexpr int kPackThreads = 256;
+constexpr int kPackChunksPerThread = 4;  // 16-byte chunks of R per thread
 
 // Activation-aware key: |x| * |d| exactly (binary64), NaN canonical; compared as unsigned integers.
 __device__ __forceinline__ uint64_t scaled_key(float x, float d) {
@@ -30,16 +31,18 @@ __device__ __forceinline__ uint64_t scaled_key(float x, float d) {
   return p != p ? 0x7FF8000000000000ull : (uint64_t)__double_as_longlong(p);
 }
 
-template <bool BF16, bool SCALED>
+template <bool BF16, bool SCALED, int CPT>
 __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_t* __restrict__ R,
                                                                     const float* __restrict__ dscale, int n_out, int K,
                                                                     int TK, u32x4_t* __restrict__ values,
                                                                     uint32_t* __restrict__ meta) {
   constexpr int kEsz = BF16 ? 2 : 4;            // bytes per entry
   constexpr int kPerChunk = 16 / kEsz;          // entries per 16-byte chunk (8 bf16 = 2 groups, 4 fp32 = 1)
-  constexpr int kCols = 32 * kPerChunk;         // columns per workgroup (32 chunks a row)
-  constexpr int kTiles = kCols / 64;            // packed tiles per workgroup (4 bf16, 2 fp32)
+  constexpr int kRowChunks = 16 * CPT;          // 16-byte chunks per row: CPT per thread over 16 rows
+  constexpr int kCols = kRowChunks * kPerChunk; // columns per workgroup
+  constexpr int kTiles = kCols / 64;            // packed tiles per workgroup
   constexpr int kTileU4 = 512 * kEsz / 16;      // 16-byte units of values per tile (64 / 128)
+  static_assert((kRowChunks & (kRowChunks - 1)) == 0 && kTiles >= 1, "power-of-two row chunks, whole tiles");
   __shared__ u32x4_t sv[kTiles * kTileU4];
   __shared__ uint32_t sm[kTiles * 32];
 
@@ -47,13 +50,13 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   const int tk0 = blockIdx.y * kTiles;          // first tile column of this workgroup
   const int tid = threadIdx.x;
 
-  u32x4_t x[2];
-  f32x4_t ds[2][kPerChunk / 4];  // this chunk's column scales (SCALED only)
-  bool valid[2];
+  u32x4_t x[CPT];
+  f32x4_t ds[CPT][kPerChunk / 4];  // this chunk's column scales (SCALED only)
+  bool valid[CPT];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CPT; ++c) {
     const int q = tid + c * kPackThreads;
-    const int r = q >> 5, ch = q & 31;
+    const int r = q / kRowChunks, ch = q % kRowChunks;
     const int n = tr * 16 + r;
     const int k = blockIdx.y * kCols + ch * kPerChunk;
     valid[c] = n < n_out && k < K;
@@ -66,9 +69,9 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
     }
   }
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CPT; ++c) {
     const int q = tid + c * kPackThreads;
-    const int r = q >> 5, ch = q & 31;
+    const int r = q / kRowChunks, ch = q % kRowChunks;
     uint32_t word;  // this chunk's nibbles, merged below into metadata words
     if constexpr (BF16) {
       // chunk = groups gi0, gi0+1 of tile tkl (gi0 even)
@@ -128,21 +131,24 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   // tiles (tr, tk0 .. tk0 + kTiles - 1) are contiguous in the packed arrays
   const size_t t0 = (size_t)tr * TK + tk0;
   const int n_tiles = min(kTiles, TK - tk0);
-  if (tid < n_tiles * kTileU4) values[t0 * kTileU4 + tid] = sv[tid];
+#pragma unroll
+  for (int u = tid; u < kTiles * kTileU4; u += kPackThreads)
+    if (u < n_tiles * kTileU4) values[t0 * kTileU4 + u] = sv[u];
   if (tid < n_tiles * 8) ((u32x4_t*)meta)[t0 * 8 + tid] = ((const u32x4_t*)sm)[tid];
 }
 
 template <bool SCALED>
 hipError_t launch_pack(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16, void* values,
                        uint32_t* meta, hipStream_t stream) {
+  constexpr int CPT = kPackChunksPerThread;
   const int TK = (int)ceil_div(n_in, 64);
-  const int cols = bf16 ? 256 : 128;
+  const int cols = 16 * CPT * (bf16 ? 8 : 4);
   dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(n_in, cols));
   if (bf16)
-    prune24_pack_kernel<true, SCALED><<<grid, dim3(kPackThreads), 0, stream>>>(
+    prune24_pack_kernel<true, SCALED, CPT><<<grid, dim3(kPackThreads), 0, stream>>>(
         (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta);
   else
-    prune24_pack_kernel<false, SCALED><<<grid, dim3(kPackThreads), 0, stream>>>(
+    prune24_pack_kernel<false, SCALED, CPT><<<grid, dim3(kPackThreads), 0, stream>>>(
         (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta);
   return hipGetLastError();
 }
