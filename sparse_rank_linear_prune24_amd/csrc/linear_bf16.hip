@@ -282,9 +282,63 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* _
   }
 }
 
+// Store acc[i][j] like store_tile, but through a per-wave LDS buffer `buf` (64 tokens x 64 rows of
+// float32, row pitch kYPitch floats) so that the global stores are row-contiguous: the wave writes
+// its accumulators for 64 tokens into the buffer (16-byte writes, a 16-lane phase on distinct
+// banks), reads them back as 256-byte segments of token rows and stores four token rows per
+// instruction, which runs faster than storing the fragment order (16 token rows x 64 bytes per
+// instruction). All addressing is derived here from the lane and the tile origin.
+constexpr int kYPitch = 68;
+constexpr int kRowsEpilogueMaxTiles = 256;  // one workgroup per CU of MI355X
+template <int NI, int NJ>
+__device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[NI][NJ], float* buf, void* __restrict__ Yv,
+                                                int y_bf16, int M, int n_out, int nrow0, int mrow0) {
+  static_assert(NI == 4 && NJ % 4 == 0, "a wave owns 64 rows; tokens go through the buffer 64 at a time");
+  const int lane = threadIdx.x & 63;
+  const int wr = (lane & 15) * kYPitch + 4 * (lane >> 4);   // write: token lane%16, rows 4*(lane/16)
+  const int rd = (lane >> 4) * kYPitch + 4 * (lane & 15);   // read: token lane/16, rows 4*(lane%16)
+  const int n = nrow0 + 4 * (lane & 15);
+  const bool vec_ok = (n_out & 3) == 0 && n + 3 < n_out;
+#pragma unroll
+  for (int h = 0; h < NJ / 4; ++h) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) *(f32x4_t*)(buf + wr + 16 * jj * kYPitch + 16 * i) = acc[i][4 * h + jj];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const f32x4_t v = *(const f32x4_t*)(buf + rd + 4 * t * kYPitch);
+      const int m = mrow0 + 64 * h + 4 * t + (lane >> 4);
+      if (m >= M) continue;
+      if (y_bf16) {
+        uint16_t* yrow = (uint16_t*)Yv + (size_t)m * n_out;
+        uint32_t hb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hb[e] = float_to_bf16_bits(v[e]);
+        if (vec_ok) {
+          *(u32x2_t*)(yrow + n) = u32x2_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < n_out) yrow[n + e] = (uint16_t)hb[e];
+        }
+      } else {
+        float* yrow = (float*)Yv + (size_t)m * n_out;
+        if (vec_ok) {
+          *(f32x4_t*)(yrow + n) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < n_out) yrow[n + e] = v[e];
+        }
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------------- prefill
 
-template <int NI, int NJ, int P, int PX>
+template <int NI, int NJ, int P, int PX, bool ROWS_EPI>
 __global__ __launch_bounds__(256) void linear_prefill_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
     const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16, int M, int K,
@@ -506,7 +560,16 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
       lds_barrier();
     }
   }
-  store_tile<NI, NJ>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
+  if constexpr (ROWS_EPI) {
+    // Y leaves through LDS (every slot is free now: the last barrier above retired all reads of
+    // them); waves 0, 1 use the T pair slot, waves 2, 3 the U slot
+    static_assert(2 * 64 * kYPitch * 4 <= (int)sizeof(tpair) && 2 * 64 * kYPitch * 4 <= (int)sizeof(ulds),
+                  "epilogue buffers fit");
+    float* ybuf = (wave < 2 ? (float*)&tpair[0][0] : (float*)&ulds[0]) + (wave & 1) * 64 * kYPitch;
+    store_tile_rows<NI, NJ>(acc, ybuf, Y, y_bf16, M, n_out, nrow0, m0);
+  } else {
+    store_tile<NI, NJ>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
+  }
 }
 
 // ----------------------------------------------------------------------------------- decode
@@ -660,9 +723,18 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   const int n_tiles = tiles_n * tiles_m;
   const int per_xcd = (int)ceil_div(n_tiles, 8);
   const int group_m = 4;
-  linear_prefill_kernel<NI, NJ, P, PX><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
-      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
-      (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+  // When every tile runs at once (one workgroup per CU), the Y stores of all tiles come at the end
+  // together and are exposed: the row-contiguous epilogue stores them faster. With several tiles per
+  // CU the stores overlap the next tile's loop, and with r > 64 the extra registers of that
+  // epilogue cost spills in the rank-r blocks after the loop: there the direct epilogue is faster.
+  if (n_tiles <= kRowsEpilogueMaxTiles && r <= 64)
+    linear_prefill_kernel<NI, NJ, P, PX, true><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
+        (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
+        (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+  else
+    linear_prefill_kernel<NI, NJ, P, PX, false><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
+        (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
+        (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   return hipGetLastError();
 }
 
