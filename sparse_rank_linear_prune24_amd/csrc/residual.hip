@@ -9,13 +9,16 @@
 // (bfloat16: to nearest even); a NaN result is stored as the canonical quiet NaN.
 //
 // Vector-ALU bound (r fused multiply-adds per weight; matrix cores cannot keep the sequential
-// rounding order). A workgroup of 4 waves takes a run of 16-row tile rows; each wave owns 256
-// columns (lane l: columns 4l .. 4l+3, one group of four), keeps V's 64 x 4 block of its columns in
-// registers as float32 (for r <= 64 once per workgroup) and reads U (staged per tile row and rank
-// block in LDS as float32, shared by the 4 waves) with broadcast LDS reads. Rows run one at a time;
-// for r > 64 a row's running sums wait in LDS between rank blocks. Each rounded row is selected
-// and written into a per-wave LDS image of the 4 packed tiles, which leaves with contiguous 16-byte
-// stores.
+// rounding order). Columns per lane: a wave owns kResColsPerLane 64-column packed tiles of one
+// tile row (lane l: column l of each), a workgroup of 4 waves the neighbouring tiles. Each lane
+// keeps its columns' 16 running sums and, per block of kRJ ranks, its columns of V in registers;
+// U for the tile row and the rank block is staged in LDS as float32 and read with broadcast reads
+// (one read feeds 4 ranks of every column of the lane). Registers stay low enough for several
+// waves per SIMD, which hide each other's LDS and memory latency.
+// The rounded rows of a tile pass through LDS so that each lane selects whole groups (four rows'
+// worth of groups per lane instead of every lane of a group repeating the selection); the kept
+// pairs and nibbles form a per-wave LDS image of the packed tile, which leaves with contiguous
+// 16-byte stores.
 #include <algorithm>
 
 #include "common.hpp"
@@ -25,30 +28,13 @@ namespace splr {
 namespace {
 
 constexpr int kResWaves = 4;
-constexpr int kRJ = 64;  // ranks whose V block a lane holds in registers at a time
+constexpr int kRJ = 32;   // ranks per block (a lane's column of V for the block sits in registers)
+constexpr int kResColsPerLane = 1;  // columns (tiles) per lane (wave)
 
 template <bool BF16>
 __device__ __forceinline__ float load_elem(const void* base, size_t i) {
   if constexpr (BF16) return __uint_as_float((uint32_t)((const uint16_t*)base)[i] << 16);
   else return ((const float*)base)[i];
-}
-
-// four consecutive elements starting at i (8- or 16-byte aligned)
-template <bool BF16>
-__device__ __forceinline__ void load4(const void* base, size_t i, float (&x)[4]) {
-  if constexpr (BF16) {
-    const u32x2_t w = *(const u32x2_t*)((const uint16_t*)base + i);
-    x[0] = __uint_as_float(w[0] << 16);
-    x[1] = __uint_as_float(w[0] & 0xFFFF0000u);
-    x[2] = __uint_as_float(w[1] << 16);
-    x[3] = __uint_as_float(w[1] & 0xFFFF0000u);
-  } else {
-    const f32x4_t w = *(const f32x4_t*)((const float*)base + i);
-    x[0] = w[0];
-    x[1] = w[1];
-    x[2] = w[2];
-    x[3] = w[3];
-  }
 }
 
 // residual entry -> storage bits: NaN canonical, bfloat16 rounded to nearest even
@@ -60,256 +46,146 @@ __device__ __forceinline__ uint32_t storage_bits(float acc) {
   else return nan ? 0x7FC00000u : u;
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
-    const void* __restrict__ W, const void* __restrict__ U, const void* __restrict__ V, int n_out, int K, int r,
-    int TK, int TR, int tile_rows_per_wg, u32x4_t* __restrict__ values, uint32_t* __restrict__ meta) {
-  constexpr int kTileU32 = BF16 ? 256 : 512;  // one packed tile's values in 32-bit words
-  __shared__ f32x4_t us[16 * kRJ / 4];        // U rows of the tile row, one rank block, float32
-  __shared__ uint32_t img[kResWaves][4 * kTileU32];
-  __shared__ uint32_t mimg[kResWaves][4 * 32];
-  __shared__ f32x4_t accl[kResWaves][16][64];  // running sums between rank blocks (r > kRJ)
-
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col_block = (blockIdx.x * kResWaves + wave) * 256;  // this wave's first column
-  const int c0 = col_block + 4 * lane;
-  const bool col_ok = c0 < K;
-  const int cc = col_ok ? c0 : 0;  // clamped column for loads
-  const int tl = lane >> 4, gi = lane & 15;
-  const int tr_begin = blockIdx.y * tile_rows_per_wg, tr_end = min(TR, tr_begin + tile_rows_per_wg);
-  const bool single = r <= kRJ;
-
-  float v[kRJ][4];
-  auto load_v = [&](int jb) {
+// acc[s][i] = fma(-U[row i][j], V[j][column s], acc[s][i]) for j = 0 .. NJ-1 in order, U from the
+// staged block `us` (16 rows x kRJ ranks, float32), V from registers
+template <int NJ, int CPL>
+__device__ __forceinline__ void fma_block(float (&acc)[CPL][16], const float (&v)[CPL][kRJ], const f32x4_t* us) {
 #pragma unroll
-    for (int j = 0; j < kRJ; ++j) load4<BF16>(V, (size_t)min(jb + j, max(r - 1, 0)) * K + cc, v[j]);
-  };
-  // the fused multiply-adds of ranks jb .. jb + nj - 1 for row i of the staged block, in rank order
-  auto fma_block = [&](float (&a)[4], int i, int nj) {
-    if (nj == kRJ) {
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int j4 = 0; j4 < kRJ / 4; ++j4) {
-        const f32x4_t u = us[i * (kRJ / 4) + j4];
+    for (int j4 = 0; j4 < NJ / 4; ++j4) {
+      const f32x4_t u = us[i * (kRJ / 4) + j4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) a[c] = __builtin_fmaf(-u[t], v[4 * j4 + t][c], a[c]);
-      }
-    } else {  // partial block: exactly nj steps (a padding step is not neutral)
-#pragma unroll
-      for (int j4 = 0; j4 < kRJ / 4; ++j4) {
-        const f32x4_t u = us[i * (kRJ / 4) + j4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (4 * j4 + t < nj) {  // wave-uniform
-#pragma unroll
-            for (int c = 0; c < 4; ++c) a[c] = __builtin_fmaf(-u[t], v[4 * j4 + t][c], a[c]);
-          }
-      }
+        for (int s = 0; s < CPL; ++s) acc[s][i] = __builtin_fmaf(-u[q], v[s][4 * j4 + q], acc[s][i]);
     }
-  };
-  // round row i, select the top two of each group, write it into this wave's LDS image of 4 tiles
-  auto select_row = [&](const float (&a)[4], int i, bool row_ok) {
-    const bool ok = col_ok && row_ok;
-    uint32_t e[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) e[c] = ok ? storage_bits<BF16>(a[c]) : 0u;
-    const uint32_t m = BF16 ? 0x7FFFu : 0x7FFFFFFFu;
-    uint32_t va, vb;
-    uint32_t nib = top2_of_4(e[0] & m, e[1] & m, e[2] & m, e[3] & m, e[0], e[1], e[2], e[3], va, vb);
-    if (!ok) nib = 0;
-    const int slot = i + 16 * (gi >> 2);
-    if constexpr (BF16) {
-      img[wave][tl * kTileU32 + slot * 4 + (gi & 3)] = va | (vb << 16);
-    } else {
-      *(u32x2_t*)&img[wave][tl * kTileU32 + slot * 8 + 2 * (gi & 3)] = u32x2_t{va, vb};
-    }
-    // nibble gi % 8 of word gi / 8 of row i: the eight lanes gi % 8 = 0..7 share it
-    uint32_t word = nib;
-    word |= (uint32_t)__shfl_down((int)word, 1) << 4;
-    word |= (uint32_t)__shfl_down((int)word, 2) << 8;
-    word |= (uint32_t)__shfl_down((int)word, 4) << 16;
-    if ((gi & 7) == 0) mimg[wave][tl * 32 + (gi >> 3) * 16 + i] = word;
-  };
+}
 
-  if (r > 0 && single) load_v(0);
-  for (int tr = tr_begin; tr < tr_end; ++tr) {
-    if (r == 0) {
-#pragma unroll 1
+// the same for ranks J0 .. J0 + nb - 1 (nb < 16)
+template <int J0, int CPL>
+__device__ __forceinline__ void fma_tail(float (&acc)[CPL][16], const float (&v)[CPL][kRJ], const f32x4_t* us,
+                                         int nb) {
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    if (jj < nb) {  // uniform
+#pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float a[4];
-        load4<BF16>(W, (size_t)min(tr * 16 + i, n_out - 1) * K + cc, a);
-        select_row(a, i, tr * 16 + i < n_out);
-      }
-    }
-    for (int jb = 0; jb < r; jb += kRJ) {
-      const int nj = min(kRJ, r - jb);
-      const bool last = jb + nj >= r;
-      __syncthreads();  // every wave is done reading the previous block of U
-      for (int q = threadIdx.x; q < 16 * kRJ; q += 64 * kResWaves) {
-        const int i = q / kRJ, j = q % kRJ;
-        ((float*)us)[q] = j < nj ? load_elem<BF16>(U, (size_t)min(tr * 16 + i, n_out - 1) * r + jb + j) : 0.0f;
-      }
-      __syncthreads();
-      if (!single) load_v(jb);
-#pragma unroll 1
-      for (int i = 0; i < 16; ++i) {
-        float a[4];
-        if (jb == 0) {
-          load4<BF16>(W, (size_t)min(tr * 16 + i, n_out - 1) * K + cc, a);
-        } else {
-          const f32x4_t p = accl[wave][i][lane];
-          a[0] = p[0], a[1] = p[1], a[2] = p[2], a[3] = p[3];
-        }
-        fma_block(a, i, nj);
-        if (last) select_row(a, i, tr * 16 + i < n_out);
-        else accl[wave][i][lane] = f32x4_t{a[0], a[1], a[2], a[3]};
-      }
-    }
-
-    // tiles (tr, col_block / 64 + t) are contiguous in the packed arrays; this wave's LDS writes
-    // are complete before its own reads below (LDS operations of one wave execute in order)
-    const int tk0 = col_block / 64;
-    constexpr int kTileU4 = kTileU32 / 4;
+        const float u = ((const float*)us)[i * kRJ + J0 + jj];
 #pragma unroll
-    for (int q = lane; q < 4 * kTileU4; q += 64) {
-      const int t = q / kTileU4;
-      if (tk0 + t < TK) values[((size_t)tr * TK + tk0 + t) * kTileU4 + q % kTileU4] = ((const u32x4_t*)img[wave])[q];
-    }
-    if (lane < 32) {
-      const int t = lane / 8;
-      if (tk0 + t < TK) ((u32x4_t*)meta)[((size_t)tr * TK + tk0 + t) * 8 + lane % 8] = ((const u32x4_t*)mimg[wave])[lane];
+        for (int s = 0; s < CPL; ++s) acc[s][i] = __builtin_fmaf(-u, v[s][J0 + jj], acc[s][i]);
+      }
     }
   }
 }
 
-// r <= 64 (one register block of V): the same arithmetic with the memory latency hidden. W of the
-// next tile row (raw storage bits) and its U block are loaded while the current tile row computes;
-// the 16 rows of a tile row are unrolled, each selected as soon as its sums are complete.
-template <bool BF16>
-__global__ __launch_bounds__(64 * kResWaves) void residual_pack_r64_kernel(
+// Grid (tile-column blocks of kResWaves * CPL tiles, tile rows). Lane l of wave w owns column l of
+// tiles (blockIdx.x * kResWaves + w) * CPL + s, s < CPL.
+template <bool BF16, int CPL>
+__global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
     const void* __restrict__ W, const void* __restrict__ U, const void* __restrict__ V, int n_out, int K, int r,
-    int TK, int TR, int tile_rows_per_wg, u32x4_t* __restrict__ values, uint32_t* __restrict__ meta) {
-  constexpr int kTileU32 = BF16 ? 256 : 512;
-  constexpr int kWRaw = BF16 ? 2 : 4;                       // 32-bit words of one row's 4 entries
-  constexpr int kUPer = 16 * kRJ / (64 * kResWaves);       // U elements each thread stages per tile row
-  __shared__ f32x4_t us[16 * kRJ / 4];
-  __shared__ uint32_t img[kResWaves][4 * kTileU32];
-  __shared__ uint32_t mimg[kResWaves][4 * 32];
+    int TK, u32x4_t* __restrict__ values, uint32_t* __restrict__ meta) {
+  constexpr int kTileU32 = BF16 ? 256 : 512;  // one packed tile's values in 32-bit words
+  __shared__ f32x4_t us[16 * kRJ / 4];        // U rows of the tile row, one rank block, float32
+  __shared__ uint32_t img[kResWaves][kTileU32];
+  __shared__ uint32_t mimg[kResWaves][32];
+  __shared__ __align__(16) uint32_t ebuf[kResWaves][16 * 64];  // rounded rows of a tile (storage bits)
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col_block = (blockIdx.x * kResWaves + wave) * 256;
-  const int c0 = col_block + 4 * lane;
-  const bool col_ok = c0 < K;
-  const int cc = col_ok ? c0 : 0;
-  const int tl = lane >> 4, gi = lane & 15;
-  const int tr_begin = blockIdx.y * tile_rows_per_wg, tr_end = min(TR, tr_begin + tile_rows_per_wg);
-  if (tr_begin >= tr_end) return;  // uniform over the workgroup
-
-  float v[kRJ][4];
+  const int tk0 = (blockIdx.x * kResWaves + wave) * CPL;  // this wave's first tile column
+  const int tr = blockIdx.y;
+  const size_t esz = BF16 ? 2 : 4;
+  bool col_ok[CPL];
+  int cc[CPL];
 #pragma unroll
-  for (int j = 0; j < kRJ; ++j) load4<BF16>(V, (size_t)min(j, r - 1) * K + cc, v[j]);
+  for (int s = 0; s < CPL; ++s) {
+    const int c = (tk0 + s) * 64 + lane;
+    col_ok[s] = c < K;
+    cc[s] = col_ok[s] ? c : K - 1;  // clamped column for loads
+  }
 
-  uint32_t wraw[16][kWRaw];
-  float unext[kUPer];
-  auto load_w = [&](int tr) {
+  // running sums, initialised with W; row pointers advance by one row per step (rows past n_out
+  // repeat the last)
+  float acc[CPL][16];
+  {
+    const char* wp = (const char*)W + (size_t)min(tr * 16, n_out - 1) * K * esz;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t* p = (const uint32_t*)W + ((size_t)min(tr * 16 + i, n_out - 1) * K + cc) * (BF16 ? 2 : 4) / 4;
-      if constexpr (BF16) {
-        const u32x2_t w = *(const u32x2_t*)p;
-        wraw[i][0] = w[0], wraw[i][1] = w[1];
-      } else {
-        const u32x4_t w = *(const u32x4_t*)p;
-        wraw[i][0] = w[0], wraw[i][1] = w[1], wraw[i][2] = w[2], wraw[i][3] = w[3];
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) acc[s][i] = load_elem<BF16>(wp, cc[s]);
+      if (tr * 16 + i + 1 < n_out) wp += (size_t)K * esz;
+    }
+  }
+
+  for (int jb = 0; jb < r; jb += kRJ) {
+    const int nj = min(kRJ, r - jb);
+    __syncthreads();  // every wave is done reading the previous block of U
+    for (int q = threadIdx.x; q < 16 * kRJ; q += 64 * kResWaves) {
+      const int row = q / kRJ, j = q % kRJ;
+      ((float*)us)[q] = j < nj ? load_elem<BF16>(U, (size_t)min(tr * 16 + row, n_out - 1) * r + jb + j) : 0.0f;
+    }
+    float v[CPL][kRJ];
+    {
+      const char* vp = (const char*)V + (size_t)jb * K * esz;
+#pragma unroll
+      for (int j = 0; j < kRJ; ++j) {
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) v[s][j] = load_elem<BF16>(vp, cc[s]);
+        if (j + 1 < nj) vp += (size_t)K * esz;  // ranks past r repeat the last (never used)
       }
     }
-  };
-  auto load_u = [&](int tr) {
-#pragma unroll
-    for (int t = 0; t < kUPer; ++t) {
-      const int q = threadIdx.x + t * 64 * kResWaves, i = q / kRJ, j = q % kRJ;
-      unext[t] = j < r ? load_elem<BF16>(U, (size_t)min(tr * 16 + i, n_out - 1) * r + j) : 0.0f;
+    __syncthreads();
+    // exactly nj steps (a padding step is not neutral): whole 16-rank parts, then the rest
+    const int nb = nj & 15;
+    static_assert(kRJ == 32 || kRJ == 64, "rank block of 32 or 64");
+    switch (nj >> 4) {
+      case 4: if constexpr (kRJ == 64) fma_block<64, CPL>(acc, v, us); break;
+      case 3: if constexpr (kRJ == 64) { fma_block<48, CPL>(acc, v, us); fma_tail<48, CPL>(acc, v, us, nb); } break;
+      case 2: fma_block<32, CPL>(acc, v, us); if constexpr (kRJ == 64) fma_tail<32, CPL>(acc, v, us, nb); break;
+      case 1: fma_block<16, CPL>(acc, v, us); fma_tail<16, CPL>(acc, v, us, nb); break;
+      default: fma_tail<0, CPL>(acc, v, us, nb); break;
     }
-  };
-  auto stage_u = [&]() {
-#pragma unroll
-    for (int t = 0; t < kUPer; ++t) ((float*)us)[threadIdx.x + t * 64 * kResWaves] = unext[t];
-  };
+  }
 
-  load_u(tr_begin);
-  stage_u();
-  load_w(tr_begin);
-  __syncthreads();
-  for (int tr = tr_begin; tr < tr_end; ++tr) {
-    const bool more = tr + 1 < tr_end;
-    if (more) load_u(tr + 1);  // in flight during this tile row
+  // round, select the top two of each group, pack: tile (tr, tk0 + s) per column s. The rounded
+  // rows go through the per-wave buffer `ebuf` so that each lane selects whole groups: item
+  // m*64 + lane = row 4m + lane/16, group lane%16.
+  constexpr uint32_t kMag = BF16 ? 0x7FFFu : 0x7FFFFFFFu;
+  const int gg = lane & 15;
+#pragma unroll
+  for (int s = 0; s < CPL; ++s) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float a[4];
-      if constexpr (BF16) {
-        a[0] = __uint_as_float(wraw[i][0] << 16), a[1] = __uint_as_float(wraw[i][0] & 0xFFFF0000u);
-        a[2] = __uint_as_float(wraw[i][1] << 16), a[3] = __uint_as_float(wraw[i][1] & 0xFFFF0000u);
-      } else {
-        a[0] = __uint_as_float(wraw[i][0]), a[1] = __uint_as_float(wraw[i][1]);
-        a[2] = __uint_as_float(wraw[i][2]), a[3] = __uint_as_float(wraw[i][3]);
-      }
-      if (r == kRJ) {
+      const bool ok = col_ok[s] && tr * 16 + i < n_out;
+      ebuf[wave][i * 64 + lane] = ok ? storage_bits<BF16>(acc[s][i]) : 0u;
+    }
+    const bool gok = (tk0 + s) * 64 + 4 * gg < K;  // the group's columns exist (K is a multiple of 32)
 #pragma unroll
-        for (int j4 = 0; j4 < kRJ / 4; ++j4) {
-          const f32x4_t u = us[i * (kRJ / 4) + j4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) a[c] = __builtin_fmaf(-u[t], v[4 * j4 + t][c], a[c]);
-        }
-      } else {
-#pragma unroll
-        for (int j4 = 0; j4 < kRJ / 4; ++j4) {
-          const f32x4_t u = us[i * (kRJ / 4) + j4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (4 * j4 + t < r) {  // wave-uniform
-#pragma unroll
-              for (int c = 0; c < 4; ++c) a[c] = __builtin_fmaf(-u[t], v[4 * j4 + t][c], a[c]);
-            }
-        }
-      }
-      const bool ok = col_ok && tr * 16 + i < n_out;
-      uint32_t e[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) e[c] = ok ? storage_bits<BF16>(a[c]) : 0u;
-      const uint32_t m = BF16 ? 0x7FFFu : 0x7FFFFFFFu;
+    for (int m = 0; m < 4; ++m) {
+      const int i = 4 * m + (lane >> 4);
+      const u32x4_t e = *(const u32x4_t*)&ebuf[wave][i * 64 + 4 * gg];
       uint32_t va, vb;
-      uint32_t nib = top2_of_4(e[0] & m, e[1] & m, e[2] & m, e[3] & m, e[0], e[1], e[2], e[3], va, vb);
-      if (!ok) nib = 0;
-      const int slot = i + 16 * (gi >> 2);
-      if constexpr (BF16) {
-        img[wave][tl * kTileU32 + slot * 4 + (gi & 3)] = va | (vb << 16);
-      } else {
-        *(u32x2_t*)&img[wave][tl * kTileU32 + slot * 8 + 2 * (gi & 3)] = u32x2_t{va, vb};
-      }
+      uint32_t nib = top2_of_4(e[0] & kMag, e[1] & kMag, e[2] & kMag, e[3] & kMag, e[0], e[1], e[2], e[3], va, vb);
+      if (!gok || tr * 16 + i >= n_out) nib = 0;  // padding: zero entries (already zero) and zero nibbles
+      const int slot = i + 16 * (gg >> 2);
+      if constexpr (BF16) img[wave][slot * 4 + (gg & 3)] = va | (vb << 16);
+      else *(u32x2_t*)&img[wave][slot * 8 + 2 * (gg & 3)] = u32x2_t{va, vb};
+      // nibble gg % 8 of word gg / 8 of row i: the eight lanes gg % 8 = 0..7 share it
       uint32_t word = nib;
       word |= (uint32_t)__shfl_down((int)word, 1) << 4;
       word |= (uint32_t)__shfl_down((int)word, 2) << 8;
       word |= (uint32_t)__shfl_down((int)word, 4) << 16;
-      if ((gi & 7) == 0) mimg[wave][tl * 32 + (gi >> 3) * 16 + i] = word;
+      if ((lane & 7) == 0) mimg[wave][(gg >> 3) * 16 + i] = word;
     }
-    if (more) load_w(tr + 1);  // the raw W of this tile row is consumed
-    const int tk0 = col_block / 64;
-    constexpr int kTileU4 = kTileU32 / 4;
+    // this wave's LDS writes are complete before its own reads below, and those before the next
+    // tile's writes (LDS operations of one wave execute in order)
+    const int tk = tk0 + s;
+    if (tk < TK) {
+      constexpr int kTileU4 = kTileU32 / 4;
 #pragma unroll
-    for (int q = lane; q < 4 * kTileU4; q += 64) {
-      const int t = q / kTileU4;
-      if (tk0 + t < TK) values[((size_t)tr * TK + tk0 + t) * kTileU4 + q % kTileU4] = ((const u32x4_t*)img[wave])[q];
+      for (int q = lane; q < kTileU4; q += 64) values[((size_t)tr * TK + tk) * kTileU4 + q] = ((const u32x4_t*)img[wave])[q];
+      if (lane < 8) ((u32x4_t*)meta)[((size_t)tr * TK + tk) * 8 + lane] = ((const u32x4_t*)mimg[wave])[lane];
     }
-    if (lane < 32) {
-      const int t = lane / 8;
-      if (tk0 + t < TK) ((u32x4_t*)meta)[((size_t)tr * TK + tk0 + t) * 8 + lane % 8] = ((const u32x4_t*)mimg[wave])[lane];
-    }
-    __syncthreads();  // every wave is done with this tile row's U
-    if (more) stage_u();
-    __syncthreads();
   }
 }
 
@@ -317,25 +193,15 @@ __global__ __launch_bounds__(64 * kResWaves) void residual_pack_r64_kernel(
 
 hipError_t launch_prune24_pack_residual(const void* W, const void* U, const void* V, int64_t n_out, int64_t n_in,
                                         int64_t r, bool bf16, void* values, uint32_t* meta, hipStream_t stream) {
+  constexpr int CPL = kResColsPerLane;
   const int TK = (int)ceil_div(n_in, 64), TR = (int)ceil_div(n_out, 16);
-  const int col_groups = (int)ceil_div(n_in, 256 * kResWaves);
-  // about 512 workgroups; each takes a run of tile rows (V stays in registers across the run)
-  const int tile_rows = (int)std::max<int64_t>(1, ceil_div((int64_t)TR * col_groups, 512));
-  dim3 grid((unsigned)col_groups, (unsigned)ceil_div(TR, tile_rows));
-  if (r >= 1 && r <= kRJ) {
-    if (bf16)
-      residual_pack_r64_kernel<true><<<grid, dim3(64 * kResWaves), 0, stream>>>(
-          W, U, V, (int)n_out, (int)n_in, (int)r, TK, TR, tile_rows, (u32x4_t*)values, meta);
-    else
-      residual_pack_r64_kernel<false><<<grid, dim3(64 * kResWaves), 0, stream>>>(
-          W, U, V, (int)n_out, (int)n_in, (int)r, TK, TR, tile_rows, (u32x4_t*)values, meta);
-  } else if (bf16) {
-    residual_pack_kernel<true><<<grid, dim3(64 * kResWaves), 0, stream>>>(
-        W, U, V, (int)n_out, (int)n_in, (int)r, TK, TR, tile_rows, (u32x4_t*)values, meta);
-  } else {
-    residual_pack_kernel<false><<<grid, dim3(64 * kResWaves), 0, stream>>>(
-        W, U, V, (int)n_out, (int)n_in, (int)r, TK, TR, tile_rows, (u32x4_t*)values, meta);
-  }
+  dim3 grid((unsigned)ceil_div(TK, kResWaves * CPL), (unsigned)TR);
+  if (bf16)
+    residual_pack_kernel<true, CPL><<<grid, dim3(64 * kResWaves), 0, stream>>>(W, U, V, (int)n_out, (int)n_in, (int)r,
+                                                                              TK, (u32x4_t*)values, meta);
+  else
+    residual_pack_kernel<false, CPL><<<grid, dim3(64 * kResWaves), 0, stream>>>(W, U, V, (int)n_out, (int)n_in,
+                                                                               (int)r, TK, (u32x4_t*)values, meta);
   return hipGetLastError();
 }
 
