@@ -29,12 +29,22 @@ import torch
 from . import binding
 
 
+def _gram(Y: torch.Tensor) -> np.ndarray:
+    """Y^T Y in float64 for Y [n, k] (k small), as the sum of per-chunk products of up to 32 row
+    chunks (a batched product keeps many workgroups busy where one k x k product over all n rows
+    would run on a single one)."""
+    n, k = Y.shape
+    chunks = 32 if n % 32 == 0 and n >= 32 * k else 1
+    Yd = Y.double().reshape(chunks, n // chunks, k)
+    return torch.bmm(Yd.transpose(1, 2).contiguous(), Yd).sum(0).cpu().numpy()
+
+
 def _orthonormalize(Y: torch.Tensor) -> torch.Tensor:
     """Orthonormal basis of the columns of Y [n, k] (k small) by Cholesky QR, twice: the Gram
     matrix is formed in float64 on the GPU, its k x k Cholesky factor inverted in float64 on the
     host, and Y multiplied by the inverse."""
     for _ in range(2):
-        G = (Y.double().T @ Y.double()).cpu().numpy()
+        G = _gram(Y)
         Rinv = np.linalg.inv(np.linalg.cholesky(G).T)
         Y = Y @ torch.from_numpy(Rinv).to(device=Y.device, dtype=torch.float32)
     return Y
@@ -54,7 +64,7 @@ def _low_rank(Z: torch.Tensor, r: int, basis: Optional[torch.Tensor], power_iter
         B = _orthonormalize(Z.T @ Q)
     Q = _orthonormalize(Z @ B)
     small = Q.T @ Z                                   # [k, n_in]
-    lam, vec = np.linalg.eigh((small.double() @ small.double().T).cpu().numpy())
+    lam, vec = np.linalg.eigh(_gram(small.T.contiguous()))
     order = np.argsort(lam)[::-1][:k]
     lam, vec = np.maximum(lam[order], 0.0), vec[:, order]
     s = np.sqrt(lam)
