@@ -234,8 +234,8 @@ __device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint
 }
 
 // Store acc[i][j] (rows n = nrow0 + 16 i + 4*(lane/16) + 0..3, token m = mrow0 + 16 j + lane%16), as
-// float32, or (y_bf16) rounded to bfloat16 (to nearest even).
-template <int NI, int NJ>
+// float32, or (y_bf16) rounded to bfloat16 (to nearest even); NT: non-temporal vector stores.
+template <int NI, int NJ, bool NT = false>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* __restrict__ Yv, int y_bf16, int M,
                                            int n_out, int nrow0, int mrow0, int lane) {
   const bool vec_ok = (n_out & 3) == 0;
@@ -252,7 +252,9 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* _
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(acc[i][j][e]);
         if (vec_ok && n + 3 < n_out) {
-          *(u32x2_t*)(yrow + n) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          const u32x2_t w = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          if constexpr (NT) __builtin_nontemporal_store(w, (u32x2_t*)(yrow + n));
+          else *(u32x2_t*)(yrow + n) = w;
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -272,7 +274,8 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* _
     for (int i = 0; i < NI; ++i) {
       const int n = nrow0 + 16 * i + 4 * (lane >> 4);
       if (vec_ok && n + 3 < n_out) {
-        *(f32x4_t*)(yrow + n) = acc[i][j];
+        if constexpr (NT) __builtin_nontemporal_store(acc[i][j], (f32x4_t*)(yrow + n));
+        else *(f32x4_t*)(yrow + n) = acc[i][j];
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -290,6 +293,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* _
 // instruction). All addressing is derived here from the lane and the tile origin.
 constexpr int kYPitch = 68;
 constexpr int kRowsEpilogueMaxTiles = 256;  // one workgroup per CU of MI355X
+constexpr double kNonTemporalYBytes = 192.0 * (1 << 20);
 template <int NI, int NJ>
 __device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[NI][NJ], float* buf, void* __restrict__ Yv,
                                                 int y_bf16, int M, int n_out, int nrow0, int mrow0) {
@@ -338,11 +342,14 @@ __device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[NI][NJ], fl
 
 // ----------------------------------------------------------------------------------- prefill
 
-template <int NI, int NJ, int P, int PX, bool ROWS_EPI>
+// EPI: how Y is stored -- kEpiDirect (fragment order), kEpiRows (row-contiguous through LDS),
+// kEpiDirectNT (fragment order, non-temporal)
+constexpr int kEpiDirect = 0, kEpiRows = 1, kEpiDirectNT = 2;
+template <int NI, int NJ, int P, int PX, int EPI>
 __global__ __launch_bounds__(256) void linear_prefill_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16, int M, int K,
-    int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
+    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16,
+    int M, int K, int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
   constexpr int WAVES = 4;
   constexpr int BN = 16 * NI * WAVES;
   constexpr int BM = 16 * NJ;
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
       lds_barrier();
     }
   }
-  if constexpr (ROWS_EPI) {
+  if constexpr (EPI == kEpiRows) {
     // Y leaves through LDS (every slot is free now: the last barrier above retired all reads of
     // them); waves 0, 1 use the T pair slot, waves 2, 3 the U slot
     static_assert(2 * 64 * kYPitch * 4 <= (int)sizeof(tpair) && 2 * 64 * kYPitch * 4 <= (int)sizeof(ulds),
@@ -568,7 +575,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
     float* ybuf = (wave < 2 ? (float*)&tpair[0][0] : (float*)&ulds[0]) + (wave & 1) * 64 * kYPitch;
     store_tile_rows<NI, NJ>(acc, ybuf, Y, y_bf16, M, n_out, nrow0, m0);
   } else {
-    store_tile<NI, NJ>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
+    store_tile<NI, NJ, EPI == kEpiDirectNT>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
   }
 }
 
@@ -727,12 +734,22 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   // together and are exposed: the row-contiguous epilogue stores them faster. With several tiles per
   // CU the stores overlap the next tile's loop, and with r > 64 the extra registers of that
   // epilogue cost spills in the rank-r blocks after the loop: there the direct epilogue is faster.
+  // A Y larger than three quarters of the 256 MB Infinity Cache is stored non-temporally: kept in the
+  // cache it evicts the S and X rows that later tile groups re-read (measured: -6 to -11 % on
+  // 4096/8192 tokens x 14336 outputs; +5 % slower on 8192 x 4096, 134 MB, so the threshold sits
+  // between).
+  const bool y_nt = (double)M * n_out * (y_bf16 ? 2 : 4) > kNonTemporalYBytes;
+  const dim3 grid((unsigned)(8 * per_xcd)), block(256);
   if (n_tiles <= kRowsEpilogueMaxTiles && r <= 64)
-    linear_prefill_kernel<NI, NJ, P, PX, true><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
+    linear_prefill_kernel<NI, NJ, P, PX, kEpiRows><<<grid, block, 0, stream>>>(
+        (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
+        (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+  else if (y_nt)
+    linear_prefill_kernel<NI, NJ, P, PX, kEpiDirectNT><<<grid, block, 0, stream>>>(
         (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
         (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   else
-    linear_prefill_kernel<NI, NJ, P, PX, false><<<dim3((unsigned)(8 * per_xcd)), dim3(256), 0, stream>>>(
+    linear_prefill_kernel<NI, NJ, P, PX, kEpiDirect><<<grid, block, 0, stream>>>(
         (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
         (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   return hipGetLastError();
