@@ -42,3 +42,28 @@ def test_bf16_output(dtype, M, n_in, n_out, r):
     y = inputs.bf16_bits_to_f32(bits16).astype(np.float64)
     bound = TAU[dtype] * rms(y_ref) + np.abs(y_ref) * 2.0 ** -8
     assert np.all(np.abs(y - y_ref) <= bound)
+
+
+def test_bf16_output_full_mlp_layer():
+    """The 8192-token MLP gate layer at rank 128 (the block workload's largest output): its
+    bfloat16 Y (235 MB) is stored non-temporally. Bit for bit against the host's rounding of the
+    float32 Y (also non-temporal, 470 MB) of the same kernels, and sampled token rows against the
+    oracle within TAU * rms + half an ulp."""
+    L = inputs.make_layer("C5", 4)
+    assert (L.M, L.n_in, L.n_out, L.r) == (8192, 4096, 14336, 128)
+    print(f"[linear bf16 Y] C5/{L.name} M={L.M} n_in={L.n_in} n_out={L.n_out} r={L.r}", flush=True)
+    Xd, Ud, Vd = to_dev(L.X, "bf16"), to_dev(L.U, "bf16"), to_dev(L.V, "bf16")
+    vd, md = binding.prune24_pack(to_dev(L.R, "bf16"))
+    y16 = binding.linear_ex(Xd, vd, md, Ud, Vd, y_dtype=torch.bfloat16, n_out=L.n_out)
+    y32 = binding.linear(Xd, vd, md, Ud, Vd, n_out=L.n_out)
+    torch.cuda.synchronize()
+    bits16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    y32h = y32.cpu().numpy()
+    del y16, y32
+    assert np.array_equal(bits16, rne_bf16_bits(y32h))
+    rows = np.array([0, 1, 127, 128, 4095, 8191])
+    v_ref, m_ref = oracle.prune24_pack(L.R, "bf16")
+    y_ref = oracle.linear(L.X, v_ref, m_ref, L.n_out, L.U, L.V, "bf16", rows=rows)
+    y = inputs.bf16_bits_to_f32(bits16[rows]).astype(np.float64)
+    bound = TAU["bf16"] * rms(y_ref) + np.abs(y_ref) * 2.0 ** -8
+    assert np.all(np.abs(y - y_ref) <= bound)
