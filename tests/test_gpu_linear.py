@@ -55,6 +55,9 @@ SHAPES = [
     (1024, 1024, 384, 64),
     # low-rank pre-pass: many K slices (decode), rank counts that are not a multiple of 64
     (16, 4096, 64, 64), (40, 1056, 100, 80), (128, 4096, 256, 192),
+    # first stage with 128 ranks per workgroup (r > 64) at its three token blocks (16 / 32 / 64 by
+    # M), partial rank blocks, the largest rank on both paths
+    (1100, 2080, 300, 128), (4100, 320, 72, 144), (96, 512, 80, 1024), (16, 256, 64, 1024),
 ]
 
 
