@@ -18,7 +18,9 @@ the cost of an event.
 
 Prints one JSON line. `value` is dense-equivalent TFLOP/s (2 M n_out n_in per layer) of the whole
 step for the prefill workloads, or GB/s of the weight-side bytes (packed values, metadata, U, V)
-for the decode workload. `roofline` describes the kernel with the largest share of the step.
+for the decode workload. `roofline` describes the kernel with the largest share of the step;
+`context` holds reference points from the same run (a dense GEMM of the first layer's shape through
+torch, a plain device copy moving as many bytes as its weight side).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2] [--no-cpu-baseline]
 """
@@ -310,6 +312,8 @@ def main():
         input_generation_s=round(gen_s, 1),
     )
 
+    out["context"] = measure_context(layers, decode, tdt, stream, dev, args)
+
     if not args.no_next:
         out["next"] = measure_next(binding, inputs, layers, sets, copies, stream, dev, args)
 
@@ -335,6 +339,45 @@ def time_per_call(issue, n, stream, spin_cycles):
         e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / (n * REPEAT)
+
+
+def measure_context(layers, decode, tdt, stream, dev, args):
+    """Reference points measured in the same run (context for the fractions of peak, not targets),
+    on the first layer: a dense GEMM of the layer's shape (torch.mm in the storage type: X
+    [M x n_in] times a dense [n_in x n_out], hipBLASLt; prefill workloads), and a plain read stream
+    of the same size as the layer's weight-side bytes (packed values, metadata, U, V): a device copy
+    reading half of them and writing the other half, rotated over enough buffers to miss the 256 MB
+    Infinity Cache."""
+    import torch
+    L = layers[0]
+    isz = 2 if tdt == torch.bfloat16 else 4
+    n = max(8, args.steps // 2)
+    spin = int(4e4 * n * REPEAT)
+    res = {}
+    if not decode:
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        X = torch.randn(L.M, L.n_in, device=dev, generator=g).to(tdt)
+        Ws = [torch.randn(L.n_in, L.n_out, device=dev, generator=g).to(tdt) for _ in range(4)]
+        ms = time_per_call(lambda i: torch.mm(X, Ws[i % len(Ws)]), n, stream, spin)
+        flop = 2 * L.M * L.n_out * L.n_in
+        peak = PEAK_BF16_TFLOPS if isz == 2 else PEAK_FP32_TFLOPS
+        res["dense_gemm"] = dict(layer=L.name, op="torch.mm (hipBLASLt), dense weight of the same shape",
+                                 us=round(ms * 1e3, 2), TFLOPs=round(flop / (ms * 1e-3) / 1e12, 1),
+                                 frac_of_peak=round(flop / (ms * 1e-3) / 1e12 / peak, 4))
+        del X, Ws
+    wbytes = L.n_out * L.n_in // 2 * isz + L.n_out * L.n_in // 8 + (L.n_out + L.n_in) * L.r * isz
+    half = wbytes // 2 // 16 * 16
+    nbuf = max(2, math.ceil(MALL_DEFEAT_BYTES / wbytes))
+    srcs = [torch.ones(half, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    dsts = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    ms = time_per_call(lambda i: dsts[i % nbuf].copy_(srcs[i % nbuf]), n, stream, spin)
+    res["stream"] = dict(layer=L.name, op="device copy moving the weight-side bytes (half read, half written)",
+                         bytes=2 * half, us=round(ms * 1e3, 2), GBps=round(2 * half / (ms * 1e-3) / 1e9, 1),
+                         frac_hbm=round(2 * half / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+    del srcs, dsts
+    torch.cuda.synchronize()
+    return res
 
 
 def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
