@@ -9,7 +9,7 @@
 // as a binary64 product, which is exact for binary32 (and bfloat16) factors; NaN scores are made
 // one canonical value, so they tie and outrank every number. The kept entries are R's own.
 //
-// HBM streaming kernel. A workgroup owns 16 rows x 512 bytes of R (four bf16 tiles or two fp32
+// HBM streaming kernel. A workgroup owns 16 rows x 1 KiB of R (eight bf16 tiles or four fp32
 // tiles of the packed layout). Each lane reads 16-byte chunks with row-contiguous, fully
 // coalesced loads, ranks the four entries of each group with six integer compares of keys (the
 // sign-cleared bit patterns, or the bit patterns of the exact binary64 scores: bit-exact either way),

@@ -13,7 +13,9 @@
 // tile row (lane l: column l of each), a workgroup of 4 waves the neighbouring tiles. Each lane
 // keeps its columns' 16 running sums and, per block of kRJ ranks, its columns of V in registers;
 // U for the tile row and the rank block is staged in LDS as float32 and read with broadcast reads
-// (one read feeds 4 ranks of every column of the lane). Registers stay low enough for several
+// (one read feeds 4 ranks of every column of the lane). A broadcast 16-byte read still returns
+// 1 KiB per wave through the LDS data path, so with one column per lane that path, not the FMAs,
+// sets the pace; two columns halve the LDS bytes per FMA. Registers stay low enough for three
 // waves per SIMD, which hide each other's LDS and memory latency.
 // The rounded rows of a tile pass through LDS so that each lane selects whole groups (four rows'
 // worth of groups per lane instead of every lane of a group repeating the selection); the kept
@@ -29,7 +31,7 @@ namespace {
 
 constexpr int kResWaves = 4;
 constexpr int kRJ = 32;   // ranks per block (a lane's column of V for the block sits in registers)
-constexpr int kResColsPerLane = 1;  // columns (tiles) per lane (wave)
+constexpr int kResColsPerLane = 2;  // columns (tiles) per lane (wave)
 
 template <bool BF16>
 __device__ __forceinline__ float load_elem(const void* base, size_t i) {
