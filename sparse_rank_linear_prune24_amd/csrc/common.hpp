@@ -65,10 +65,21 @@ __device__ __forceinline__ f32x4_t smfmac16x16x64(bf16x8_t a, bf16x16_t b, f32x4
 template <typename Key>
 __device__ __forceinline__ uint32_t top2_of_4(Key k0, Key k1, Key k2, Key k3, uint32_t e0, uint32_t e1, uint32_t e2,
                                               uint32_t e3, uint32_t& va, uint32_t& vb) {
-  const int w0 = (k0 >= k1) + (k0 >= k2) + (k0 >= k3);
-  const int w1 = (k1 > k0) + (k1 >= k2) + (k1 >= k3);
-  const int w2 = (k2 > k0) + (k2 > k1) + (k2 >= k3);
-  const int w3 = (k3 > k0) + (k3 > k1) + (k3 > k2);
+  int w0, w1, w2, w3;
+  if constexpr (sizeof(Key) == 8) {
+    // 64-bit keys: one compare per pair (k_j > k_i is 1 - (k_i >= k_j) for totally ordered keys)
+    const int c01 = k0 >= k1, c02 = k0 >= k2, c03 = k0 >= k3, c12 = k1 >= k2, c13 = k1 >= k3, c23 = k2 >= k3;
+    w0 = c01 + c02 + c03;
+    w1 = 1 - c01 + c12 + c13;
+    w2 = 2 - c02 - c12 + c23;
+    w3 = 3 - c03 - c13 - c23;
+  } else {
+    // 32-bit keys: both compares of a pair are cheap, and this form measured slightly faster
+    w0 = (k0 >= k1) + (k0 >= k2) + (k0 >= k3);
+    w1 = (k1 > k0) + (k1 >= k2) + (k1 >= k3);
+    w2 = (k2 > k0) + (k2 > k1) + (k2 >= k3);
+    w3 = (k3 > k0) + (k3 > k1) + (k3 > k2);
+  }
   const bool keep0 = w0 >= 2, keep1 = w1 >= 2, keep2 = w2 >= 2, keep3 = w3 >= 2;
   const int a = keep0 ? 0 : (keep1 ? 1 : 2);
   const int b = keep3 ? 3 : (keep2 ? 2 : 1);

@@ -25,9 +25,10 @@ namespace {
 constexpr int kPackThreads = 256;
 constexpr int kPackChunksPerThread = 4;  // 16-byte chunks of R per thread
 
-// Activation-aware key: |x| * |d| exactly (binary64), NaN canonical; compared as unsigned integers.
-__device__ __forceinline__ uint64_t scaled_key(float x, float d) {
-  const double p = (double)fabsf(x) * (double)fabsf(d);
+// Activation-aware key: |x| * |d| exactly (binary64; dmag = |d| as binary64), NaN canonical;
+// compared as unsigned integers.
+__device__ __forceinline__ uint64_t scaled_key(float x, double dmag) {
+  const double p = (double)fabsf(x) * dmag;
   return p != p ? 0x7FF8000000000000ull : (uint64_t)__double_as_longlong(p);
 }
 
@@ -50,8 +51,10 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   const int tk0 = blockIdx.y * kTiles;          // first tile column of this workgroup
   const int tid = threadIdx.x;
 
+  // a thread's chunks are rows tid / kRowChunks + 4c of one column chunk (kPackThreads is a
+  // multiple of kRowChunks), so they share their column scales
+  static_assert(kPackThreads % kRowChunks == 0, "a thread's chunks share their columns");
   u32x4_t x[CPT];
-  f32x4_t ds[CPT][kPerChunk / 4];  // this chunk's column scales (SCALED only)
   bool valid[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -62,10 +65,16 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
     valid[c] = n < n_out && k < K;
     x[c] = valid[c] ? __builtin_nontemporal_load((const u32x4_t*)(R + ((size_t)n * K + k) * kEsz))
                     : u32x4_t{0, 0, 0, 0};
-    if constexpr (SCALED) {
+  }
+  // column scales of the thread's chunk as float64 magnitudes (SCALED only)
+  double dmag[kPerChunk];
+  if constexpr (SCALED) {
+    const int k = blockIdx.y * kCols + (tid % kRowChunks) * kPerChunk;
 #pragma unroll
-      for (int h = 0; h < kPerChunk / 4; ++h)
-        ds[c][h] = k < K ? *(const f32x4_t*)(dscale + k + 4 * h) : f32x4_t{0, 0, 0, 0};
+    for (int h = 0; h < kPerChunk / 4; ++h) {
+      const f32x4_t d4 = k < K ? *(const f32x4_t*)(dscale + k + 4 * h) : f32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dmag[4 * h + e] = (double)fabsf(d4[e]);
     }
   }
 #pragma unroll
@@ -80,12 +89,11 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
       const uint32_t d0 = x[c][0], d1 = x[c][1], d2 = x[c][2], d3 = x[c][3];
       uint32_t n0, n1;
       if constexpr (SCALED) {
-        auto key = [](uint32_t bits16, float s) { return scaled_key(__uint_as_float(bits16 << 16), s); };
-        const f32x4_t s0 = ds[c][0], s1 = ds[c][1];
-        n0 = top2_of_4(key(d0 & 0xFFFFu, s0[0]), key(d0 >> 16, s0[1]), key(d1 & 0xFFFFu, s0[2]), key(d1 >> 16, s0[3]),
-                       d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16, v[0], v[1]);
-        n1 = top2_of_4(key(d2 & 0xFFFFu, s1[0]), key(d2 >> 16, s1[1]), key(d3 & 0xFFFFu, s1[2]), key(d3 >> 16, s1[3]),
-                       d2 & 0xFFFFu, d2 >> 16, d3 & 0xFFFFu, d3 >> 16, v[2], v[3]);
+        auto key = [](uint32_t bits16, double s) { return scaled_key(__uint_as_float(bits16 << 16), s); };
+        n0 = top2_of_4(key(d0 & 0xFFFFu, dmag[0]), key(d0 >> 16, dmag[1]), key(d1 & 0xFFFFu, dmag[2]),
+                       key(d1 >> 16, dmag[3]), d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16, v[0], v[1]);
+        n1 = top2_of_4(key(d2 & 0xFFFFu, dmag[4]), key(d2 >> 16, dmag[5]), key(d3 & 0xFFFFu, dmag[6]),
+                       key(d3 >> 16, dmag[7]), d2 & 0xFFFFu, d2 >> 16, d3 & 0xFFFFu, d3 >> 16, v[2], v[3]);
       } else {
         n0 = top2_of_4(d0 & 0x7FFFu, (d0 >> 16) & 0x7FFFu, d1 & 0x7FFFu, (d1 >> 16) & 0x7FFFu, d0 & 0xFFFFu, d0 >> 16,
                        d1 & 0xFFFFu, d1 >> 16, v[0], v[1]);
@@ -108,10 +116,9 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
       const uint32_t e0 = x[c][0], e1 = x[c][1], e2 = x[c][2], e3 = x[c][3];
       uint32_t va, vb, nb;
       if constexpr (SCALED) {
-        const f32x4_t sc = ds[c][0];
-        nb = top2_of_4(scaled_key(__uint_as_float(e0), sc[0]), scaled_key(__uint_as_float(e1), sc[1]),
-                       scaled_key(__uint_as_float(e2), sc[2]), scaled_key(__uint_as_float(e3), sc[3]), e0, e1, e2, e3,
-                       va, vb);
+        nb = top2_of_4(scaled_key(__uint_as_float(e0), dmag[0]), scaled_key(__uint_as_float(e1), dmag[1]),
+                       scaled_key(__uint_as_float(e2), dmag[2]), scaled_key(__uint_as_float(e3), dmag[3]), e0, e1,
+                       e2, e3, va, vb);
       } else {
         nb = top2_of_4(e0 & 0x7FFFFFFFu, e1 & 0x7FFFFFFFu, e2 & 0x7FFFFFFFu, e3 & 0x7FFFFFFFu, e0, e1, e2, e3, va, vb);
       }
