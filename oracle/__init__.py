@@ -47,6 +47,7 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.splr_ref_prune24_pack.argtypes = [P, I64, I64, ctypes.c_int, P, P]
         lib.splr_ref_prune24_pack_scaled.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
+        lib.splr_ref_prune_nm.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
         lib.splr_ref_residual.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P]
         lib.splr_ref_prune24_pack_residual.argtypes = [P, P, P, I64, I64, I64, ctypes.c_int, P, P]
         lib.splr_ref_unpack.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
@@ -88,6 +89,27 @@ def prune24_pack(R: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
     if rc:
         raise ValueError(f"splr_ref_prune24_pack failed ({rc}) for shape {R.shape}")
     return values, meta
+
+
+def prune_nm(R: np.ndarray, n: int, m: int, dtype: str) -> np.ndarray:
+    """N:M projection of R [n_out x n_in]: in every group of m consecutive columns keep the n
+    entries of largest magnitude (ties to the lower column) as bit copies, the rest +0."""
+    R = _check(R, dtype, 2, "R")
+    n_out, n_in = R.shape
+    Rp = np.empty_like(R)
+    rc = _load().splr_ref_prune_nm(_ptr(R), n_out, n_in, n, m, _DT[dtype], _ptr(Rp))
+    if rc:
+        raise ValueError(f"splr_ref_prune_nm failed ({rc}) for shape {R.shape}, {n}:{m}")
+    return Rp
+
+
+def prune_nm_pack(R: np.ndarray, n: int, m: int, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """N:M projection, stored in the 2:4 packed layout: prune24_pack(prune_nm(R, n, m)). For n <= 2
+    and 4 | m every aligned group of four holds at most two nonzeros of the projection, so the 2:4
+    pack keeps all of them and the packed S is exactly the N:M matrix."""
+    if not (n <= 2 and m % 4 == 0):
+        raise ValueError(f"{n}:{m} is not storable in the 2:4 layout (needs n <= 2 and 4 | m)")
+    return prune24_pack(prune_nm(R, n, m, dtype), dtype)
 
 
 def prune24_pack_scaled(R: np.ndarray, d: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:

@@ -37,6 +37,12 @@
  *                                decompositions acts on the weight minus the current low-rank part,
  *                                R = W - U V (HASSLE-free page, §4 and §4.1.1, the sparse subproblem
  *                                (P1)); the fused pack forms R entry by entry and projects it.
+ *   splr_ref_prune_nm         -- N:M projection: in every group of M consecutive input columns keep
+ *                                the N entries of largest magnitude and zero the rest, the same
+ *                                hard thresholding under an N:M constraint (HASSLE-free page, §1 and
+ *                                §2: the framework targets N:M sparsity; 3BASiL article, "A
+ *                                three-block ADMM replaces alternating minimization": N:M structures
+ *                                such as 2:4, and the 2:8 + rank-64 configuration after LoRA).
  *   splr_ref_linear           -- the compressed forward pass sums the sparse product and the
  *                                low-rank product, computed side by side (LoSparse page, §3 and
  *                                §3.2), here as Y = X S^T + (X V^T) U^T.
@@ -180,6 +186,40 @@ int splr_ref_prune24_pack_scaled(const void *R, const float *d, int64_t n_out, i
                                  void *values, uint32_t *meta) {
   if (!d) return SPLR_REF_EINVAL;
   return pack_by_keys(R, d, n_out, n_in, dtype, values, meta);
+}
+
+/*
+ * N:M projection of R [n_out x n_in] into Rp (same storage type): in every group of m consecutive
+ * columns of a row, entry i is kept (bit copy) when fewer than n entries of the group outrank it
+ * (larger magnitude key, or an equal key at a lower position); every other entry becomes +0.
+ * Readings: ties go to the lower position, as in the 2:4 projection; a dropped entry is stored as
+ * +0 (the projection sets it to zero, and zero has no sign to keep).  Requires 1 <= n <= m and m | n_in.
+ */
+int splr_ref_prune_nm(const void *R, int64_t n_out, int64_t n_in, int n, int m, int dtype, void *Rp) {
+  if (!R || !Rp) return SPLR_REF_EINVAL;
+  if (n_out < 0 || n_in < 0 || m < 1 || n < 1 || n > m || n_in % m != 0) return SPLR_REF_EINVAL;
+  if (dtype != SPLR_REF_FP32 && dtype != SPLR_REF_BF16) return SPLR_REF_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < n_out; ++row) {
+    for (int64_t g0 = 0; g0 < n_in; g0 += m) {
+      const size_t base = (size_t)row * (size_t)n_in + (size_t)g0;
+      for (int i = 0; i < m; ++i) {
+        const uint32_t ki = magnitude_key(R, dtype, base + i);
+        int above = 0;
+        for (int j = 0; j < m; ++j) {
+          const uint32_t kj = magnitude_key(R, dtype, base + j);
+          if (kj > ki || (kj == ki && j < i)) ++above;
+        }
+        if (above < n)
+          copy_elem(Rp, base + i, R, base + i, dtype);
+        else if (dtype == SPLR_REF_BF16)
+          ((uint16_t *)Rp)[base + i] = 0;
+        else
+          ((uint32_t *)Rp)[base + i] = 0;
+      }
+    }
+  }
+  return SPLR_REF_OK;
 }
 
 /* binary32 (not NaN) -> bfloat16 bits, round to nearest even. */
