@@ -383,7 +383,8 @@ def measure_context(layers, decode, tdt, stream, dev, args):
 def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
     """The parts built beyond the hot path, each timed per call on every layer of the workload
     (outside the timed step): the activation-aware pack (keys |R| |d|, d = column norms of the
-    layer's activations), the fused residual + pack (R = W - U V formed in the kernel), the layer
+    layer's activations), the 2:8 projection stored in the 2:4 layout, the fused residual + pack
+    (R = W - U V formed in the kernel), the layer
     product with a bfloat16 Y (splr_linear_ex) and steps of the data-free alternating minimisation."""
     import torch
     n = max(8, args.steps // 2)
@@ -404,6 +405,22 @@ def measure_next(binding, inputs, layers, sets, copies, stream, dev, args):
                               frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)))
     res["pack_scaled"] = dict(entry="splr_prune24_pack_scaled", bound="hbm",
                               work="bytes: R + d + packed values + metadata", per_layer=per_layer)
+
+    # N:M projection (2:8, the pages' post-fine-tuning pattern) stored in the 2:4 layout: HBM bound,
+    # the same bytes as the 2:4 pack
+    per_layer = []
+    for li, L in enumerate(layers):
+        nbytes = pack_bytes(L.n_in, L.n_out, inputs.itemsize(L.dtype))
+
+        def issue(i, li=li):
+            s = sets[i % copies][li]
+            binding.prune_nm_pack(s["R"], 2, 8, s["values"], s["meta"], stream=stream)
+
+        ms = time_per_call(issue, n, stream, spin)
+        per_layer.append(dict(layer=L.name, us=round(ms * 1e3, 2), GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                              frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)))
+    res["pack_2_8"] = dict(entry="splr_prune_nm_pack (n = 2, m = 8)", bound="hbm",
+                           work="bytes: R + packed values + metadata", per_layer=per_layer)
 
     # fused residual + pack: vector-ALU bound (r fused multiply-adds per weight, binary32, not packed)
     per_layer = []

@@ -85,6 +85,31 @@ splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr
                                 void* values, uint32_t* meta, hipStream_t stream);
 
 /*
+ * splr_prune_nm_pack -- Euclidean projection onto an N:M set, stored in the 2:4 packed layout.
+ *
+ * N:M sparsity keeps at most n of every m consecutive weights (HASSLE-free page, §1 and §2: the
+ * framework targets N:M sparsity; 3BASiL article, "A three-block ADMM replaces alternating
+ * minimization": N:M structures such as 2:4, and the 2:8 + rank-64 configuration after LoRA
+ * fine-tuning); with an identity Hessian the projection is hard thresholding (HASSLE-free §4.1.1).
+ * For each row and each group of m consecutive columns the n entries of largest magnitude are kept
+ * as bit copies (magnitude and ties exactly as in splr_prune24_pack: equal magnitudes go to the
+ * lower column) and the others become +0; the result is then packed exactly as splr_prune24_pack
+ * packs it.  With n <= 2 and m a multiple of 4, no aligned group of four holds more than two
+ * nonzeros, so the packed S is exactly the N:M matrix and splr_linear computes with it unchanged
+ * (patterns denser than 2:4 somewhere, e.g. 4:8, do not fit the 2:4 operand and are rejected).
+ * n = 2, m = 4 is splr_prune24_pack itself.  Bit-exact and deterministic.
+ *
+ *   R      [n_out][n_in] dtype, row-major       input
+ *   n, m   n in {1, 2}, m in {4, 8, 16}
+ *   values, meta                               output, packed layout above
+ * Errors: NULL pointer -> SPLR_ERR_NULL; n_out < 1, n_in < 32, n_in % 32 != 0, or (n, m) outside
+ *         the sets above -> SPLR_ERR_SHAPE; bad dtype -> SPLR_ERR_DTYPE; misaligned pointer ->
+ *         SPLR_ERR_ALIGN.
+ */
+splr_status_t splr_prune_nm_pack(const void* R, int64_t n_out, int64_t n_in, int32_t n, int32_t m,
+                                 splr_dtype_t dtype, void* values, uint32_t* meta, hipStream_t stream);
+
+/*
  * splr_prune24_pack_residual -- residual R = W - U V formed in the kernel, then projected and packed
  * exactly as splr_prune24_pack does (R never goes to memory).
  *

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libsplr.so")
 SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
-EXPORTS = ("splr_prune24_pack", "splr_linear_ex", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
+EXPORTS = ("splr_prune24_pack", "splr_prune_nm_pack", "splr_linear_ex", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
            "splr_linear_stage1", "splr_linear_stage2", "splr_dense_reconstruct", "splr_status_string",
            "splr_version")
 
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.splr_prune24_pack.argtypes = [_P, _I64, _I64, _I32, _P, _P, _P]
         L.splr_prune24_pack.restype = _I32
         L.splr_prune24_pack_scaled.argtypes = [_P, _P, _I64, _I64, _I32, _P, _P, _P]
+        L.splr_prune_nm_pack.argtypes = [_P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]
+        L.splr_prune_nm_pack.restype = _I32
         L.splr_prune24_pack_scaled.restype = _I32
         L.splr_prune24_pack_residual.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _P]
         L.splr_prune24_pack_residual.restype = _I32
@@ -124,6 +126,21 @@ def prune24_pack(R: torch.Tensor, values: Optional[torch.Tensor] = None, meta: O
         meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
     _check("splr_prune24_pack", lib().splr_prune24_pack(_dev(R, "R"), n_out, n_in, _dtype_code(R),
                                                         _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
+    return values, meta
+
+
+def prune_nm_pack(R: torch.Tensor, n: int, m: int, values: Optional[torch.Tensor] = None,
+                  meta: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """N:M projection (n in {1, 2}, m in {4, 8, 16}) of R [n_out, n_in], stored in the 2:4 packed
+    layout -> (values, meta) as prune24_pack returns them."""
+    n_out, n_in = R.shape
+    TR, TK = tiles(n_out, n_in)
+    if values is None:
+        values = torch.empty((TR, TK, 64, 8), dtype=R.dtype, device=R.device)
+    if meta is None:
+        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
+    _check("splr_prune_nm_pack", lib().splr_prune_nm_pack(_dev(R, "R"), n_out, n_in, n, m, _dtype_code(R),
+                                                          _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
     return values, meta
 
 

@@ -54,6 +54,18 @@ splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr
   return from_hip(splr::launch_prune24_pack(R, n_out, n_in, dtype == SPLR_BF16, values, meta, stream));
 }
 
+splr_status_t splr_prune_nm_pack(const void* R, int64_t n_out, int64_t n_in, int32_t n, int32_t m,
+                                 splr_dtype_t dtype, void* values, uint32_t* meta, hipStream_t stream) {
+  if (!R || !values || !meta) return SPLR_ERR_NULL;
+  splr_status_t s = check_in(n_in);
+  if (s == SPLR_OK) s = check_rows(n_out, n_in);
+  if (s == SPLR_OK && !((n == 1 || n == 2) && (m == 4 || m == 8 || m == 16))) s = SPLR_ERR_SHAPE;
+  if (s != SPLR_OK) return s;  // n_in % 32 == 0, so every m above divides n_in
+  if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!aligned16(R) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
+  return from_hip(splr::launch_prune_nm_pack(R, n_out, n_in, n, m, dtype == SPLR_BF16, values, meta, stream));
+}
+
 splr_status_t splr_prune24_pack_residual(const void* W, const void* U, const void* V, int64_t n_out, int64_t n_in,
                                          int64_t r, splr_dtype_t dtype, void* values, uint32_t* meta,
                                          hipStream_t stream) {

@@ -12,6 +12,9 @@ hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool 
 // Fused residual R = W - U V (pinned binary32 fused multiply-add order, then rounding) + pack.
 hipError_t launch_prune24_pack_residual(const void* W, const void* U, const void* V, int64_t n_out, int64_t n_in,
                                         int64_t r, bool bf16, void* values, uint32_t* meta, hipStream_t stream);
+// N:M projection (n in {1, 2}, m in {4, 8, 16}), then the 2:4 pack of the result.
+hipError_t launch_prune_nm_pack(const void* R, int64_t n_out, int64_t n_in, int n, int m, bool bf16, void* values,
+                                uint32_t* meta, hipStream_t stream);
 // The same with keys |R[n][k]| * |d[k]| (d: float32 [n_in]).
 hipError_t launch_prune24_pack_scaled(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16,
                                       void* values, uint32_t* meta, hipStream_t stream);

@@ -9,6 +9,15 @@
 // as a binary64 product, which is exact for binary32 (and bfloat16) factors; NaN scores are made
 // one canonical value, so they tie and outrank every number. The kept entries are R's own.
 //
+// N:M projection (HASSLE-free page, §1 and §2: N:M sparsity; 3BASiL article, "A three-block ADMM
+// replaces alternating minimization": N:M structures such as 2:4, and the 2:8 configuration): in
+// every group of M consecutive columns the n entries of largest magnitude are kept (ties to the
+// lower column) and the rest become +0; the result then goes through the 2:4 selection and pack
+// unchanged. For n <= 2 and 4 | M no aligned group of four holds more than two nonzeros, so the
+// packed 2:4 operand is exactly the N:M matrix and the layer product runs on it as it is. A group
+// that spans several 16-byte chunks lies in neighbouring lanes (a lane's chunk index along the row
+// is its lane id), whose words are exchanged with cross-lane shuffles.
+//
 // HBM streaming kernel. A workgroup owns 16 rows x 1 KiB of R (eight bf16 tiles or four fp32
 // tiles of the packed layout). Each lane reads 16-byte chunks with row-contiguous, fully
 // coalesced loads, ranks the four entries of each group with six integer compares of keys (the
@@ -32,11 +41,97 @@ __device__ __forceinline__ uint64_t scaled_key(float x, double dmag) {
   return p != p ? 0x7FF8000000000000ull : (uint64_t)__double_as_longlong(p);
 }
 
-template <bool BF16, bool SCALED, int CPT>
+// N:M projection of one 16-byte chunk in place (group size M, n_keep kept per group). Every lane of
+// the wave must call this (the shuffles read neighbouring lanes); `lane` is the chunk's index along
+// its row within the wave's 64 chunks.
+template <bool BF16, int M>
+__device__ __forceinline__ void nm_project_chunk(u32x4_t& x, int n_keep, int lane) {
+  constexpr int kPer = BF16 ? 8 : 4;                  // entries per chunk
+  constexpr int kChunks = M > kPer ? M / kPer : 1;    // chunks (lanes) per group
+  constexpr int kGroup = M < kPer ? M : kPer * kChunks;  // entries per group (= M)
+  static_assert(kGroup == M && (kChunks & (kChunks - 1)) == 0 && 64 % kChunks == 0, "groups of whole lanes");
+  // the group's words, in column order (this lane's own chunk at position lane % kChunks)
+  uint32_t w[kChunks][4];
+  const int base = lane & ~(kChunks - 1);
+#pragma unroll
+  for (int g = 0; g < kChunks; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[g][i] = kChunks == 1 ? x[i] : (uint32_t)__shfl((int)x[i], base + g);
+  auto key = [&](int g, int e) -> uint32_t {  // magnitude key of entry e of chunk g
+    if constexpr (BF16) return (w[g][e >> 1] >> (16 * (e & 1))) & 0x7FFFu;
+    else return w[g][e] & 0x7FFFFFFFu;
+  };
+  const int own = lane & (kChunks - 1);
+  constexpr int kSeen = kChunks * kPer;  // entries the lane sees: its group, or the chunk's groups
+  int above[kPer];                       // 0: outranks all others of its group; >= n_keep: dropped
+  if constexpr (BF16) {
+    // 15-bit keys: the value (key << 4) | (15 - position in the group) is unique within a group
+    // and orders its entries exactly as "outranks" (larger key, then lower position), so the
+    // first and second of a group are its largest and second-largest values
+    static_assert(M <= 16, "4 position bits");
+    uint32_t cv[kSeen];
+#pragma unroll
+    for (int t = 0; t < kSeen; ++t) cv[t] = (key(t / kPer, t % kPer) << 4) | (uint32_t)(15 - t % M);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) above[e] = 2;
+#pragma unroll
+    for (int g0 = 0; g0 < kSeen; g0 += M) {
+      uint32_t m1 = cv[g0];
+#pragma unroll
+      for (int t = g0 + 1; t < g0 + M; ++t) m1 = max(m1, cv[t]);
+      uint32_t m2 = 0;  // values are unique and a group has >= 4, so the second is > 0
+#pragma unroll
+      for (int t = g0; t < g0 + M; ++t) m2 = max(m2, cv[t] != m1 ? cv[t] : 0u);
+      const uint32_t thr = n_keep == 1 ? m1 : m2;  // kept: the values >= the n-th largest
+      // this lane's entries of the group
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        if (kChunks == 1 && (e < g0 || e >= g0 + M)) continue;  // compile-time
+        const uint32_t c = (key(own, e) << 4) | (uint32_t)(15 - (kChunks == 1 ? e - g0 : own * kPer + e));
+        above[e] = c >= thr ? 0 : 2;
+      }
+    }
+  } else {
+    // 31-bit keys: rank by one compare per unordered pair (the lower position i outranks j iff
+    // k_i >= k_j, and the pair counts for one of the two)
+    int rk[kSeen];
+#pragma unroll
+    for (int t = 0; t < kSeen; ++t) rk[t] = 0;
+#pragma unroll
+    for (int g0 = 0; g0 < kSeen; g0 += M)
+#pragma unroll
+      for (int i = g0; i < g0 + M; ++i)
+#pragma unroll
+        for (int j = i + 1; j < g0 + M; ++j) {
+          const int c = key(i / kPer, i % kPer) >= key(j / kPer, j % kPer) ? 1 : 0;
+          rk[j] += c;
+          rk[i] += 1 - c;
+        }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      above[e] = rk[e];
+#pragma unroll
+      for (int g = 1; g < kChunks; ++g) above[e] = own == g ? rk[g * kPer + e] : above[e];
+    }
+  }
+  uint32_t out[4] = {x[0], x[1], x[2], x[3]};
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if (above[e] >= n_keep) {  // dropped: +0
+      if constexpr (BF16) out[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      else out[e] = 0u;
+    }
+  }
+  x = u32x4_t{out[0], out[1], out[2], out[3]};
+}
+
+// NM: 0 for the 2:4 projection, else the group size M of an N:M projection applied first
+// (n_keep kept per group).
+template <bool BF16, bool SCALED, int CPT, int NM = 0>
 __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_t* __restrict__ R,
                                                                     const float* __restrict__ dscale, int n_out, int K,
                                                                     int TK, u32x4_t* __restrict__ values,
-                                                                    uint32_t* __restrict__ meta) {
+                                                                    uint32_t* __restrict__ meta, int n_keep = 2) {
   constexpr int kEsz = BF16 ? 2 : 4;            // bytes per entry
   constexpr int kPerChunk = 16 / kEsz;          // entries per 16-byte chunk (8 bf16 = 2 groups, 4 fp32 = 1)
   constexpr int kRowChunks = 16 * CPT;          // 16-byte chunks per row: CPT per thread over 16 rows
@@ -76,6 +171,11 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
 #pragma unroll
       for (int e = 0; e < 4; ++e) dmag[4 * h + e] = (double)fabsf(d4[e]);
     }
+  }
+  if constexpr (NM > 0) {
+    static_assert(!SCALED && kPackThreads % 64 == 0 && kRowChunks == 64, "a lane's chunk index is its lane id");
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) nm_project_chunk<BF16, NM>(x[c], n_keep, tid & 63);
   }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -144,19 +244,19 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   if (tid < n_tiles * 8) ((u32x4_t*)meta)[t0 * 8 + tid] = ((const u32x4_t*)sm)[tid];
 }
 
-template <bool SCALED>
+template <bool SCALED, int NM = 0>
 hipError_t launch_pack(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16, void* values,
-                       uint32_t* meta, hipStream_t stream) {
+                       uint32_t* meta, hipStream_t stream, int n_keep = 2) {
   constexpr int CPT = kPackChunksPerThread;
   const int TK = (int)ceil_div(n_in, 64);
   const int cols = 16 * CPT * (bf16 ? 8 : 4);
   dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(n_in, cols));
   if (bf16)
-    prune24_pack_kernel<true, SCALED, CPT><<<grid, dim3(kPackThreads), 0, stream>>>(
-        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta);
+    prune24_pack_kernel<true, SCALED, CPT, NM><<<grid, dim3(kPackThreads), 0, stream>>>(
+        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta, n_keep);
   else
-    prune24_pack_kernel<false, SCALED, CPT><<<grid, dim3(kPackThreads), 0, stream>>>(
-        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta);
+    prune24_pack_kernel<false, SCALED, CPT, NM><<<grid, dim3(kPackThreads), 0, stream>>>(
+        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta, n_keep);
   return hipGetLastError();
 }
 
@@ -165,6 +265,17 @@ hipError_t launch_pack(const void* R, const float* d, int64_t n_out, int64_t n_i
 hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
                                uint32_t* meta, hipStream_t stream) {
   return launch_pack<false>(R, nullptr, n_out, n_in, bf16, values, meta, stream);
+}
+
+hipError_t launch_prune_nm_pack(const void* R, int64_t n_out, int64_t n_in, int n, int m, bool bf16, void* values,
+                                uint32_t* meta, hipStream_t stream) {
+  if (n == 2 && m == 4) return launch_pack<false>(R, nullptr, n_out, n_in, bf16, values, meta, stream);
+  switch (m) {
+    case 4: return launch_pack<false, 4>(R, nullptr, n_out, n_in, bf16, values, meta, stream, n);
+    case 8: return launch_pack<false, 8>(R, nullptr, n_out, n_in, bf16, values, meta, stream, n);
+    case 16: return launch_pack<false, 16>(R, nullptr, n_out, n_in, bf16, values, meta, stream, n);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prune24_pack_scaled(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16,

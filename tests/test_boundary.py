@@ -49,6 +49,19 @@ def test_pack_validation():
     assert f(A, 4, 64, 0, A, MIS, None) == ALIGN
 
 
+def test_prune_nm_pack_validation():
+    f = binding.lib().splr_prune_nm_pack
+    assert f(None, 4, 64, 2, 8, 1, A, A, None) == NULL
+    assert f(A, 4, 64, 2, 8, 1, None, A, None) == NULL
+    assert f(A, 0, 64, 2, 8, 1, A, A, None) == SHAPE
+    assert f(A, 4, 48, 2, 8, 1, A, A, None) == SHAPE
+    for n, m in [(0, 4), (3, 4), (3, 8), (4, 8), (2, 6), (2, 32), (1, 2)]:
+        assert f(A, 4, 64, n, m, 1, A, A, None) == SHAPE, (n, m)
+    assert f(A, 4, 64, 2, 8, 2, A, A, None) == DTYPE
+    assert f(MIS, 4, 64, 2, 8, 1, A, A, None) == ALIGN
+    assert f(A, 4, 64, 1, 16, 0, A, MIS, None) == ALIGN
+
+
 def test_pack_scaled_validation():
     f = binding.lib().splr_prune24_pack_scaled
     assert f(None, A, 4, 64, 1, A, A, None) == NULL
