@@ -20,7 +20,33 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 from . import prune24_pack_residual, unpack
-from sparse_rank_linear_prune24_amd import inputs
+
+
+# ---- storage-type conversions (this module's own; the oracle imports nothing from the product)
+
+def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of a stored array: float32 values, or bfloat16 bit patterns (uint16),
+    which are the upper 16 bits of a float32."""
+    if dtype == "fp32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _from_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 to the storage type: to the nearest float32 (ties to even), then for bfloat16
+    to the nearest bfloat16 (ties to even: add 0x7FFF plus the lowest kept bit, drop 16 bits).
+    The factors rounded here are finite."""
+    a32 = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    if dtype == "fp32":
+        return a32
+    if dtype != "bf16":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    if not np.all(np.isfinite(a32)):
+        raise ValueError("non-finite factor")
+    u = a32.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
 def truncated_svd(Z: np.ndarray, r: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -35,13 +61,13 @@ def balanced_factors(Z: np.ndarray, r: int, dtype: str) -> Tuple[Optional[np.nda
         return None, None
     u, s, vt = truncated_svd(Z, r)
     root = np.sqrt(s)
-    return inputs.from_f64(u * root, dtype), inputs.from_f64(root[:, None] * vt, dtype)
+    return _from_f64(u * root, dtype), _from_f64(root[:, None] * vt, dtype)
 
 
 def dense_sparse(values, meta, n_out: int, n_in: int, dtype: str) -> np.ndarray:
     """The packed S as a dense float64 matrix (stored entries at their columns, zeros elsewhere)."""
     kept, nib = unpack(values, meta, n_out, n_in, dtype)
-    k = inputs.to_f64(kept, dtype)
+    k = _to_f64(kept, dtype)
     S = np.zeros((n_out, n_in))
     groups = n_in // 4
     a = (nib & 3).astype(np.int64)
@@ -57,7 +83,7 @@ def alternating_minimization(W: np.ndarray, r: int, iters: int, dtype: str):
     """Returns (values, meta, U, V, objectives) after `iters` steps; objectives[t] is
     ||W - S_t - U_t V_t||_F after step t (each step: S from the current factors, then new factors)."""
     n_out, n_in = W.shape
-    w = inputs.to_f64(W, dtype)
+    w = _to_f64(W, dtype)
     U, V = balanced_factors(w, r, dtype)
     objectives: List[float] = []
     values = meta = None
@@ -65,6 +91,6 @@ def alternating_minimization(W: np.ndarray, r: int, iters: int, dtype: str):
         values, meta = prune24_pack_residual(W, U, V, dtype)
         S = dense_sparse(values, meta, n_out, n_in, dtype)
         U, V = balanced_factors(w - S, r, dtype)
-        L = 0.0 if U is None else inputs.to_f64(U, dtype) @ inputs.to_f64(V, dtype)
+        L = 0.0 if U is None else _to_f64(U, dtype) @ _to_f64(V, dtype)
         objectives.append(float(np.linalg.norm(w - S - L)))
     return values, meta, U, V, objectives

@@ -367,6 +367,8 @@ int splr_ref_linear(const void *X, int64_t M, int64_t n_in, const void *values,
 /*
  * W_hat[n][k] = S[n][k] + sum_j U[n][j] * V[j][k] in float64, where S is the dense matrix
  * scattered from (values, meta): the two stored entries at their positions, +0 elsewhere.
+ * Without a low-rank part (r = 0) W_hat is S itself, entry for entry: a stored -0 stays -0 (adding
+ * an empty sum, +0, would turn it into +0).  With r > 0 the rank-r sum is added to every entry.
  */
 int splr_ref_dense_reconstruct(const void *values, const uint32_t *meta, const void *U,
                                const void *V, int64_t n_out, int64_t n_in, int64_t r, int dtype,
@@ -386,6 +388,7 @@ int splr_ref_dense_reconstruct(const void *values, const uint32_t *meta, const v
       w[4 * g + a] = load_f64(values, dtype, value_index(n, g, 0, n_in));
       w[4 * g + b] = load_f64(values, dtype, value_index(n, g, 1, n_in));
     }
+    if (r == 0) continue;
     for (int64_t k = 0; k < n_in; ++k) {
       double lowrank = 0.0;
       for (int64_t j = 0; j < r; ++j)

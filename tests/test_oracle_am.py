@@ -68,3 +68,17 @@ def test_rank_r_weight_is_fitted_by_the_start():
     W = (A.astype(np.float64) @ B.astype(np.float64)).astype(np.float32)
     _, _, _, _, obj = am.alternating_minimization(W, 6, 2, "fp32")
     assert obj[0] < 1e-5 * np.linalg.norm(W.astype(np.float64))
+
+
+def test_storage_rounding_helpers():
+    """The alternating minimisation's own conversions: exact widening, and round to nearest even
+    at the bfloat16 boundary (hand-written cases: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 and
+    goes to the even 1; 1 + 3 * 2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6 and goes to 1 + 2^-6;
+    just above a halfway point rounds up)."""
+    from oracle import am as oam
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -2.5, 0.0, -0.0])
+    b = oam._from_f64(x, "bf16")
+    assert b.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x0000, 0x8000]
+    assert oam._to_f64(b, "bf16").tolist() == [1.0, 1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -2.5, 0.0, -0.0]
+    f = oam._from_f64(np.array([1 + 2.0 ** -30, 3.0]), "fp32")
+    assert f.dtype == np.float32 and f.tolist() == [1.0, 3.0]

@@ -227,3 +227,42 @@ def test_tiled_layout_positions(dtype):
     rows_used[[0, 16, 32, 48]] = True
     assert not values[1][:, ~rows_used, :].any()
     assert not meta[1][:, :, 1:].any()
+
+
+def _fixture_cases():
+    rows = {"fp32": [], "bf16": []}
+    with open(os.path.join(HERE, "golden", "pack_special_groups.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                p = line.split()
+                rows[p[0]].append(([int(t, 16) for t in p[1:5]], int(p[5], 16), int(p[6], 16), int(p[7], 16)))
+    return rows
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_reconstruct_without_low_rank_is_the_stored_entries(dtype):
+    """With no low-rank part the reconstruction is S itself (LoSparse page, §3: W ~ UV + S with the
+    low-rank part absent): the fixture's two stored entries, widened exactly to float32, at the
+    positions of its hand-written nibble, and +0 at the other two. The fixture keeps -0 in several
+    groups (e.g. 80000000 00000000 00000000 00000001 -> 80000000 at position 0), so an
+    implementation that adds an empty low-rank sum (-0 + 0 = +0) fails here."""
+    cases = _fixture_cases()[dtype]
+    width = np.uint32 if dtype == "fp32" else np.uint16
+    R, ng = groups_to_matrix(np.array([c[0] for c in cases], dtype=width).view(NP[dtype]), dtype)
+    values, meta = oracle.prune24_pack(R, dtype)
+    W = oracle.dense_reconstruct(values, meta, R.shape[0], R.shape[1], None, None, dtype)
+    got = W.astype(np.float32).view(np.uint32).reshape(-1, 4)
+    widen = (lambda b: b) if dtype == "fp32" else (lambda b: b << 16)
+    for i, (xs, nibble, v0, v1) in enumerate(cases):
+        a, b = nibble & 3, nibble >> 2
+        want = [0, 0, 0, 0]
+        want[a], want[b] = widen(v0), widen(v1)
+        # NaN payloads do not survive the float64 round trip bit for bit; compare them as NaN
+        for q in range(4):
+            wq = np.array([want[q]], dtype=np.uint32).view(np.float32)[0]
+            if np.isnan(wq):
+                assert np.isnan(got[i, q].view(np.float32)), (dtype, i, q)
+            else:
+                assert int(got[i, q]) == want[q], (dtype, [hex(x) for x in xs], q, hex(int(got[i, q])), hex(want[q]))
+    assert any(c[2] in (0x80000000, 0x8000) or c[3] in (0x80000000, 0x8000) for c in cases), "fixture keeps a -0"
