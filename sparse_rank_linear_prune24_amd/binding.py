@@ -83,10 +83,14 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (use torch.bfloat16 or torch.float32)")
 
 
+def _is_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _dev(t: Optional[torch.Tensor], name: str) -> Optional[int]:
     if t is None:
         return None
-    if not t.is_cuda:
+    if not _is_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -94,8 +98,72 @@ def _dev(t: Optional[torch.Tensor], name: str) -> Optional[int]:
 
 
 def _stream(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    return _the_stream(stream).cuda_stream
+
+
+def _the_stream(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _expect(t: Optional[torch.Tensor], name: str, dtype, numel: int, device, shape=None):
+    """Raise ValueError unless `t` is a contiguous device tensor of `dtype` on `device` holding
+    exactly `numel` elements (and of `shape`, when given). The C ABI sees only pointers, so a
+    buffer of the wrong size would be read or written out of bounds: every tensor is checked here,
+    before the call."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not _is_device(t):
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, expected {numel}")
+
+
+def _matrix(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    if not isinstance(t, torch.Tensor) or not _is_device(t):
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape[0], t.shape[1]
+
+
+def _packed_out(values, meta, n_out, n_in, dtype, device, stream):
+    """Check caller-supplied packed buffers (or allocate them on the call's stream)."""
+    TR, TK = tiles(n_out, n_in)
+    if values is None or meta is None:
+        with torch.cuda.stream(_the_stream(stream)):
+            if values is None:
+                values = torch.empty((TR, TK, 64, 8), dtype=dtype, device=device)
+            if meta is None:
+                meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=device)
+    _expect(values, "values", dtype, TR * TK * 512, device)
+    _expect(meta, "meta", torch.int32, TR * TK * 32, device)
+    return values, meta
+
+
+def _check_packed_in(values, meta, n_out, n_in, dtype, device):
+    TR, TK = tiles(n_out, n_in)
+    _expect(values, "values", dtype, TR * TK * 512, device)
+    _expect(meta, "meta", torch.int32, TR * TK * 32, device)
+
+
+def _check_factors(U, V, n_out, n_in, dtype, device):
+    """U [n_out, r] and V [r, n_in] of the storage type (both or neither); returns r."""
+    if (U is None) != (V is None):
+        raise ValueError("U and V are given together (or neither, for no low-rank part)")
+    if U is None:
+        return 0
+    r = U.shape[1] if U.dim() == 2 else -1
+    _expect(U, "U", dtype, n_out * max(r, 0), device, (n_out, r))
+    _expect(V, "V", dtype, r * n_in, device, (r, n_in))
+    return r
 
 
 def _check(fn: str, status: int):
@@ -118,12 +186,9 @@ def packed_bytes(n_out: int, n_in: int, dtype: torch.dtype) -> Tuple[int, int]:
 def prune24_pack(R: torch.Tensor, values: Optional[torch.Tensor] = None, meta: Optional[torch.Tensor] = None,
                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """2:4 projection + pack of R [n_out, n_in] -> (values (TR, TK, 64, 8), meta int32 (TR, TK, 2, 16))."""
-    n_out, n_in = R.shape
-    TR, TK = tiles(n_out, n_in)
-    if values is None:
-        values = torch.empty((TR, TK, 64, 8), dtype=R.dtype, device=R.device)
-    if meta is None:
-        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
+    n_out, n_in = _matrix(R, "R")
+    _dtype_code(R)
+    values, meta = _packed_out(values, meta, n_out, n_in, R.dtype, R.device, stream)
     _check("splr_prune24_pack", lib().splr_prune24_pack(_dev(R, "R"), n_out, n_in, _dtype_code(R),
                                                         _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
     return values, meta
@@ -133,12 +198,9 @@ def prune_nm_pack(R: torch.Tensor, n: int, m: int, values: Optional[torch.Tensor
                   meta: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """N:M projection (n in {1, 2}, m in {4, 8, 16}) of R [n_out, n_in], stored in the 2:4 packed
     layout -> (values, meta) as prune24_pack returns them."""
-    n_out, n_in = R.shape
-    TR, TK = tiles(n_out, n_in)
-    if values is None:
-        values = torch.empty((TR, TK, 64, 8), dtype=R.dtype, device=R.device)
-    if meta is None:
-        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
+    n_out, n_in = _matrix(R, "R")
+    _dtype_code(R)
+    values, meta = _packed_out(values, meta, n_out, n_in, R.dtype, R.device, stream)
     _check("splr_prune_nm_pack", lib().splr_prune_nm_pack(_dev(R, "R"), n_out, n_in, n, m, _dtype_code(R),
                                                           _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
     return values, meta
@@ -148,13 +210,10 @@ def prune24_pack_residual(W: torch.Tensor, U: Optional[torch.Tensor], V: Optiona
                           values: Optional[torch.Tensor] = None, meta: Optional[torch.Tensor] = None,
                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """2:4 projection + pack of R = W - U V, formed in the kernel (pinned fused multiply-add order)."""
-    n_out, n_in = W.shape
-    r = 0 if U is None else U.shape[1]
-    TR, TK = tiles(n_out, n_in)
-    if values is None:
-        values = torch.empty((TR, TK, 64, 8), dtype=W.dtype, device=W.device)
-    if meta is None:
-        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=W.device)
+    n_out, n_in = _matrix(W, "W")
+    _dtype_code(W)
+    r = _check_factors(U, V, n_out, n_in, W.dtype, W.device)
+    values, meta = _packed_out(values, meta, n_out, n_in, W.dtype, W.device, stream)
     _check("splr_prune24_pack_residual",
            lib().splr_prune24_pack_residual(_dev(W, "W"), _dev(U, "U"), _dev(V, "V"), n_out, n_in, r, _dtype_code(W),
                                             _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
@@ -166,14 +225,10 @@ def prune24_pack_scaled(R: torch.Tensor, d: torch.Tensor, values: Optional[torch
     """Activation-aware 2:4 projection + pack of R [n_out, n_in] with per-column scales d (float32
     [n_in]): keeps the two entries of largest |R[n][k]| * |d[k]| per group. Same outputs as
     prune24_pack."""
-    n_out, n_in = R.shape
-    if d.dtype != torch.float32 or tuple(d.shape) != (n_in,):
-        raise ValueError(f"d must be float32 of shape ({n_in},), got {d.dtype} {tuple(d.shape)}")
-    TR, TK = tiles(n_out, n_in)
-    if values is None:
-        values = torch.empty((TR, TK, 64, 8), dtype=R.dtype, device=R.device)
-    if meta is None:
-        meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=R.device)
+    n_out, n_in = _matrix(R, "R")
+    _dtype_code(R)
+    _expect(d, "d", torch.float32, n_in, R.device, (n_in,))
+    values, meta = _packed_out(values, meta, n_out, n_in, R.dtype, R.device, stream)
     _check("splr_prune24_pack_scaled",
            lib().splr_prune24_pack_scaled(_dev(R, "R"), _dev(d, "d"), n_out, n_in, _dtype_code(R),
                                           _dev(values, "values"), _dev(meta, "meta"), _stream(stream)))
@@ -185,23 +240,43 @@ def workspace_bytes(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype) -
     return int(lib().splr_linear_workspace_bytes(M, n_out, n_in, r, code))
 
 
-def new_workspace(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype, device="cuda") -> Optional[torch.Tensor]:
-    """A workspace for splr_linear with these sizes (None when none is needed). Any workspace of at
-    least workspace_bytes() serves any call; this one is zero-filled so that nothing depends on
-    leftover contents."""
+def new_workspace(M: int, n_out: int, n_in: int, r: int, dtype: torch.dtype, device="cuda",
+                  stream=None) -> Optional[torch.Tensor]:
+    """A workspace for splr_linear with these sizes (None when none is needed), allocated on
+    `stream` (default: the current stream). Any workspace of at least workspace_bytes() serves any
+    call, and its contents need no initialisation: every byte the second stage reads is written by
+    the first stage of the same call."""
     need = workspace_bytes(M, n_out, n_in, r, dtype)
-    return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
+    if not need:
+        return None
+    with torch.cuda.stream(_the_stream(stream)):
+        return torch.empty(need, dtype=torch.uint8, device=device)
 
 
-def _linear_args(X, values, U, n_out, out, workspace, with_workspace=True):
-    M, n_in = X.shape
+def _linear_args(X, values, meta, U, V, n_out, out, workspace, stream, y_dtype=torch.float32, with_workspace=True,
+                 need_v=True):
+    """Checks every tensor of a layer-product call against the sizes passed to the C ABI, and
+    allocates what is missing on the call's stream."""
+    M, n_in = _matrix(X, "X")
+    _dtype_code(X)
     if n_out is None:
         n_out = U.shape[0] if U is not None else values.shape[0] * 16
-    r = 0 if U is None else U.shape[1]
+    _check_packed_in(values, meta, n_out, n_in, X.dtype, X.device)
+    if need_v:
+        r = _check_factors(U, V, n_out, n_in, X.dtype, X.device)
+    else:
+        r = 0 if U is None else (U.shape[1] if U.dim() == 2 else -1)
+        if U is not None:
+            _expect(U, "U", X.dtype, n_out * max(r, 0), X.device, (n_out, r))
     if out is None:
-        out = torch.empty((M, n_out), dtype=torch.float32, device=X.device)
+        with torch.cuda.stream(_the_stream(stream)):
+            out = torch.empty((M, n_out), dtype=y_dtype, device=X.device)
     if workspace is None and with_workspace:
-        workspace = new_workspace(M, n_out, n_in, r, X.dtype, X.device)
+        workspace = new_workspace(M, n_out, n_in, r, X.dtype, X.device, stream)
+    _expect(out, "out", y_dtype, M * n_out, X.device, (M, n_out))
+    if workspace is not None:
+        if not _is_device(workspace) or workspace.device != X.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of X")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return M, n_in, n_out, r, out, workspace, ws_bytes
 
@@ -210,7 +285,7 @@ def linear(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optiona
            V: Optional[torch.Tensor], n_out: Optional[int] = None, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Y [M, n_out] float32 = X S^T + (X V^T) U^T (n_out defaults to U's rows, else 16 * TR)."""
-    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, U, n_out, out, workspace)
+    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, meta, U, V, n_out, out, workspace, stream)
     _check("splr_linear", lib().splr_linear(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
                                             _dev(U, "U"), _dev(V, "V"), r, _dtype_code(X), _dev(out, "out"),
                                             _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
@@ -225,14 +300,8 @@ def linear_ex(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Opti
     even)."""
     if y_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"y_dtype must be float32 or bfloat16, got {y_dtype}")
-    M = X.shape[0]
-    if n_out is None:
-        n_out = U.shape[0] if U is not None else values.shape[0] * 16
-    if out is None:
-        out = torch.empty((M, n_out), dtype=y_dtype, device=X.device)
-    if out.dtype != y_dtype:
-        raise ValueError(f"out is {out.dtype}, expected {y_dtype}")
-    M, n_in, n_out, r, _, workspace, ws_bytes = _linear_args(X, values, U, n_out, out, workspace)
+    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, meta, U, V, n_out, out, workspace, stream,
+                                                               y_dtype=y_dtype)
     ycode = SPLR_BF16 if y_dtype == torch.bfloat16 else SPLR_FP32
     _check("splr_linear_ex", lib().splr_linear_ex(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"),
                                                   n_out, _dev(U, "U"), _dev(V, "V"), r, _dtype_code(X), ycode,
@@ -244,8 +313,15 @@ def linear_ex(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Opti
 def linear_stage1(X: torch.Tensor, V: Optional[torch.Tensor], workspace: torch.Tensor, n_out: int = 0,
                   stream=None) -> torch.Tensor:
     """First low-rank stage T = X V^T into `workspace` (sized by workspace_bytes); returns it."""
-    M, n_in = X.shape
-    r = 0 if V is None else V.shape[0]
+    M, n_in = _matrix(X, "X")
+    _dtype_code(X)
+    r = 0
+    if V is not None:
+        r = V.shape[0] if V.dim() == 2 else -1
+        _expect(V, "V", X.dtype, max(r, 0) * n_in, X.device, (r, n_in))
+    if workspace is not None and (not _is_device(workspace) or workspace.device != X.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the device of X")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("splr_linear_stage1", lib().splr_linear_stage1(_dev(X, "X"), M, n_in, _dev(V, "V"), r, _dtype_code(X),
                                                           _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
@@ -256,8 +332,8 @@ def linear_stage2(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: 
                   workspace: Optional[torch.Tensor], n_out: Optional[int] = None, out: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """Y = X S^T + T U^T with T left in `workspace` by linear_stage1 (same X and r)."""
-    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, U, n_out, out, workspace,
-                                                               with_workspace=False)
+    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, meta, U, None, n_out, out, workspace, stream,
+                                                               with_workspace=False, need_v=False)
     _check("splr_linear_stage2",
            lib().splr_linear_stage2(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
                                     _dev(U, "U"), r, _dtype_code(X), _dev(out, "out"), _dev(workspace, "workspace"),
@@ -269,13 +345,19 @@ def dense_reconstruct(values: torch.Tensor, meta: torch.Tensor, U: Optional[torc
                       V: Optional[torch.Tensor], n_out: Optional[int] = None, n_in: Optional[int] = None,
                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """W_hat [n_out, n_in] float32 = S + U V (sizes default to U / V's, else to the tile grid)."""
+    if not _is_device(values):
+        raise ValueError("values must be a device tensor")
     if n_out is None:
         n_out = U.shape[0] if U is not None else values.shape[0] * 16
     if n_in is None:
         n_in = V.shape[1] if V is not None else values.shape[1] * 64
-    r = 0 if U is None else U.shape[1]
+    _dtype_code(values)
+    _check_packed_in(values, meta, n_out, n_in, values.dtype, values.device)
+    r = _check_factors(U, V, n_out, n_in, values.dtype, values.device)
     if out is None:
-        out = torch.empty((n_out, n_in), dtype=torch.float32, device=values.device)
+        with torch.cuda.stream(_the_stream(stream)):
+            out = torch.empty((n_out, n_in), dtype=torch.float32, device=values.device)
+    _expect(out, "out", torch.float32, n_out * n_in, values.device, (n_out, n_in))
     _check("splr_dense_reconstruct",
            lib().splr_dense_reconstruct(_dev(values, "values"), _dev(meta, "meta"), _dev(U, "U"), _dev(V, "V"),
                                         n_out, n_in, r, _dtype_code(values), _dev(out, "out"), _stream(stream)))

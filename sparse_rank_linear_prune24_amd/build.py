@@ -9,6 +9,7 @@ the feature; that warning is harmless).
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -30,9 +31,27 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def source_files():
+    """Every file the library is built from: the HIP sources, their headers and the public header."""
+    names = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
+    return [os.path.join(CSRC, f) for f in names] + [os.path.join(INCLUDE, "splr.h")]
+
+
+def source_hash() -> str:
+    """First 16 hex digits of the SHA-256 over the sources (name and contents, in name order); the
+    build embeds it in splr_version()."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, defines=()) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -42,8 +61,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 4)), 16)
+    defines = [f'-DSPLR_SOURCE_SHA="{source_hash()}"']
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, defines), SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

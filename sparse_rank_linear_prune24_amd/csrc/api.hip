@@ -50,6 +50,7 @@ splr_status_t splr_prune24_pack(const void* R, int64_t n_out, int64_t n_in, splr
   if (s == SPLR_OK) s = check_rows(n_out, n_in);
   if (s != SPLR_OK) return s;
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!splr::pack_grids_fit(n_out, n_in, dtype == SPLR_BF16)) return SPLR_ERR_SHAPE;
   if (!aligned16(R) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
   return from_hip(splr::launch_prune24_pack(R, n_out, n_in, dtype == SPLR_BF16, values, meta, stream));
 }
@@ -62,6 +63,7 @@ splr_status_t splr_prune_nm_pack(const void* R, int64_t n_out, int64_t n_in, int
   if (s == SPLR_OK && !((n == 1 || n == 2) && (m == 4 || m == 8 || m == 16))) s = SPLR_ERR_SHAPE;
   if (s != SPLR_OK) return s;  // n_in % 32 == 0, so every m above divides n_in
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!splr::pack_grids_fit(n_out, n_in, dtype == SPLR_BF16)) return SPLR_ERR_SHAPE;
   if (!aligned16(R) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
   return from_hip(splr::launch_prune_nm_pack(R, n_out, n_in, n, m, dtype == SPLR_BF16, values, meta, stream));
 }
@@ -76,6 +78,7 @@ splr_status_t splr_prune24_pack_residual(const void* W, const void* U, const voi
   if (s == SPLR_OK && (r < 0 || r > kMaxRank)) s = SPLR_ERR_SHAPE;
   if (s != SPLR_OK) return s;
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!splr::residual_grids_fit(n_out, n_in)) return SPLR_ERR_SHAPE;
   if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
   if (r > 0 && (!aligned16(U) || !aligned16(V))) return SPLR_ERR_ALIGN;
   return from_hip(
@@ -89,6 +92,7 @@ splr_status_t splr_prune24_pack_scaled(const void* R, const float* d, int64_t n_
   if (s == SPLR_OK) s = check_rows(n_out, n_in);
   if (s != SPLR_OK) return s;
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!splr::pack_grids_fit(n_out, n_in, dtype == SPLR_BF16)) return SPLR_ERR_SHAPE;
   if (!aligned16(R) || !aligned16(d) || !aligned16(values) || !aligned16(meta)) return SPLR_ERR_ALIGN;
   return from_hip(
       splr::launch_prune24_pack_scaled(R, d, n_out, n_in, dtype == SPLR_BF16, values, meta, stream));
@@ -129,6 +133,10 @@ splr_status_t check_linear(const void* X, int64_t M, int64_t n_in, const void* v
   if (s == SPLR_OK && need_sparse && M * n_out > kMaxElems) s = SPLR_ERR_SHAPE;
   if (s != SPLR_OK) return s;
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  // every launch of the call fits the dispatch limits (stage 2 only when it runs)
+  if (need_sparse ? !splr::linear_grids_fit(M, n_in, n_out, r, dtype == SPLR_BF16)
+                  : !splr::lowrank_grids_fit(M, n_in, r, dtype == SPLR_BF16))
+    return SPLR_ERR_SHAPE;
   if (!aligned16(X)) return SPLR_ERR_ALIGN;
   if (need_sparse && (!aligned16(values) || !aligned16(meta) || !aligned16(Y) || (r > 0 && !aligned16(U))))
     return SPLR_ERR_ALIGN;
@@ -201,6 +209,7 @@ splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, c
   if (s == SPLR_OK) s = check_rank(r);
   if (s != SPLR_OK) return s;
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
+  if (!splr::reconstruct_grids_fit(n_out, n_in)) return SPLR_ERR_SHAPE;
   if (!aligned16(values) || !aligned16(meta) || !aligned16(W_hat)) return SPLR_ERR_ALIGN;
   if (r > 0 && (!aligned16(U) || !aligned16(V))) return SPLR_ERR_ALIGN;
   return from_hip(splr::launch_dense_reconstruct(values, meta, U, V, n_out, n_in, r, dtype == SPLR_BF16, W_hat,
@@ -220,6 +229,11 @@ const char* splr_status_string(splr_status_t status) {
   return "SPLR_ERR_UNKNOWN";
 }
 
-const char* splr_version(void) { return "0.1.0"; }
+// The library version, followed by the first 16 hex digits of the SHA-256 of the sources it was
+// built from (the build passes it in), so a loaded binary can be matched to a source tree.
+#ifndef SPLR_SOURCE_SHA
+#define SPLR_SOURCE_SHA "unknown"
+#endif
+const char* splr_version(void) { return "0.2.0+" SPLR_SOURCE_SHA; }
 
 }  // extern "C"

@@ -7,6 +7,21 @@
 
 namespace splr {
 
+// Dispatch limits of one launch (HIP on gfx9): fewer than 2^32 work-items along x, at most 65535
+// workgroups along y and z. Every entry point checks the grids of all the launches it will make
+// against these limits before its first HIP call (the *_grids_fit functions below compute those
+// grids exactly as the launchers do).
+inline bool grid_fits(dim3 g, unsigned threads) {
+  return g.x >= 1 && g.y >= 1 && g.z >= 1 && (uint64_t)g.x * threads < (uint64_t(1) << 32) && g.y <= 65535u &&
+         g.z <= 65535u;
+}
+bool pack_grids_fit(int64_t n_out, int64_t n_in, bool bf16);
+bool residual_grids_fit(int64_t n_out, int64_t n_in);
+bool lowrank_grids_fit(int64_t M, int64_t n_in, int64_t r, bool bf16);
+bool linear_grids_fit(int64_t M, int64_t n_in, int64_t n_out, int64_t r, bool bf16);
+bool reconstruct_grids_fit(int64_t n_out, int64_t n_in);
+dim3 linear_f32_grid(int64_t M, int64_t n_out);
+
 hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
                                uint32_t* meta, hipStream_t stream);
 // Fused residual R = W - U V (pinned binary32 fused multiply-add order, then rounding) + pack.

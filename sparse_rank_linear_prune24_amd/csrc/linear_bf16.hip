@@ -701,19 +701,36 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
   if (wave == 0) store_tile<1, MB>(acc, Y, y_bf16, M, n_out, tr * 16, m0, lane);
 }
 
+dim3 decode_grid(int64_t M, int64_t n_out, int MB) {
+  return dim3((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(M, 16 * MB));
+}
+
 template <int MB>
 hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                          int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
                          int y_bf16, hipStream_t stream) {
   constexpr int P = MB == 1 ? 8 : 4, W = 4;
-  dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(M, 16 * MB));
+  const dim3 grid = decode_grid(M, n_out, MB);
   linear_decode_kernel<MB, P, W><<<grid, dim3(64 * W), 0, stream>>>(
       (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, y_bf16, (int)M,
       (int)n_in, (int)n_out, (int)r);
   return hipGetLastError();
 }
 
+// prefill: one workgroup per 256-row x 128-token tile, tiles dealt to the 8 XCDs in equal ranges
+dim3 prefill_grid(int64_t M, int64_t n_out) {
+  const int64_t n_tiles = ceil_div(n_out, 256) * ceil_div(M, 128);
+  return dim3((unsigned)(8 * ceil_div(n_tiles, 8)));
+}
+
 }  // namespace
+
+bool linear_grids_fit(int64_t M, int64_t n_in, int64_t n_out, int64_t r, bool bf16) {
+  if (!lowrank_grids_fit(M, n_in, r, bf16)) return false;
+  if (!bf16) return grid_fits(linear_f32_grid(M, n_out), 256);
+  if (M <= kDecodeMaxTokens) return grid_fits(decode_grid(M, n_out, M <= 16 ? 1 : (M <= 32 ? 2 : 4)), 256);
+  return grid_fits(prefill_grid(M, n_out), 256);
+}
 
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                               int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
@@ -728,7 +745,8 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   constexpr int BN = 16 * NI * 4, BM = 16 * NJ;
   const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
   const int n_tiles = tiles_n * tiles_m;
-  const int per_xcd = (int)ceil_div(n_tiles, 8);
+  const dim3 grid = prefill_grid(M, n_out);
+  const int per_xcd = (int)grid.x / 8;
   const int group_m = 4;
   // When every tile runs at once (one workgroup per CU), the Y stores of all tiles come at the end
   // together and are exposed: the row-contiguous epilogue stores them faster. With several tiles per
@@ -739,7 +757,7 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   // 4096/8192 tokens x 14336 outputs; +5 % slower on 8192 x 4096, 134 MB, so the threshold sits
   // between).
   const bool y_nt = (double)M * n_out * (y_bf16 ? 2 : 4) > kNonTemporalYBytes;
-  const dim3 grid((unsigned)(8 * per_xcd)), block(256);
+  const dim3 block(256);
   if (n_tiles <= kRowsEpilogueMaxTiles && r <= 64)
     linear_prefill_kernel<NI, NJ, P, PX, kEpiRows><<<grid, block, 0, stream>>>(
         (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,

@@ -166,7 +166,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Tile kernel for many tokens: a workgroup owns BM = 16*TMW*WM tokens x BR = 16*TRW*WR ranks over
-// one K slice (grid: rank blocks, token blocks, K slices), so that X is read from memory once when
+// one K slice (grid: x = token block * rank_blocks + rank block, z = K slice), so that X is read
+// from memory once when
 // BR covers r. Per 64-column K step the four waves stage the step's X rows into one slot of a
 // two-slot LDS ring (row-contiguous 16-byte loads, one barrier per step) and wave w computes its
 // 16*TMW tokens x 16*TRW ranks: X fragments come from the slot, V fragments (small, L2-resident)
@@ -176,7 +177,8 @@ __device__ __forceinline__ void lds_barrier() {
 template <int TMW, int TRW, int WM, int WR, int P>
 __global__ __launch_bounds__(256) void lowrank_tile_kernel(const uint16_t* __restrict__ X,
                                                           const uint16_t* __restrict__ V, int M, int K, int r,
-                                                          int steps_per_slice, float* __restrict__ part) {
+                                                          int rank_blocks, int steps_per_slice,
+                                                          float* __restrict__ part) {
   static_assert(WM * WR == 4, "four waves");
   constexpr int BM = 16 * TMW * WM, BR = 16 * TRW * WR;
   constexpr int kChunks = BM * 8;                  // 16-byte chunks of X per step
@@ -185,7 +187,8 @@ __global__ __launch_bounds__(256) void lowrank_tile_kernel(const uint16_t* __res
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane & 15, quad = lane >> 4;
   const int wm = wave % WM, wr = wave / WM;
-  const int j0 = blockIdx.x * BR, m0 = blockIdx.y * BM;
+  const int mb = blockIdx.x / rank_blocks;
+  const int j0 = (blockIdx.x - mb * rank_blocks) * BR, m0 = mb * BM;
   const int TK = (K + 63) / 64;
   const int kb = blockIdx.z * steps_per_slice;
   const int n_steps = min(TK, kb + steps_per_slice) - kb;  // >= 1 by the choice of slices
@@ -299,19 +302,21 @@ __global__ __launch_bounds__(256) void lowrank_tile_kernel(const uint16_t* __res
   }
 }
 
+// One wave per output T[m][j] (outputs numbered m * r + j, 64-bit); the grid strides over them.
 __global__ __launch_bounds__(256) void lowrank_f32_kernel(const float* __restrict__ X, const float* __restrict__ V,
                                                          int M, int K, int r, float* __restrict__ T) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wave >= M * r) return;
-  const int m = wave / r, j = wave % r;
-  const float* x = X + (size_t)m * K;
-  const float* v = V + (size_t)j * K;
-  float t = 0.0f;
-  for (int k = lane; k < K; k += 64) t = fmaf(x[k], v[k], t);
+  const int64_t outputs = (int64_t)M * r;
+  for (int64_t o = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); o < outputs; o += (int64_t)gridDim.x * 4) {
+    const int64_t m = o / r, j = o - m * r;
+    const float* x = X + (size_t)m * K;
+    const float* v = V + (size_t)j * K;
+    float t = 0.0f;
+    for (int k = lane; k < K; k += 64) t = fmaf(x[k], v[k], t);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
-  if (lane == 0) T[(size_t)m * r + j] = t;
+    for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+    if (lane == 0) T[o] = t;
+  }
 }
 
 }  // namespace
@@ -360,10 +365,19 @@ LowrankShape lowrank_shape(int64_t M, int64_t n_in, int64_t r) {
   return sh;
 }
 
+dim3 part_grid(const LowrankShape& sh, int64_t M, int64_t r) {
+  return dim3((unsigned)cdiv(M, 16 * sh.tf), (unsigned)(r / (16 * sh.rf)), (unsigned)sh.slices);
+}
+dim3 tile_grid(const LowrankShape& sh, int64_t M, int64_t r) {
+  return dim3((unsigned)(ceil_div(r, 128) * ceil_div(M, sh.bm)), 1u, (unsigned)sh.slices);
+}
+constexpr int64_t kMaxF32Blocks = int64_t(1) << 20;
+dim3 f32_grid(int64_t M, int64_t r) { return dim3((unsigned)std::min(ceil_div(M * r, 4), kMaxF32Blocks)); }
+
 template <int TF, int RF>
 void launch_part(const LowrankShape& sh, const void* X, const void* V, int64_t M, int64_t n_in, int64_t r,
                  float* part, hipStream_t stream) {
-  dim3 grid((unsigned)cdiv(M, 16 * TF), (unsigned)(r / (16 * RF)), (unsigned)sh.slices);
+  const dim3 grid = part_grid(sh, M, r);
   if (sh.steps_per_slice >= 16)
     lowrank_bf16_kernel<TF, RF, 4, 4><<<grid, dim3(256), 0, stream>>>((const uint16_t*)X, (const uint16_t*)V, (int)M,
                                                                     (int)n_in, (int)r, sh.steps_per_slice, part);
@@ -375,12 +389,19 @@ void launch_part(const LowrankShape& sh, const void* X, const void* V, int64_t M
 template <int TMW>
 void launch_tile(const LowrankShape& sh, const void* X, const void* V, int64_t M, int64_t n_in, int64_t r,
                  float* part, hipStream_t stream) {
-  dim3 grid((unsigned)cdiv(r, 128), (unsigned)cdiv(M, 16 * TMW), (unsigned)sh.slices);
+  const dim3 grid = tile_grid(sh, M, r);
   lowrank_tile_kernel<TMW, 2, 1, 4, 4><<<grid, dim3(256), 0, stream>>>(
-      (const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in, (int)r, sh.steps_per_slice, part);
+      (const uint16_t*)X, (const uint16_t*)V, (int)M, (int)n_in, (int)r, cdiv(r, 128), sh.steps_per_slice, part);
 }
 
 }  // namespace
+
+bool lowrank_grids_fit(int64_t M, int64_t n_in, int64_t r, bool bf16) {
+  if (r == 0) return true;
+  if (!bf16) return grid_fits(f32_grid(M, r), 256);
+  const LowrankShape sh = lowrank_shape(M, n_in, r);
+  return grid_fits(sh.tile ? tile_grid(sh, M, r) : part_grid(sh, M, r), 256);
+}
 
 int lowrank_slices(int64_t M, int64_t n_in, int64_t r, bool bf16) {
   return (r == 0 || !bf16) ? 1 : lowrank_shape(M, n_in, r).slices;
@@ -409,8 +430,7 @@ hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in,
       launch_tile<4>(sh, X, V, M, n_in, r, part, stream);
     }
   } else {
-    const int64_t waves = M * r;
-    lowrank_f32_kernel<<<dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, stream>>>(
+    lowrank_f32_kernel<<<f32_grid(M, r), dim3(256), 0, stream>>>(
         (const float*)X, (const float*)V, (int)M, (int)n_in, (int)r, part);
   }
   return hipGetLastError();

@@ -244,13 +244,17 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   if (tid < n_tiles * 8) ((u32x4_t*)meta)[t0 * 8 + tid] = ((const u32x4_t*)sm)[tid];
 }
 
+dim3 pack_grid(int64_t n_out, int64_t n_in, bool bf16) {
+  const int cols = 16 * kPackChunksPerThread * (bf16 ? 8 : 4);
+  return dim3((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(n_in, cols));
+}
+
 template <bool SCALED, int NM = 0>
 hipError_t launch_pack(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16, void* values,
                        uint32_t* meta, hipStream_t stream, int n_keep = 2) {
   constexpr int CPT = kPackChunksPerThread;
   const int TK = (int)ceil_div(n_in, 64);
-  const int cols = 16 * CPT * (bf16 ? 8 : 4);
-  dim3 grid((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(n_in, cols));
+  const dim3 grid = pack_grid(n_out, n_in, bf16);
   if (bf16)
     prune24_pack_kernel<true, SCALED, CPT, NM><<<grid, dim3(kPackThreads), 0, stream>>>(
         (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta, n_keep);
@@ -261,6 +265,10 @@ hipError_t launch_pack(const void* R, const float* d, int64_t n_out, int64_t n_i
 }
 
 }  // namespace
+
+bool pack_grids_fit(int64_t n_out, int64_t n_in, bool bf16) {
+  return grid_fits(pack_grid(n_out, n_in, bf16), kPackThreads);
+}
 
 hipError_t launch_prune24_pack(const void* R, int64_t n_out, int64_t n_in, bool bf16, void* values,
                                uint32_t* meta, hipStream_t stream) {

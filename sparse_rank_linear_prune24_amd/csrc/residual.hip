@@ -81,12 +81,13 @@ __device__ __forceinline__ void fma_tail(float (&acc)[CPL][16], const float (&v)
   }
 }
 
-// Grid (tile-column blocks of kResWaves * CPL tiles, tile rows). Lane l of wave w owns column l of
-// tiles (blockIdx.x * kResWaves + w) * CPL + s, s < CPL.
+// One-dimensional grid of tile rows x blocks of kResWaves * CPL tile columns, the column block
+// varying fastest (workgroup b: column block b % col_blocks of tile row b / col_blocks). Lane l of
+// wave w owns column l of tiles (column block * kResWaves + w) * CPL + s, s < CPL.
 template <bool BF16, int CPL>
 __global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
     const void* __restrict__ W, const void* __restrict__ U, const void* __restrict__ V, int n_out, int K, int r,
-    int TK, u32x4_t* __restrict__ values, uint32_t* __restrict__ meta) {
+    int TK, int col_blocks, u32x4_t* __restrict__ values, uint32_t* __restrict__ meta) {
   constexpr int kTileU32 = BF16 ? 256 : 512;  // one packed tile's values in 32-bit words
   __shared__ f32x4_t us[16 * kRJ / 4];        // U rows of the tile row, one rank block, float32
   __shared__ uint32_t img[kResWaves][kTileU32];
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
   __shared__ __align__(16) uint32_t ebuf[kResWaves][16 * 64];  // rounded rows of a tile (storage bits)
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tk0 = (blockIdx.x * kResWaves + wave) * CPL;  // this wave's first tile column
-  const int tr = blockIdx.y;
+  const int tr = blockIdx.x / col_blocks;
+  const int tk0 = ((blockIdx.x - tr * col_blocks) * kResWaves + wave) * CPL;  // this wave's first tile column
   const size_t esz = BF16 ? 2 : 4;
   bool col_ok[CPL];
   int cc[CPL];
@@ -193,17 +194,28 @@ __global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
 
 }  // namespace
 
+namespace {
+int residual_col_blocks(int64_t n_in) { return (int)ceil_div(ceil_div(n_in, 64), kResWaves * kResColsPerLane); }
+dim3 residual_grid(int64_t n_out, int64_t n_in) {
+  return dim3((unsigned)(ceil_div(n_out, 16) * residual_col_blocks(n_in)));
+}
+}  // namespace
+
+bool residual_grids_fit(int64_t n_out, int64_t n_in) {
+  return grid_fits(residual_grid(n_out, n_in), 64 * kResWaves);
+}
+
 hipError_t launch_prune24_pack_residual(const void* W, const void* U, const void* V, int64_t n_out, int64_t n_in,
                                         int64_t r, bool bf16, void* values, uint32_t* meta, hipStream_t stream) {
   constexpr int CPL = kResColsPerLane;
-  const int TK = (int)ceil_div(n_in, 64), TR = (int)ceil_div(n_out, 16);
-  dim3 grid((unsigned)ceil_div(TK, kResWaves * CPL), (unsigned)TR);
+  const int TK = (int)ceil_div(n_in, 64), cb = residual_col_blocks(n_in);
+  const dim3 grid = residual_grid(n_out, n_in);
   if (bf16)
     residual_pack_kernel<true, CPL><<<grid, dim3(64 * kResWaves), 0, stream>>>(W, U, V, (int)n_out, (int)n_in, (int)r,
-                                                                              TK, (u32x4_t*)values, meta);
+                                                                              TK, cb, (u32x4_t*)values, meta);
   else
     residual_pack_kernel<false, CPL><<<grid, dim3(64 * kResWaves), 0, stream>>>(W, U, V, (int)n_out, (int)n_in,
-                                                                               (int)r, TK, (u32x4_t*)values, meta);
+                                                                               (int)r, TK, cb, (u32x4_t*)values, meta);
   return hipGetLastError();
 }
 

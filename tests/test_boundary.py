@@ -185,3 +185,37 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         binding.prune24_pack(torch.zeros((4, 64), dtype=torch.bfloat16))
+
+
+def test_version_names_the_sources():
+    """splr_version() carries the hash of the sources the library was built from."""
+    from sparse_rank_linear_prune24_amd import build
+    assert binding.version() == "0.2.0+" + build.source_hash()
+
+
+NO_GPU = not os.path.exists("/dev/kfd")
+
+
+@pytest.mark.skipif(not NO_GPU, reason="reaches a kernel launch with placeholder pointers: only without a GPU")
+def test_largest_sizes_pass_validation():
+    """The largest sizes the ABI accepts pass every check, including the dispatch limits of each
+    launch (grids of up to 2^24 rows or tokens): with no GPU present the call then fails at the
+    launch (SPLR_ERR_HIP), not in validation. One step beyond a limit is SPLR_ERR_SHAPE."""
+    lib = binding.lib()
+    rows, cols = 1 << 24, 4096              # rows * cols = 2^36 elements, the largest matrix
+    big = 1 << 40
+    for dt in (0, 1):
+        assert lib.splr_prune24_pack(A, rows, cols, dt, A, A, None) == HIP
+        assert lib.splr_prune24_pack(A, rows + 1, cols, dt, A, A, None) == SHAPE
+        assert lib.splr_prune24_pack(A, rows, cols + 32, dt, A, A, None) == SHAPE
+        assert lib.splr_prune24_pack_scaled(A, A, rows, cols, dt, A, A, None) == HIP
+        assert lib.splr_prune_nm_pack(A, rows, cols, 2, 8, dt, A, A, None) == HIP
+        assert lib.splr_prune24_pack_residual(A, A, A, rows, cols, 1024, dt, A, A, None) == HIP
+        assert lib.splr_dense_reconstruct(A, A, A, A, rows, cols, 1024, dt, A, None) == HIP
+        assert lib.splr_dense_reconstruct(A, A, A, A, rows, cols + 32, 1024, dt, A, None) == SHAPE
+        # tokens x outputs = 2^36, rank 1024 (float32: M * r = 2^34 first-stage outputs)
+        for M, n_out in ((rows, cols), (cols, rows), (16, rows), (64, rows)):
+            assert lib.splr_linear(A, M, cols, A, A, n_out, A, A, 1024, dt, A, A, big, None) == HIP, (dt, M, n_out)
+            assert lib.splr_linear_stage1(A, M, cols, A, 1024, dt, A, big, None) == HIP
+            assert lib.splr_linear_stage2(A, M, cols, A, A, n_out, A, 1024, dt, A, A, big, None) == HIP
+        assert lib.splr_linear(A, rows, cols, A, A, cols + 16, A, A, 1024, dt, A, A, big, None) == SHAPE
