@@ -21,7 +21,7 @@ this library's kernels.
 from __future__ import annotations
 
 import time
-from typing import Dict, List, Optional
+from typing import Callable, Dict, List, Optional
 
 import numpy as np
 import torch
@@ -78,12 +78,15 @@ def _low_rank(Z: torch.Tensor, r: int, basis: Optional[torch.Tensor], power_iter
 
 def alternating_minimization(W: torch.Tensor, r: int, iters: int, *, power_iters: int = 2, start_iters: int = 6,
                              oversample: int = 16, seed: int = 0, X: Optional[torch.Tensor] = None,
-                             track: bool = True) -> Dict:
+                             track: bool = True, on_step: Optional[Callable[[Dict], None]] = None) -> Dict:
     """Run `iters` steps on W [n_out, n_in] (bfloat16 or float32, on the GPU).
 
     Returns dict(values, meta, U, V, objective, layer_rel_error, seconds): the packed S and factors
     after the last step; objective[t] = ||W - S_t - U_t V_t||_F after step t (when `track`); with
-    activations X [M, n_in], layer_rel_error[t] = ||X W^T - splr_linear(X)||_F / ||X W^T||_F."""
+    activations X [M, n_in], layer_rel_error[t] = ||X W^T - splr_linear(X)||_F / ||X W^T||_F.
+    `on_step`, if given, is called after every step with dict(step, U_in, V_in: the stored factors
+    the projection used; values, meta: the packed S it produced; U32, V32: the float32 factors of
+    the low-rank step, before rounding to storage) -- device tensors, valid during the call."""
     n_out, n_in = W.shape
     dtype = W.dtype
     gen = torch.Generator(device=W.device)
@@ -99,13 +102,17 @@ def alternating_minimization(W: torch.Tensor, r: int, iters: int, *, power_iters
     layer_err: List[float] = []
     ref = X.float() @ W32.T if X is not None else None
     values = meta = None
-    for _ in range(iters):
+    for step in range(iters):
+        U_in, V_in = U, V
         values, meta = binding.prune24_pack_residual(W, U, V, values, meta)
         S = binding.dense_reconstruct(values, meta, None, None, n_out=n_out, n_in=n_in)
         Z = W32 - S
         if r > 0:
             U32, V32, basis = _low_rank(Z, r, basis, power_iters, oversample, gen)
             U, V = U32.to(dtype).contiguous(), V32.to(dtype).contiguous()
+        if on_step is not None:
+            on_step(dict(step=step, U_in=U_in, V_in=V_in, values=values, meta=meta,
+                         U32=U32 if r > 0 else None, V32=V32 if r > 0 else None))
         if track:
             L = U.float() @ V.float() if r > 0 else 0.0
             objective.append(float(torch.linalg.norm(Z - L)))

@@ -12,7 +12,7 @@ import torch
 import oracle
 import oracle.am as oam
 from sparse_rank_linear_prune24_amd import am, binding, inputs
-from tests._helpers import to_dev
+from tests._helpers import from_dev, meta_from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -57,3 +57,65 @@ def test_layer_error_tracked():
     res = am.alternating_minimization(to_dev(W, "bf16"), r, 6, X=to_dev(X, "bf16"))
     err = res["layer_rel_error"]
     assert len(err) == 6 and all(np.isfinite(err)) and err[-1] < err[0] and err[-1] < 0.5
+
+
+def _record_steps(W, dtype, r, iters, power_iters):
+    """Run the GPU loop and keep host copies of every step's inputs and outputs."""
+    steps = []
+
+    def keep(st):
+        steps.append(dict(U_in=None if st["U_in"] is None else from_dev(st["U_in"], dtype),
+                          V_in=None if st["V_in"] is None else from_dev(st["V_in"], dtype),
+                          values=from_dev(st["values"], dtype), meta=meta_from_dev(st["meta"]),
+                          U32=None if st["U32"] is None else st["U32"].double().cpu().numpy(),
+                          V32=None if st["V32"] is None else st["V32"].double().cpu().numpy()))
+
+    am.alternating_minimization(to_dev(W, dtype), r, iters, power_iters=power_iters, track=False, on_step=keep)
+    return steps
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_projection_steps_bit_exact(dtype):
+    """Every sparse step of the GPU loop (HASSLE-free page, §4.1.1: hard thresholding of W - U V
+    onto the 2:4 set) equals the oracle's projection of the same stored factors, bit for bit."""
+    n_out, n_in, r, iters = 256, 512, 16, 6
+    print(f"[am projection] dtype={dtype} {n_out}x{n_in} r={r} iters={iters}", flush=True)
+    W = weight(n_out, n_in, r, dtype, seed=4)
+    steps = _record_steps(W, dtype, r, iters, power_iters=2)
+    assert len(steps) == iters
+    for t, st in enumerate(steps):
+        v_ref, m_ref = oracle.prune24_pack_residual(W, st["U_in"], st["V_in"], dtype)
+        bits = np.uint32 if dtype == "fp32" else np.uint16
+        assert np.array_equal(st["meta"], m_ref), f"step {t}: metadata differs"
+        assert np.array_equal(st["values"].view(bits), v_ref.view(bits)), f"step {t}: values differ"
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_low_rank_steps_match_truncated_svd(dtype):
+    """Every low-rank step of the GPU loop against the exact rank-r truncated SVD C_r(Z) of the same
+    Z = W - S_t (HASSLE-free page, §4.2.1; C_r is the best rank-r approximation, §3), Z formed in
+    float64 from the stored W and the GPU's S.
+
+    Bound: the GPU works in float32, which amounts to taking C_r of a perturbed Z + E with
+    ||E||_2 <= sqrt(n_in) * 2^-24 * sigma_1 (float32 rounding of sums over n_in terms). The best
+    rank-r approximation moves by at most ||E||_2 (1 + 2 sigma_1 / (sigma_r - sigma_(r+1))) under
+    such a perturbation (Weyl for the kept values, Wedin's sin-theta bound for the singular
+    subspaces, both scaled by sigma_1), so ||U V - C_r(Z)||_2 must stay below that. With 4 power
+    iterations per step the subspace iteration's own truncation error is far below it on this
+    weight (its rank-r head is separated: sigma_r / sigma_(r+1) > 3). Dropping one singular
+    component costs sigma_r, about 10^5 times the bound."""
+    n_out, n_in, r, iters = 256, 512, 16, 6
+    print(f"[am low rank] dtype={dtype} {n_out}x{n_in} r={r} iters={iters}", flush=True)
+    W = weight(n_out, n_in, r, dtype, seed=1)
+    w = inputs.to_f64(W, dtype)
+    steps = _record_steps(W, dtype, r, iters, power_iters=4)
+    for t, st in enumerate(steps):
+        Z = w - oam.dense_sparse(st["values"], st["meta"], n_out, n_in, dtype)
+        u, s, vt = np.linalg.svd(Z, full_matrices=False)
+        C_r = (u[:, :r] * s[:r]) @ vt[:r]
+        bound = (1 + 2 * s[0] / (s[r - 1] - s[r])) * np.sqrt(n_in) * 2.0 ** -24 * s[0]
+        err = np.linalg.norm(st["U32"] @ st["V32"] - C_r, 2)
+        print(f"[am low rank] step {t}: ||UV - C_r||_2 = {err:.2e}, bound {bound:.2e}, gap ratio "
+              f"{s[r - 1] / s[r]:.2f}", flush=True)
+        assert s[r - 1] / s[r] > 3
+        assert err <= bound, f"step {t}: {err:.3e} > {bound:.3e}"

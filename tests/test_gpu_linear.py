@@ -80,14 +80,30 @@ def test_named_full(cfg):
     check_layer(L, c.dtype, cfg)
 
 
+def sampled_rows(M, seed, tile=128):
+    """Token rows the oracle evaluates on a full-size layer: at least one row in every 128-token
+    tile of the prefill kernel (its position inside the tile varies from tile to tile, so every
+    16-token fragment row and every lane position is met), the edges of the first and last tiles,
+    and a few random rows. Every output column of a sampled row is compared."""
+    g = np.random.default_rng(seed)
+    per_tile = [t * tile + (37 * t + 5) % min(tile, M - t * tile) for t in range((M + tile - 1) // tile)]
+    edges = [0, 1, 15, 16, 127, 128, 255, M - 129, M - 128, M - 1]
+    return np.unique(np.clip(np.concatenate([per_tile, edges, g.integers(0, M, size=16)]), 0, M - 1))
+
+
+def test_sampled_rows_cover_every_tile():
+    rows = sampled_rows(8192, 5)
+    assert set(rows // 128) == set(range(64))
+    assert len(set(rows % 16)) == 16
+
+
 @pytest.mark.parametrize("cfg", ["C4", "C5"])
 def test_named_sampled_rows(cfg):
     """Full-size layers (the benchmark's launch configuration); the oracle evaluates sampled token
-    rows (first, last, tile edges and random ones), each compared element by element."""
+    rows (one or more in every 128-token tile, tile edges, random ones), each compared element by
+    element over all output columns."""
     c = configs.get(cfg)
-    g = np.random.default_rng(c.config_id)
-    rows = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, 255, c.M - 129, c.M - 1],
-                                     g.integers(0, c.M, size=23)]))
+    rows = sampled_rows(c.M, c.config_id)
     for li in range(len(c.layers)):
         L = inputs.make_layer(cfg, li)
         check_layer(L, c.dtype, f"{cfg}/{L.name}", rows=rows)
