@@ -12,7 +12,8 @@
  * -----------------------------------
  *  - Array arguments are DEVICE pointers (hipMalloc / torch CUDA tensors), row-major, contiguous,
  *    16-byte aligned.  The caller owns every buffer; the library never allocates or frees device
- *    memory.  Outputs must not alias inputs.
+ *    memory (its one buffer, splr_linear_noalloc's workspace, is a static device array, see
+ *    there).  Outputs must not alias inputs.
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns without waiting.
  *  - Arguments are validated before any HIP call: on a validation error nothing is enqueued and
  *    the error code is returned.  A failed launch returns SPLR_ERR_HIP.  No C++ exception crosses
@@ -58,7 +59,8 @@ typedef enum {
   SPLR_ERR_DTYPE = 3,     /* unknown splr_dtype_t                                               */
   SPLR_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                                   */
   SPLR_ERR_HIP = 5,       /* the HIP runtime reported an error while enqueueing                 */
-  SPLR_ERR_WORKSPACE = 6  /* workspace NULL or smaller than splr_linear_workspace_bytes()      */
+  SPLR_ERR_WORKSPACE = 6, /* workspace NULL or smaller than splr_linear_workspace_bytes()      */
+  SPLR_ERR_SCRATCH = 7    /* splr_linear_noalloc: the call needs more than its built-in buffer  */
 } splr_status_t;
 
 /*
@@ -229,6 +231,29 @@ splr_status_t splr_linear_stage2(const void* X, int64_t M, int64_t n_in, const v
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * splr_linear_noalloc -- splr_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, allocation-free serving loops, harnesses
+ * that forbid hipMalloc).  The first-stage workspace lives in a device array inside the library,
+ * SPLR_LINEAR_NOALLOC_MAX_WORKSPACE bytes on each GPU it runs on, held from the first call on that
+ * GPU until the process ends.  The call allocates nothing (no hipMalloc / hipFree, no allocating
+ * library routine); its first call on a GPU looks up that GPU's copy of the array.
+ *
+ *   Arguments and results: as splr_linear (same kernels, so Y is bit for bit splr_linear's).
+ *   Limit: splr_linear_workspace_bytes(M, n_out, n_in, r, dtype) must not exceed
+ *          SPLR_LINEAR_NOALLOC_MAX_WORKSPACE (e.g. 8192 tokens at rank 128 need 8 MiB).
+ *   Sharing: every call on one GPU uses that GPU's single array, which keeps the last call's
+ *          contents (nothing in it needs clearing: each call writes every byte it reads).  Calls
+ *          that overlap in time on one GPU (different streams or host threads) race on it; order
+ *          them on one stream or with events.
+ * Errors: as splr_linear, minus SPLR_ERR_WORKSPACE; workspace need above the limit ->
+ *         SPLR_ERR_SCRATCH (checked before any HIP call); a failed symbol lookup -> SPLR_ERR_HIP.
+ */
+#define SPLR_LINEAR_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+splr_status_t splr_linear_noalloc(const void* X, int64_t M, int64_t n_in, const void* values,
+                                  const uint32_t* meta, int64_t n_out, const void* U, const void* V,
+                                  int64_t r, splr_dtype_t dtype, float* Y, hipStream_t stream);
+
+/*
  * splr_dense_reconstruct -- W_hat = S + U V as a dense float32 matrix (LoSparse §3: the weight is
  * approximated by the sum of the sparse and the low-rank part).  A verification aid.
  *
@@ -244,7 +269,8 @@ splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, c
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* splr_status_string(splr_status_t status);
 
-/* Library version as "major.minor.patch" (static storage). */
+/* Library version as "major.minor.patch+<source hash>" (static storage): the first 16 hex digits of
+   the SHA-256 of the sources the library was built from. */
 const char* splr_version(void);
 
 #ifdef __cplusplus

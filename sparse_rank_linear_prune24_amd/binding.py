@@ -23,10 +23,10 @@ LIB_PATH = os.path.join(_PKG, "libsplr.so")
 
 SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
-          5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE"}
+          5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE", 7: "SPLR_ERR_SCRATCH"}
 EXPORTS = ("splr_prune24_pack", "splr_prune_nm_pack", "splr_linear_ex", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
-           "splr_linear_stage1", "splr_linear_stage2", "splr_dense_reconstruct", "splr_status_string",
-           "splr_version")
+           "splr_linear_stage1", "splr_linear_stage2", "splr_linear_noalloc", "splr_dense_reconstruct",
+           "splr_status_string", "splr_version")
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 _lib = None
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.splr_linear_stage1.restype = _I32
         L.splr_linear_stage2.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P]
         L.splr_linear_stage2.restype = _I32
+        L.splr_linear_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P]
+        L.splr_linear_noalloc.restype = _I32
         L.splr_dense_reconstruct.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]
         L.splr_dense_reconstruct.restype = _I32
         L.splr_status_string.argtypes = [_I32]
@@ -338,6 +340,20 @@ def linear_stage2(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: 
            lib().splr_linear_stage2(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
                                     _dev(U, "U"), r, _dtype_code(X), _dev(out, "out"), _dev(workspace, "workspace"),
                                     ws_bytes, _stream(stream)))
+    return out
+
+
+def linear_noalloc(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
+                   V: Optional[torch.Tensor], n_out: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """splr_linear with the library's built-in workspace (splr_linear_noalloc): nothing is allocated
+    when `out` is given. Calls on one GPU share that workspace, so they must not overlap in time."""
+    M, n_in, n_out, r, out, _, _ = _linear_args(X, values, meta, U, V, n_out, out, None, stream,
+                                                with_workspace=False)
+    _check("splr_linear_noalloc",
+           lib().splr_linear_noalloc(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
+                                     _dev(U, "U"), _dev(V, "V"), r, _dtype_code(X), _dev(out, "out"),
+                                     _stream(stream)))
     return out
 
 

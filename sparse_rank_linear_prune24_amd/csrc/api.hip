@@ -3,6 +3,8 @@
 // nothing; the library holds no mutable state and never allocates device memory.
 #include "splr.h"
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace {
@@ -119,10 +121,12 @@ size_t splr_linear_workspace_bytes(int64_t M, int64_t n_out, int64_t n_in, int64
 
 namespace {
 
-// Argument checks shared by splr_linear and its two stages. V is checked only when need_v.
+// Argument checks shared by splr_linear and its two stages. V is checked only when need_v, the
+// caller's workspace only when check_ws.
 splr_status_t check_linear(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                            int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, const void* Y,
-                           const void* workspace, size_t ws_bytes, bool need_sparse, bool need_v) {
+                           const void* workspace, size_t ws_bytes, bool need_sparse, bool need_v,
+                           bool check_ws = true) {
   if (!X) return SPLR_ERR_NULL;
   if (need_sparse && (!values || !meta || !Y || (r > 0 && !U))) return SPLR_ERR_NULL;
   if (need_v && r > 0 && !V) return SPLR_ERR_NULL;
@@ -141,6 +145,7 @@ splr_status_t check_linear(const void* X, int64_t M, int64_t n_in, const void* v
   if (need_sparse && (!aligned16(values) || !aligned16(meta) || !aligned16(Y) || (r > 0 && !aligned16(U))))
     return SPLR_ERR_ALIGN;
   if (need_v && r > 0 && !aligned16(V)) return SPLR_ERR_ALIGN;
+  if (!check_ws) return SPLR_OK;
   const size_t need = workspace_bytes(M, n_in, r, dtype);
   if (need > 0 && (!workspace || ws_bytes < need)) return SPLR_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return SPLR_ERR_ALIGN;
@@ -199,6 +204,61 @@ splr_status_t splr_linear_stage2(const void* X, int64_t M, int64_t n_in, const v
   return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, false, const_cast<void*>(workspace), stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- splr_linear_noalloc
+// For callers that cannot allocate: the first-stage workspace lives in a file-scope device array.
+// Each GPU the library runs on holds its own copy (from the first call on it until the process
+// ends), at its own address, found once per device with hipGetSymbolAddress. In host code the
+// array's name is only a stand-in for the symbol; kernels get the looked-up device address.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;  // SPLR_LINEAR_NOALLOC_MAX_WORKSPACE in splr.h
+static_assert(kScratchBytes == SPLR_LINEAR_NOALLOC_MAX_WORKSPACE, "header and library agree");
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's copy of `scratch`, looked up on the first call with that device current.
+hipError_t device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+splr_status_t splr_linear_noalloc(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                                  int64_t n_out, const void* U, const void* V, int64_t r, splr_dtype_t dtype, float* Y,
+                                  hipStream_t stream) {
+  const splr_status_t s =
+      check_linear(X, M, n_in, values, meta, n_out, U, V, r, dtype, Y, nullptr, 0, true, true, false);
+  if (s != SPLR_OK) return s;
+  const size_t need = workspace_bytes(M, n_in, r, dtype);
+  if (need > kScratchBytes) return SPLR_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && device_scratch(&ws) != hipSuccess) return SPLR_ERR_HIP;
+  // the same kernels as splr_linear; the workspace needs no clearing (every byte the second stage
+  // reads is written by the first stage of this call)
+  if (splr::launch_lowrank(X, V, M, n_in, r, dtype == SPLR_BF16, ws, stream) != hipSuccess) return SPLR_ERR_HIP;
+  return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, false, ws, stream);
+}
+
 splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, const void* U, const void* V,
                                      int64_t n_out, int64_t n_in, int64_t r, splr_dtype_t dtype, float* W_hat,
                                      hipStream_t stream) {
@@ -225,6 +285,8 @@ const char* splr_status_string(splr_status_t status) {
     case SPLR_ERR_ALIGN: return "SPLR_ERR_ALIGN: a pointer is not 16-byte aligned";
     case SPLR_ERR_HIP: return "SPLR_ERR_HIP: the HIP runtime reported an error";
     case SPLR_ERR_WORKSPACE: return "SPLR_ERR_WORKSPACE: workspace missing or too small";
+    case SPLR_ERR_SCRATCH:
+      return "SPLR_ERR_SCRATCH: the call needs more workspace than splr_linear_noalloc's built-in buffer holds";
   }
   return "SPLR_ERR_UNKNOWN";
 }

@@ -9,7 +9,7 @@ import pytest
 from sparse_rank_linear_prune24_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, DTYPE, ALIGN, HIP, WORKSPACE = range(7)
+OK, NULL, SHAPE, DTYPE, ALIGN, HIP, WORKSPACE, SCRATCH = range(8)
 A = 0x10000          # an aligned, never dereferenced address
 MIS = 0x10008        # misaligned
 
@@ -30,7 +30,7 @@ def test_exports_match_header():
 
 def test_status_strings():
     lib = binding.lib()
-    for code in range(7):
+    for code in range(8):
         assert lib.splr_status_string(code).decode().startswith(binding.STATUS[code])
     assert lib.splr_status_string(99) == b"SPLR_ERR_UNKNOWN"
 
@@ -219,3 +219,25 @@ def test_largest_sizes_pass_validation():
             assert lib.splr_linear_stage1(A, M, cols, A, 1024, dt, A, big, None) == HIP
             assert lib.splr_linear_stage2(A, M, cols, A, A, n_out, A, 1024, dt, A, A, big, None) == HIP
         assert lib.splr_linear(A, rows, cols, A, A, cols + 16, A, A, 1024, dt, A, A, big, None) == SHAPE
+
+
+def test_linear_noalloc_validation():
+    f = binding.lib().splr_linear_noalloc
+    args = dict(X=A, M=16, n_in=64, values=A, meta=A, n_out=32, U=A, V=A, r=16, dt=1, Y=A, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["X"], a["M"], a["n_in"], a["values"], a["meta"], a["n_out"], a["U"], a["V"], a["r"], a["dt"],
+                 a["Y"], a["stream"])
+
+    assert call(X=None) == NULL
+    assert call(V=None) == NULL
+    assert call(n_in=48) == SHAPE
+    assert call(r=8) == SHAPE
+    assert call(dt=4) == DTYPE
+    assert call(Y=MIS) == ALIGN
+    # the built-in workspace holds 32 MiB: 16384 tokens at rank 1024 need more (checked before any HIP call)
+    ws = binding.lib().splr_linear_workspace_bytes
+    assert ws(16384, 4096, 4096, 1024, 1) > 32 << 20 and ws(16384, 4096, 4096, 1024, 0) > 32 << 20
+    assert call(M=16384, n_in=4096, n_out=4096, r=1024) == SCRATCH
+    assert call(M=16384, n_in=4096, n_out=4096, r=1024, dt=0) == SCRATCH
