@@ -71,6 +71,7 @@ def parse():
                    help="C1..C5 (default: C5, the Llama-3-8B block linear set, 8192 tokens, rank 128)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     p.add_argument("--no-next", action="store_true", help="skip the measurements of the parts beyond the hot path")
+    p.add_argument("--no-context", action="store_true", help="skip the same-run reference points (profiling runs)")
     p.add_argument("--cpu-rows", type=int, default=0, help="token rows of the oracle sample (0 = auto)")
     p.add_argument("--graph", action="store_true", help="replay the steps from HIP graphs (for comparison)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -177,7 +178,7 @@ def main():
             s.append(dict(
                 R=to_dev(L.R), X=to_dev(L.X), U=to_dev(L.U), V=to_dev(L.V),
                 values=torch.empty((*binding.tiles(L.n_out, L.n_in), 64, 8), dtype=tdt, device=dev),
-                meta=torch.empty((*binding.tiles(L.n_out, L.n_in), 2, 16), dtype=torch.int32, device=dev),
+                meta=torch.empty(binding.meta_shape(L.n_out, L.n_in), dtype=torch.int32, device=dev),
                 Y=torch.empty((L.M, L.n_out), dtype=torch.float32, device=dev),
                 ws=torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)))
         sets.append(s)
@@ -349,7 +350,8 @@ def main():
         input_generation_s=round(gen_s, 1),
     )
 
-    out["context"] = measure_context(layers, decode, tdt, stream, dev, args)
+    if not args.no_context:
+        out["context"] = measure_context(layers, decode, tdt, stream, dev, args)
 
     if not args.no_next:
         out["next"] = measure_next(binding, inputs, layers, stream, dev, args, to_dev)
@@ -436,7 +438,7 @@ def measure_next(binding, inputs, layers, stream, dev, args, to_dev):
     R0, W0, X0, U0, V0 = to_dev(L.R), to_dev(L.W), to_dev(L.X), to_dev(L.U), to_dev(L.V)
     cp = [dict(R=R0.clone(), W=W0.clone(), X=X0.clone(), U=U0.clone(), V=V0.clone(),
                values=torch.empty((TR, TK, 64, 8), dtype=tdt, device=dev),
-               meta=torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=dev),
+               meta=torch.empty(binding.meta_shape(L.n_out, L.n_in), dtype=torch.int32, device=dev),
                ws=binding.new_workspace(L.M, L.n_out, L.n_in, L.r, tdt, dev, stream)) for _ in range(nc)]
     d = torch.from_numpy(inputs.column_scales(L.X, L.dtype)).to(dev)
 

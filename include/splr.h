@@ -31,9 +31,15 @@
  *  values: t-major, 64 slots of 8 entries per tile (TR*TK*512 entries of dtype). Row n, group g
  *          (columns 4g..4g+3): gi = g % 16, slot L = n % 16 + 16*(gi / 4); its two kept entries,
  *          in ascending column order, are entries 2*(gi % 4) and 2*(gi % 4)+1 of slot L.
- *  meta:   t-major, 2 x 16 uint32 words per tile (TR*TK*32 words). Word (gi / 8)*16 + n % 16
- *          of the tile holds the nibble (a | b << 2) of the group at bits 4*(gi % 8), where
- *          a < b in {0,1,2,3} are the kept positions. Valid nibbles: 0x4 0x8 0xC 0x9 0xD 0xE.
+ *  meta:   blocks of 8 consecutive tile columns of one tile row, TKB = ceil(TK/8) per tile row,
+ *          block (tr, tb) at index tr*TKB + tb, 1 KiB (256 uint32 words) each: TR*TKB*256 words.
+ *          Slot L of a block owns words 4L .. 4L+3, i.e. eight 16-bit units; unit u is the low
+ *          (u even) or high (u odd) half of word 4L + u/2 and belongs to tile column 8*tb + u.
+ *          The unit of slot L = n % 16 + 16*(gi / 4) in tile (tr, tk) holds the nibbles of
+ *          groups gi with gi / 4 = L / 16 of row n, group gi at bits 4*(gi % 4); a nibble is
+ *          (a | b << 2), where a < b in {0,1,2,3} are the kept positions. Valid nibbles: 0x4 0x8
+ *          0xC 0x9 0xD 0xE. (One 16-byte load gives a lane the indices of 8 tiles, and a 32-bit
+ *          word is the index operand of two steps of the structured-sparse MFMA.)
  *  Entries and nibbles outside the matrix (row padding n >= n_out, column padding k >= n_in)
  *  are zero. splr_packed_bytes() gives both buffer sizes. Metadata not produced by
  *  splr_prune24_pack gives unspecified results (it is not validated).

@@ -6,8 +6,9 @@ outputs) through ctypes. It shares no code with the GPU library and never loads 
 
 Conventions: "bf16" arrays are numpy uint16 bit patterns, "fp32" arrays numpy float32.
 Packed S is returned in its tiled layout (tiles of 16 rows x 64 input columns, see
-splr_oracle.c): values shaped (TR, TK, 64, 8) and meta (TR, TK, 2, 16) uint32, with
-TR = ceil(n_out / 16), TK = ceil(n_in / 64). `unpack` gives the logical per-group view.
+splr_oracle.c): values shaped (TR, TK, 64, 8) and meta (TR, TKB, 64, 4) uint32 (blocks of 8
+tile columns, 16 bytes per slot), with TR = ceil(n_out / 16), TK = ceil(n_in / 64),
+TKB = ceil(TK / 8). `unpack` gives the logical per-group view.
 """
 from __future__ import annotations
 
@@ -73,18 +74,24 @@ def _check(a: np.ndarray, dtype: str, ndim: int, name: str) -> np.ndarray:
     return a
 
 
+def meta_shape(n_out: int, n_in: int) -> Tuple[int, int, int, int]:
+    """Shape of the packed metadata: (TR, TKB, 64, 4) uint32, blocks of 8 tile columns."""
+    TR, TK = tiles(n_out, n_in)
+    return TR, (TK + 7) // 8, 64, 4
+
+
 def tiles(n_out: int, n_in: int) -> Tuple[int, int]:
     """(TR, TK): tile rows and tile columns of the packed layout."""
     return (n_out + 15) // 16, (n_in + 63) // 64
 
 
 def prune24_pack(R: np.ndarray, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
-    """2:4 projection of R [n_out x n_in] -> (values (TR, TK, 64, 8), meta uint32 (TR, TK, 2, 16))."""
+    """2:4 projection of R [n_out x n_in] -> (values (TR, TK, 64, 8), meta uint32 (TR, TKB, 64, 4))."""
     R = _check(R, dtype, 2, "R")
     n_out, n_in = R.shape
     TR, TK = tiles(n_out, n_in)
     values = np.empty((TR, TK, 64, 8), dtype=_NP[dtype])
-    meta = np.empty((TR, TK, 2, 16), dtype=np.uint32)
+    meta = np.empty(meta_shape(n_out, n_in), dtype=np.uint32)
     rc = _load().splr_ref_prune24_pack(_ptr(R), n_out, n_in, _DT[dtype], _ptr(values), _ptr(meta))
     if rc:
         raise ValueError(f"splr_ref_prune24_pack failed ({rc}) for shape {R.shape}")
@@ -124,7 +131,7 @@ def prune24_pack_scaled(R: np.ndarray, d: np.ndarray, dtype: str) -> Tuple[np.nd
         raise ValueError(f"d: expected shape ({n_in},), got {d.shape}")
     TR, TK = tiles(n_out, n_in)
     values = np.empty((TR, TK, 64, 8), dtype=_NP[dtype])
-    meta = np.empty((TR, TK, 2, 16), dtype=np.uint32)
+    meta = np.empty(meta_shape(n_out, n_in), dtype=np.uint32)
     rc = _load().splr_ref_prune24_pack_scaled(_ptr(R), _ptr(d), n_out, n_in, _DT[dtype], _ptr(values), _ptr(meta))
     if rc:
         raise ValueError(f"splr_ref_prune24_pack_scaled failed ({rc}) for shape {R.shape}")
@@ -160,7 +167,7 @@ def prune24_pack_residual(W: np.ndarray, U: Optional[np.ndarray], V: Optional[np
         U, V = _check(U, dtype, 2, "U"), _check(V, dtype, 2, "V")
     TR, TK = tiles(n_out, n_in)
     values = np.empty((TR, TK, 64, 8), dtype=_NP[dtype])
-    meta = np.empty((TR, TK, 2, 16), dtype=np.uint32)
+    meta = np.empty(meta_shape(n_out, n_in), dtype=np.uint32)
     rc = _load().splr_ref_prune24_pack_residual(_ptr(W), _ptr(U if r else None), _ptr(V if r else None), n_out, n_in,
                                                 r, _DT[dtype], _ptr(values), _ptr(meta))
     if rc:
@@ -172,7 +179,7 @@ def _check_packed(values, meta, n_out, n_in, dtype):
     TR, TK = tiles(n_out, n_in)
     values = _check(values, dtype, 4, "values")
     meta = np.ascontiguousarray(meta, dtype=np.uint32)
-    if values.shape != (TR, TK, 64, 8) or meta.shape != (TR, TK, 2, 16):
+    if values.shape != (TR, TK, 64, 8) or meta.shape != meta_shape(n_out, n_in):
         raise ValueError(f"packed shapes {values.shape} {meta.shape} do not match {n_out} x {n_in}")
     return values, meta
 

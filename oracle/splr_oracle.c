@@ -14,10 +14,15 @@
  *              TR = ceil(n_out / 16), TK = ceil(n_in / 64). Row n, group g (columns 4g..4g+3)
  *              has tile (n / 16, g / 16); within the tile gi = g % 16, q = gi / 4, slot
  *              L = n % 16 + 16 q. Its two kept entries a < b (positions 0..3 in the group) are
- *              values[((tile * 64 + L) * 8) + 2 (gi % 4) + {0, 1}], and its nibble (a | b << 2)
- *              sits at bits 4 (gi % 8) of meta[(tile * 2 + gi / 8) * 16 + n % 16].
- *              values holds TR * TK * 512 entries, meta TR * TK * 32 uint32 words; entries and
- *              words outside the matrix (row or column padding) are zero.
+ *              values[((tile * 64 + L) * 8) + 2 (gi % 4) + {0, 1}].
+ *              Metadata comes in blocks of 8 consecutive tile columns of one tile row: block
+ *              (tr, tb) at index tr * TKB + tb, TKB = ceil(TK / 8), 1 KiB = 256 uint32 words each.
+ *              Within a block, slot L owns words 4 L .. 4 L + 3, i.e. eight 16-bit units, unit
+ *              u = tk % 8 being the low (u even) or high (u odd) half of word 4 L + u / 2. Unit u
+ *              of slot L holds the nibbles (a | b << 2) of groups 4 q .. 4 q + 3 of row n in tile
+ *              (n / 16, 8 tb + u), group gi at bits 4 (gi % 4) of the unit.
+ *              values holds TR * TK * 512 entries, meta TR * TKB * 256 uint32 words; entries and
+ *              nibbles outside the matrix (row or column padding) are zero.
  * dtype 0 = float32 storage, 1 = bfloat16 storage (uint16 bit patterns).
  *
  * Functions and the passages they follow:
@@ -117,11 +122,15 @@ static size_t value_index(int64_t n, int64_t g, int s, int64_t n_in) {
   return (tile * 64 + (size_t)(n % 16 + 16 * q)) * 8 + (size_t)(2 * (gi % 4) + s);
 }
 
-/* index of the metadata word holding group g of row n (nibble at bits 4 * (g % 8)) */
-static size_t meta_index(int64_t n, int64_t g, int64_t n_in) {
-  const int64_t gi = g % 16;
-  const size_t tile = (size_t)(n / 16) * (size_t)tiles_cols(n_in) + (size_t)(g / 16);
-  return (tile * 2 + (size_t)(gi / 8)) * 16 + (size_t)(n % 16);
+static int64_t meta_blocks(int64_t n_in) { return (tiles_cols(n_in) + 7) / 8; }
+
+/* metadata word holding the nibble of group g of row n, and the nibble's bit position in it */
+static size_t meta_index(int64_t n, int64_t g, int64_t n_in, int *shift) {
+  const int64_t tk = g / 16, gi = g % 16;
+  const int64_t slot = n % 16 + 16 * (gi / 4), unit = tk % 8;
+  const size_t block = (size_t)(n / 16) * (size_t)meta_blocks(n_in) + (size_t)(tk / 8);
+  *shift = (int)(16 * (unit % 2) + 4 * (gi % 4));
+  return block * 256 + (size_t)(4 * slot + unit / 2);
 }
 
 size_t splr_ref_packed_values(int64_t n_out, int64_t n_in) {
@@ -129,7 +138,7 @@ size_t splr_ref_packed_values(int64_t n_out, int64_t n_in) {
 }
 
 size_t splr_ref_packed_meta(int64_t n_out, int64_t n_in) {
-  return (size_t)tiles_rows(n_out) * (size_t)tiles_cols(n_in) * 32;
+  return (size_t)tiles_rows(n_out) * (size_t)meta_blocks(n_in) * 256;
 }
 
 /*
@@ -168,7 +177,9 @@ static int pack_by_keys(const void *R, const float *d, int64_t n_out, int64_t n_
       const int b = first < second ? second : first;
       copy_elem(values, value_index(n, g, 0, n_in), R, base + a, dtype);
       copy_elem(values, value_index(n, g, 1, n_in), R, base + b, dtype);
-      meta[meta_index(n, g, n_in)] |= (uint32_t)(a | (b << 2)) << (4 * (g % 8));
+      int shift;
+      const size_t w = meta_index(n, g, n_in, &shift);
+      meta[w] |= (uint32_t)(a | (b << 2)) << shift;
     }
   }
   return SPLR_REF_OK;
@@ -281,7 +292,9 @@ int splr_ref_prune24_pack_residual(const void *W, const void *U, const void *V, 
 }
 
 static void decode_nibble(const uint32_t *meta, int64_t n, int64_t g, int64_t n_in, int *a, int *b) {
-  const uint32_t nib = (meta[meta_index(n, g, n_in)] >> (4 * (g % 8))) & 0xFu;
+  int shift;
+  const size_t w = meta_index(n, g, n_in, &shift);
+  const uint32_t nib = (meta[w] >> shift) & 0xFu;
   *a = (int)(nib & 3u);
   *b = (int)(nib >> 2);
 }
@@ -300,7 +313,9 @@ int splr_ref_unpack(const void *values, const uint32_t *meta, int64_t n_out, int
     for (int64_t g = 0; g < groups; ++g) {
       for (int s = 0; s < 2; ++s)
         copy_elem(kept, (size_t)n * (size_t)(n_in / 2) + 2 * (size_t)g + s, values, value_index(n, g, s, n_in), dtype);
-      nib[(size_t)n * (size_t)groups + g] = (uint8_t)((meta[meta_index(n, g, n_in)] >> (4 * (g % 8))) & 0xFu);
+      int shift;
+      const size_t w = meta_index(n, g, n_in, &shift);
+      nib[(size_t)n * (size_t)groups + g] = (uint8_t)((meta[w] >> shift) & 0xFu);
     }
   return SPLR_REF_OK;
 }

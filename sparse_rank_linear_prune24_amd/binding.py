@@ -7,7 +7,8 @@ if the library is missing or a call fails, an exception is raised.
 Conventions: bf16 tensors are torch.bfloat16, fp32 tensors torch.float32; metadata is int32
 (the bits of the library's uint32 words). Packed S uses the library's tiled layout (16 rows x 64
 input columns per tile, see include/splr.h): values are shaped (TR, TK, 64, 8) and metadata
-(TR, TK, 2, 16), TR = ceil(n_out / 16), TK = ceil(n_in / 64). The layer's n_out is passed
+(TR, TKB, 64, 4) (blocks of 8 tile columns), TR = ceil(n_out / 16), TK = ceil(n_in / 64),
+TKB = ceil(TK / 8). The layer's n_out is passed
 explicitly where it cannot be read off U.
 """
 from __future__ import annotations
@@ -144,16 +145,21 @@ def _packed_out(values, meta, n_out, n_in, dtype, device, stream):
             if values is None:
                 values = torch.empty((TR, TK, 64, 8), dtype=dtype, device=device)
             if meta is None:
-                meta = torch.empty((TR, TK, 2, 16), dtype=torch.int32, device=device)
+                meta = torch.empty(meta_shape(n_out, n_in), dtype=torch.int32, device=device)
     _expect(values, "values", dtype, TR * TK * 512, device)
-    _expect(meta, "meta", torch.int32, TR * TK * 32, device)
+    _expect(meta, "meta", torch.int32, _meta_words(n_out, n_in), device)
     return values, meta
+
+
+def _meta_words(n_out: int, n_in: int) -> int:
+    TR, TKB, lanes, words = meta_shape(n_out, n_in)
+    return TR * TKB * lanes * words
 
 
 def _check_packed_in(values, meta, n_out, n_in, dtype, device):
     TR, TK = tiles(n_out, n_in)
     _expect(values, "values", dtype, TR * TK * 512, device)
-    _expect(meta, "meta", torch.int32, TR * TK * 32, device)
+    _expect(meta, "meta", torch.int32, _meta_words(n_out, n_in), device)
 
 
 def _check_factors(U, V, n_out, n_in, dtype, device):
@@ -177,6 +183,12 @@ def tiles(n_out: int, n_in: int) -> Tuple[int, int]:
     return (n_out + 15) // 16, (n_in + 63) // 64
 
 
+def meta_shape(n_out: int, n_in: int) -> Tuple[int, int, int, int]:
+    """Shape of the packed metadata (int32 words): (TR, TKB, 64, 4), blocks of 8 tile columns."""
+    TR, TK = tiles(n_out, n_in)
+    return TR, (TK + 7) // 8, 64, 4
+
+
 def packed_bytes(n_out: int, n_in: int, dtype: torch.dtype) -> Tuple[int, int]:
     """(values bytes, metadata bytes) of the packed layout, as the library reports them."""
     vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
@@ -187,7 +199,7 @@ def packed_bytes(n_out: int, n_in: int, dtype: torch.dtype) -> Tuple[int, int]:
 
 def prune24_pack(R: torch.Tensor, values: Optional[torch.Tensor] = None, meta: Optional[torch.Tensor] = None,
                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """2:4 projection + pack of R [n_out, n_in] -> (values (TR, TK, 64, 8), meta int32 (TR, TK, 2, 16))."""
+    """2:4 projection + pack of R [n_out, n_in] -> (values (TR, TK, 64, 8), meta int32 (TR, TKB, 64, 4))."""
     n_out, n_in = _matrix(R, "R")
     _dtype_code(R)
     values, meta = _packed_out(values, meta, n_out, n_in, R.dtype, R.device, stream)

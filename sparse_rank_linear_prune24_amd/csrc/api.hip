@@ -5,6 +5,7 @@
 
 #include <mutex>
 
+#include "common.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -107,9 +108,9 @@ splr_status_t splr_packed_bytes(int64_t n_out, int64_t n_in, splr_dtype_t dtype,
   if (s == SPLR_OK) s = check_rows(n_out, n_in);
   if (s != SPLR_OK) return s;
   if (!dtype_ok(dtype)) return SPLR_ERR_DTYPE;
-  const size_t tiles = (size_t)((n_out + 15) / 16) * (size_t)((n_in + 63) / 64);
-  *values_bytes = tiles * 512 * (dtype == SPLR_BF16 ? 2 : 4);
-  *meta_bytes = tiles * 32 * sizeof(uint32_t);
+  const size_t TR = (size_t)((n_out + 15) / 16), TK = (size_t)((n_in + 63) / 64);
+  *values_bytes = TR * TK * 512 * (dtype == SPLR_BF16 ? 2 : 4);
+  *meta_bytes = TR * (size_t)splr::meta_blocks((int)TK) * 1024;
   return SPLR_OK;
 }
 

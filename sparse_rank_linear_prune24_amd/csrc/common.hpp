@@ -58,6 +58,12 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 __device__ __forceinline__ f32x4_t smfmac16x16x64(bf16x8_t a, bf16x16_t b, f32x4_t c, int idx) {
   return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, 0);
 }
+// The same with the index taken from bits [31:16] of `idx` when ABID is 1 (bits [15:0] when 0): a
+// 32-bit metadata word holds the indices of two tile columns.
+template <int ABID>
+__device__ __forceinline__ f32x4_t smfmac16x16x64_half(bf16x8_t a, bf16x16_t b, f32x4_t c, uint32_t idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, (int)idx, 0, ABID);
+}
 
 // Keep positions of four keys (2:4 projection): i outranks j <=> k_i > k_j, or k_i == k_j and i < j. An
 // entry is kept iff it outranks at least two of the other three (ranks of four entries in a
@@ -89,5 +95,14 @@ __device__ __forceinline__ uint32_t top2_of_4(Key k0, Key k1, Key k2, Key k3, ui
 }
 
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Packed metadata: blocks of 8 tile columns of one tile row (TKB = ceil(TK / 8) per tile row),
+// 1 KiB each; slot L (the lane of the MFMA operand: row L % 16, groups 4 (L / 16) .. +3 of a tile)
+// owns 16 bytes, one 16-bit unit per tile column, the unit of tile column tk at 2 (tk % 8). Group
+// gi of the tile sits at bits 4 (gi % 4) of its unit.
+__host__ __device__ constexpr inline int meta_blocks(int TK) { return (TK + 7) / 8; }
+__device__ __forceinline__ uint32_t meta_unit(const uint32_t* __restrict__ meta, int TKB, int64_t tr, int tk, int L) {
+  return ((const uint16_t*)meta)[(((size_t)tr * TKB + tk / 8) * 64 + L) * 8 + tk % 8];
+}
 
 }  // namespace splr

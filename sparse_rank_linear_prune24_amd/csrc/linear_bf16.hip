@@ -56,6 +56,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+constexpr int lcm_int(int a, int b) { return a / gcd_int(a, b) * b; }
 
 // f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}), in order
 template <typename F, int... I>
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   constexpr int kXLoads = BM / (8 * WAVES);  // X load instructions per wave per step (8 tokens each)
   static_assert(BM % (8 * WAVES) == 0, "X stage must split evenly over the waves");
   static_assert(P >= 2 && PX >= 2 && P % 2 == 0 && PX % 2 == 0, "prefetch distances must be even");
-  constexpr int kUnroll = P * PX / gcd_int(P, PX);  // unroll factor: every register slot index is a constant
+  constexpr int kUnroll = lcm_int(P, PX);  // unroll factor: every register slot index is a constant
   // the two LDS slots are separate objects, so the compiler may move reads of one past writes of
   // the other
   __shared__ u32x4_t xs0[BM * kXPitchU4];
@@ -389,12 +390,13 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
 
   // S fragments of this wave: tile rows (clamped; rows past n_out are zero padding or unused)
   const u32x4_t* vsrc[NI];
-  const uint16_t* msrc[NI];  // this lane's 16 index bits: half (quad & 1) of its metadata word
+  const uint16_t* msrc[NI];  // this lane's 16 index bits of tile column 0: unit 0 of its slot (= lane)
+  const int TKB = meta_blocks(TK);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int tr = min(n0 / 16 + wave * NI + i, TR - 1);
     vsrc[i] = values + (size_t)tr * TK * 64 + lane;
-    msrc[i] = (const uint16_t*)(meta + (size_t)tr * TK * 32 + sub + 16 * (quad >> 1)) + (quad & 1);
+    msrc[i] = (const uint16_t*)meta + ((size_t)tr * TKB * 64 + lane) * 8;
   }
   // X rows this lane loads: token m0 + wave*BM/4 + 8 t + lane/8, 16-byte chunk lane%8 of a step
   const int xchunk = lane & 7;
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       va[i] = vsrc[i][(size_t)kk * 64];
-      wa[i] = msrc[i][(size_t)kk * 64];
+      wa[i] = msrc[i][(size_t)(kk >> 3) * 512 + (kk & 7)];
     }
   };
   auto store_x = [&](u32x4_t* slot, const u32x4_t (&v)[kXLoads]) {
@@ -579,6 +581,217 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------------- prefill, wide tile
+
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs: 32-bit data format, no swizzle, no index
+// stride (plain byte-addressed loads).
+constexpr int kBufferFlags = 0x00020000;
+
+// The structured-sparse MFMA with its accumulator pinned to the matrix-core accumulator registers
+// (the compiler would otherwise spread 256 accumulators over both register files and copy them
+// every step). ABID selects the half of the 32-bit index register the instruction reads (a
+// metadata word holds the indices of two tile columns). Hazard rules this relies on, kept by the
+// kernel below: the A, B and index operands come straight from loads (the waits for loads precede
+// the instruction; no vector-ALU instruction writes an operand), an accumulator is written by these
+// instructions only and 64 instructions apart, and anything else touches the accumulators only
+// across accumulator_fence().
+template <int ABID>
+__device__ __forceinline__ void smfmac_acc(f32x4_t& acc, bf16x8_t a, bf16x16_t b, uint32_t idx) {
+  if constexpr (ABID == 0)
+    asm volatile("v_smfmac_f32_16x16x64_bf16 %0, %1, %2, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
+  else
+    asm volatile("v_smfmac_f32_16x16x64_bf16 %0, %1, %2, %3 abid:1" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
+}
+// Wait states between accumulator writes by ordinary instructions and smfmac_acc (or the reverse),
+// followed by an empty asm per accumulator that every later use depends on, so the compiler cannot
+// move an accumulator read or write across the wait states (64 > the pass count of the 16x16x64
+// structured-sparse MFMA and every write-to-read distance the matrix core needs).
+template <int NI, int NJ>
+__device__ __forceinline__ void accumulator_fence(f32x4_t (&acc)[NI][NJ]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+// Prefill kernel with the accumulators in the matrix-core accumulator registers: workgroup tile
+// 16*NI*4 rows x 128 tokens, 4 waves, each owning 16*NI rows (NI S fragments) x all 128 tokens, so
+// 4*NI*8 accumulator registers per lane (NI = 8: 512 rows and 256 registers). Per 64-column K step
+// a CU loads 4 KiB of S values per 16 rows and 16 KiB of X for NI*128 cycles of structured-sparse
+// MFMA per SIMD, and each lane loads its metadata once per 8 steps: one 16-byte word group per
+// fragment holds its indices for a whole metadata block. The B fragments are not double-buffered
+// per step: each 16-token group's fragment is read from LDS LA groups ahead of its NI MFMAs. Since
+// a step then reads its own X slot, X goes through a three-slot LDS ring (X of step s is written
+// during step s-2, read during steps s-1 (first groups) and s), still one barrier per step. The
+// rank-r term runs after the main loop, 64 ranks at a time, with T's bfloat16 pair built in the
+// freed X slots and U read straight from memory.
+template <int NI, int LA, int P, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void linear_prefill_wide_kernel(
+    const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
+    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16,
+    int M, int K, int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
+  constexpr int NJ = 8, WAVES = 4, PX = 2;
+  constexpr int BN = 16 * NI * WAVES;  // 512 or 256 rows
+  constexpr int BM = 16 * NJ;          // 128 tokens
+  static_assert(NI % 4 == 0 && LA >= 1 && LA < NJ, "S loads in groups of four fragments");
+  constexpr int kXLoads = BM / (8 * WAVES);
+  static_assert(P >= 2 && 16 % P == 0, "S prefetch distance dividing the unroll");
+  constexpr int kUnroll = 16;  // two metadata blocks: every S, X-register and metadata ring index is constant
+  constexpr int kSlot = BM * kXPitchU4;  // one LDS slot, 16-byte units
+  __shared__ u32x4_t xs[3 * kSlot];
+
+  // XCD-aware tile order (as in the 256 x 128 kernel)
+  const int b = blockIdx.x;
+  const int logical = (b & 7) * tiles_per_xcd + (b >> 3);
+  if (logical >= tiles_n * tiles_m) return;
+  const int per_group = group_m * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * group_m;
+  const int gsize = min(group_m, tiles_m - first_m);
+  const int in_group = logical - g * per_group;
+  const int m0 = (first_m + in_group % gsize) * BM;
+  const int n0 = (in_group / gsize) * BN;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane & 15, quad = lane >> 4;
+  const int TK = (K + 63) / 64, TR = (n_out + 15) / 16, TKB = meta_blocks(TK);
+  const int nk_pad = (TK + kUnroll - 1) / kUnroll * kUnroll;
+
+  // Loads are raw buffer loads: a wave-uniform base (buffer descriptor) plus a wave-uniform byte
+  // offset (scalar register) plus one 32-bit per-lane offset, so no per-load address arithmetic
+  // runs on the vector ALUs and the per-lane state is a few registers. Each descriptor covers only
+  // the bytes this wave may touch; loads past it return zero (padding steps and fragments past the
+  // last tile row use that).
+  // S fragment i of step kk: tile row tr0 + i, 1 KiB per tile, the lane's 16 bytes; metadata block
+  // kb of tile row tr0 + i: 1 KiB, the lane's 16 bytes (its slot is its lane).
+  const int tr0 = __builtin_amdgcn_readfirstlane(min(n0 / 16 + wave * NI, TR - 1));
+  const int rows_here = min(NI, TR - tr0);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(values + (size_t)tr0 * TK * 64), (short)0, rows_here * TK * 1024, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)meta + (size_t)tr0 * TKB * 1024), (short)0, rows_here * TKB * 1024, kBufferFlags);
+  const int s_off = lane * 16;
+  const int s_stride = TK * 1024, m_stride = TKB * 1024;  // bytes per tile row
+  // X: rows m0 + wave*32 + 8t + lane/8 (clamped to M-1), 16-byte chunk lane%8 of a step; offsets
+  // from the tile's first row stay below 2^31 (at most 128 rows of at most 2^20 columns)
+  const int xchunk = lane & 7;
+  const int x_rows = min(BM, M - m0);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)m0 * K), (short)0, x_rows * K * 2, kBufferFlags);
+  int x_off[kXLoads];
+  int xdst[kXLoads];
+#pragma unroll
+  for (int t = 0; t < kXLoads; ++t) {
+    const int tloc = wave * (BM / WAVES) + 8 * t + (lane >> 3);
+    x_off[t] = min(tloc, x_rows - 1) * K * 2 + 16 * xchunk;
+    xdst[t] = tloc * kXPitchU4 + xchunk;
+  }
+
+  u32x4_t xr[PX][kXLoads];
+  u32x4_t sa[P][NI];
+  u32x4_t mb[2][NI];  // metadata of the current and the next block of 8 steps
+  bf16x16_t bx[LA + 1];
+  const int x_end = x_rows * K * 2, v_end = rows_here * s_stride, m_end = rows_here * m_stride;
+  auto load_x = [&](int kc, u32x4_t (&v)[kXLoads]) {
+    // half tail step: re-read valid columns (S is zero there); per lane, as the chunk decides
+    const int back = (kc < TK && kc * 64 + 8 * xchunk >= K) ? 64 : 0;
+    const int so = kc < TK ? kc * 128 : x_end;
+#pragma unroll
+    for (int t = 0; t < kXLoads; ++t) v[t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, x_off[t] - back, so, 0);
+  };
+  auto load_s_frag = [&](int kc, int i, u32x4_t& va) {
+    va = __builtin_amdgcn_raw_buffer_load_b128(vrs, s_off, kc < TK ? i * s_stride + kc * 1024 : v_end, 0);
+  };
+  auto load_m = [&](int kb, u32x4_t (&m)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      m[i] = __builtin_amdgcn_raw_buffer_load_b128(mrs, s_off, kb < TKB ? i * m_stride + kb * 1024 : m_end, 0);
+  };
+  auto store_x = [&](int slot, const u32x4_t (&v)[kXLoads]) {
+#pragma unroll
+    for (int t = 0; t < kXLoads; ++t) xs[slot * kSlot + xdst[t]] = v[t];
+  };
+  auto read_b = [&](int slot, int j) {
+    const int row = slot * kSlot + (16 * j + sub) * kXPitchU4;
+    return cat16(as_bf16x8(xs[row + quad]), as_bf16x8(xs[row + 4 + quad]));
+  };
+  f32x4_t acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
+
+  // Step kc (u = kc mod 16, LDS slots rotating with kc mod 3): X of step kc is in slot kc % 3 and
+  // its first LA B fragments are in registers; X of step kc+1 is in slot (kc+1) % 3. Issue order,
+  // in 8 groups fenced from each other: each group first issues the B fragment read LA groups ahead
+  // (past the step's last group: the first fragments of step kc+1) and its share of the step's
+  // memory work (group 0: the LDS writes of X of step kc+2 into slot (kc+2) % 3, whose last reads
+  // finished before the previous barrier; groups 1 .. NI/4: four S loads of step kc+P-1 each; the
+  // next group: the X loads of step kc+2+PX and, at a block's first step, the next block's
+  // metadata), then its NI MFMAs. One barrier per step.
+  constexpr int kXGroup = NI / 4 + 1;
+  static_assert(kXGroup < NJ, "every load has a group");
+  auto step = [&](int kc, int s0, auto uu) {
+    constexpr int u = decltype(uu)::value;
+    constexpr int d = u % P, dprev = (u + P - 1) % P, xq = (u + 2) % PX, mq = (u / 8) % 2;
+    const int cur = (s0 + u) % 3, nxt = (s0 + u + 1) % 3, wr = (s0 + u + 2) % 3;
+    static_for<NJ>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      if constexpr (j == 0) store_x(wr, xr[xq]);
+      bx[(j + LA) % (LA + 1)] = j + LA < NJ ? read_b(cur, j + LA) : read_b(nxt, j + LA - NJ);
+      if constexpr (j >= 1 && j < kXGroup) {
+#pragma unroll
+        for (int i = 4 * (j - 1); i < 4 * j; ++i) load_s_frag(kc + P - 1, i, sa[dprev][i]);
+      }
+      if constexpr (j == kXGroup) {
+        load_x(kc + 2 + PX, xr[xq]);
+        if constexpr (u % 8 == 0) load_m(kc / 8 + 1, mb[mq ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        smfmac_acc<u % 2>(acc[i][j], as_bf16x8(sa[d][i]), bx[j % (LA + 1)], mb[mq][i][(u % 8) / 2]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    lds_barrier();
+  };
+
+  // Prologue: virtual steps v = -VS .. -1 issue what a step would (X of step v+2 into LDS, S of
+  // step v+P-1, X of step v+2+PX), so the loop starts with the steady state's loads in flight; the
+  // first metadata block goes first.
+  load_m(0, mb[0]);
+  constexpr int VS = (P - 1 > PX + 2) ? P - 1 : PX + 2;
+  static_for<VS>([&](auto ii) {
+    constexpr int v = decltype(ii)::value - VS;
+    if constexpr (v >= -2) store_x(v + 2, xr[(v + 2 + PX) % PX]);
+    if constexpr (v + P - 1 >= 0) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) load_s_frag(v + P - 1, i, sa[(v + P - 1) % P][i]);
+    }
+    if constexpr (v + 2 + PX >= 0) load_x(v + 2 + PX, xr[(v + 2 + PX) % PX]);
+  });
+  lds_barrier();
+  static_for<LA>([&](auto jj) { bx[decltype(jj)::value] = read_b(0, decltype(jj)::value); });
+  accumulator_fence(acc);  // the zeros written above, before the first smfmac_acc reads them
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kc0 = 0; kc0 < nk_pad; kc0 += kUnroll) {
+    const int s0 = kc0 % 3;
+    static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, s0, u); });
+  }
+  accumulator_fence(acc);  // the last smfmac_acc results, before the rank-r term and the stores
+
+  // rank-r term, 64 ranks at a time: T's pair in slots 0 and 1 (the last step's barrier retired
+  // every LDS access of the loop), U fragments from memory
+  const int nrow0 = n0 + wave * 16 * NI;
+  for (int j0 = 0; j0 < r; j0 += 64) {
+    build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs, xs + kSlot, threadIdx.x);
+    lds_barrier();
+    lowrank_block<NI, NJ>(acc, U, xs, xs + kSlot, n_out, r, j0, nrow0, lane);
+    lds_barrier();
+  }
+  store_tile<NI, NJ, EPI == kEpiDirectNT>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
+}
+
 // ----------------------------------------------------------------------------------- decode
 
 template <int MB, int P, int WAVES>
@@ -598,7 +811,7 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
   const int TK = (K + 63) / 64;
 
   const u32x4_t* vsrc = values + (size_t)tr * TK * 64 + lane;
-  const uint16_t* msrc = (const uint16_t*)(meta + (size_t)tr * TK * 32 + sub + 16 * (quad >> 1)) + (quad & 1);
+  const uint16_t* msrc = (const uint16_t*)meta + ((size_t)tr * meta_blocks(TK) * 64 + lane) * 8;
   const int xchunk = lane & 7;
   const uint16_t* xsrc[kXLoads];
   int xdst[kXLoads];
@@ -625,7 +838,7 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
   auto load = [&](int s, u32x4_t& va, uint32_t& wa, u32x4_t (&xv)[kXLoads]) {
     const int kc = min(wave + s * WAVES, TK - 1);
     va = vsrc[(size_t)kc * 64];
-    wa = msrc[(size_t)kc * 64];
+    wa = msrc[(size_t)(kc >> 3) * 512 + (kc & 7)];
     int col = kc * 64;
     if (col + 8 * xchunk >= K) col -= 32;  // half tail step: re-read valid columns (S is zero there)
 #pragma unroll
@@ -717,9 +930,16 @@ hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* val
   return hipGetLastError();
 }
 
-// prefill: one workgroup per 256-row x 128-token tile, tiles dealt to the 8 XCDs in equal ranges
+// The 512-row tile when it still gives every CU of the chip at least one tile, else 256 rows.
+constexpr int64_t kWideMinTiles = 256;
+int64_t prefill_rows(int64_t M, int64_t n_out) {
+  return ceil_div(n_out, 512) * ceil_div(M, 128) >= kWideMinTiles ? 512 : 256;
+}
+
+// prefill: one workgroup per tile (512 or 256 rows x 128 tokens), tiles dealt to the 8 XCDs in
+// equal ranges
 dim3 prefill_grid(int64_t M, int64_t n_out) {
-  const int64_t n_tiles = ceil_div(n_out, 256) * ceil_div(M, 128);
+  const int64_t n_tiles = ceil_div(n_out, prefill_rows(M, n_out)) * ceil_div(M, 128);
   return dim3((unsigned)(8 * ceil_div(n_tiles, 8)));
 }
 
@@ -742,7 +962,8 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
     return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, yb, stream);
 
   constexpr int NI = 4, NJ = 8, P = 4, PX = 2;
-  constexpr int BN = 16 * NI * 4, BM = 16 * NJ;
+  constexpr int BM = 16 * NJ;
+  const int BN = (int)prefill_rows(M, n_out);
   const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
   const int n_tiles = tiles_n * tiles_m;
   const dim3 grid = prefill_grid(M, n_out);
@@ -758,6 +979,17 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   // between).
   const bool y_nt = (double)M * n_out * (y_bf16 ? 2 : 4) > kNonTemporalYBytes;
   const dim3 block(256);
+  if (BN == 512) {
+    if (y_nt)
+      linear_prefill_wide_kernel<8, 1, 2, kEpiDirectNT><<<grid, block, 0, stream>>>(
+          (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
+          (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+    else
+      linear_prefill_wide_kernel<8, 1, 2, kEpiDirect><<<grid, block, 0, stream>>>(
+          (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
+          (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+    return hipGetLastError();
+  }
   if (n_tiles <= kRowsEpilogueMaxTiles && r <= 64)
     linear_prefill_kernel<NI, NJ, P, PX, kEpiRows><<<grid, block, 0, stream>>>(
         (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,

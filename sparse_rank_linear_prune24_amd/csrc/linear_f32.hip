@@ -19,11 +19,11 @@ __device__ __forceinline__ void linear_f32_output(const float* __restrict__ X, c
   const float* x = X + (size_t)m * K;
   const int TK = (K + 63) / 64;
   const float* v = values + (size_t)(n / 16) * TK * 512;  // this row's tile row
-  const uint32_t* mw = meta + (size_t)(n / 16) * TK * 32 + (n % 16);
+  const int TKB = meta_blocks(TK);
   float acc = 0.0f;
   for (int grp = 0; grp < K / 4; ++grp) {
     const int tk = grp / 16, gi = grp % 16;
-    const uint32_t nib = (mw[tk * 32 + (gi / 8) * 16] >> (4 * (gi % 8))) & 0xFu;
+    const uint32_t nib = (meta_unit(meta, TKB, n / 16, tk, n % 16 + 16 * (gi / 4)) >> (4 * (gi % 4))) & 0xFu;
     const float* kept = v + (size_t)tk * 512 + ((n % 16) + 16 * (gi / 4)) * 8 + 2 * (gi % 4);
     acc = fmaf(x[4 * grp + (nib & 3u)], kept[0], acc);
     acc = fmaf(x[4 * grp + (nib >> 2)], kept[1], acc);

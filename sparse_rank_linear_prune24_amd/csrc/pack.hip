@@ -22,9 +22,10 @@
 // tiles of the packed layout). Each lane reads 16-byte chunks with row-contiguous, fully
 // coalesced loads, ranks the four entries of each group with six integer compares of keys (the
 // sign-cleared bit patterns, or the bit patterns of the exact binary64 scores: bit-exact either way),
-// and scatters its kept pair into the tile image in LDS; the lanes that share a metadata word
-// merge their nibbles with cross-lane shuffles. The finished tiles leave LDS as contiguous
-// 16-byte stores.
+// and scatters its kept pair into the tile image in LDS; the lanes that share a 16-bit metadata
+// unit merge their nibbles with cross-lane shuffles. A bf16 workgroup's 8 tiles are exactly one
+// metadata block (8 tile columns of a tile row), an fp32 workgroup's 4 tiles half of one. The
+// finished tiles and the block leave LDS as contiguous 16-byte (fp32 metadata: 8-byte) stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -130,7 +131,7 @@ __device__ __forceinline__ void nm_project_chunk(u32x4_t& x, int n_keep, int lan
 template <bool BF16, bool SCALED, int CPT, int NM = 0>
 __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_t* __restrict__ R,
                                                                     const float* __restrict__ dscale, int n_out, int K,
-                                                                    int TK, u32x4_t* __restrict__ values,
+                                                                    int TK, int TKB, u32x4_t* __restrict__ values,
                                                                     uint32_t* __restrict__ meta, int n_keep = 2) {
   constexpr int kEsz = BF16 ? 2 : 4;            // bytes per entry
   constexpr int kPerChunk = 16 / kEsz;          // entries per 16-byte chunk (8 bf16 = 2 groups, 4 fp32 = 1)
@@ -139,8 +140,10 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
   constexpr int kTiles = kCols / 64;            // packed tiles per workgroup
   constexpr int kTileU4 = 512 * kEsz / 16;      // 16-byte units of values per tile (64 / 128)
   static_assert((kRowChunks & (kRowChunks - 1)) == 0 && kTiles >= 1, "power-of-two row chunks, whole tiles");
+  static_assert(kTiles == 8 || kTiles == 4, "a metadata block or half of one per workgroup");
   __shared__ u32x4_t sv[kTiles * kTileU4];
-  __shared__ uint32_t sm[kTiles * 32];
+  // metadata image: slot L's units for this workgroup's tiles, unit (L, t) at sm[L * kTiles + t]
+  __shared__ uint16_t sm[64 * kTiles];
 
   const int tr = blockIdx.x;                    // tile row
   const int tk0 = blockIdx.y * kTiles;          // first tile column of this workgroup
@@ -205,11 +208,11 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
       // 4 entries (8 bytes) at entry 2*(gi0 % 4) of the slot: half (gi0 % 4) / 2 of its 16 bytes
       u32x2_t* dst = (u32x2_t*)&sv[tkl * kTileU4 + slot] + ((gi0 & 3) >> 1);
       *dst = u32x2_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
-      // byte (gi0 % 8) / 2 of word (gi0 / 8) of row r: the four lanes ch % 4 = 0..3 share it
+      // the unit of slot r + 16 (gi0 / 4) in tile tkl: groups 4q .. 4q+3, this chunk's two at
+      // bits 4 (gi0 % 4); the lanes ch, ch + 1 (gi0 % 4 = 0, 2) share it
       word = n0 | (n1 << 4);
       word |= (uint32_t)__shfl_down((int)word, 1) << 8;
-      word |= (uint32_t)__shfl_down((int)word, 2) << 16;
-      if ((ch & 3) == 0) sm[tkl * 32 + (gi0 >> 3) * 16 + r] = word;
+      if ((ch & 1) == 0) sm[(r + 16 * (gi0 >> 2)) * kTiles + tkl] = (uint16_t)word;
     } else {
       // chunk = group gi of tile tkl
       const int tkl = ch >> 4, gi = ch & 15;
@@ -226,12 +229,12 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
       const int slot = r + 16 * (gi >> 2);
       u32x2_t* dst = (u32x2_t*)&sv[tkl * kTileU4 + 2 * slot] + (gi & 3);
       *dst = u32x2_t{va, vb};
-      // nibble gi % 8 of word gi / 8 of row r: the eight lanes ch % 8 = 0..7 share it
+      // the unit of slot r + 16 (gi / 4) in tile tkl: nibble at bits 4 (gi % 4); the four lanes
+      // ch % 4 = 0..3 share it
       word = nb;
       word |= (uint32_t)__shfl_down((int)word, 1) << 4;
       word |= (uint32_t)__shfl_down((int)word, 2) << 8;
-      word |= (uint32_t)__shfl_down((int)word, 4) << 16;
-      if ((ch & 7) == 0) sm[tkl * 32 + (gi >> 3) * 16 + r] = word;
+      if ((ch & 3) == 0) sm[(r + 16 * (gi >> 2)) * kTiles + tkl] = (uint16_t)word;
     }
   }
   __syncthreads();
@@ -241,7 +244,18 @@ __global__ __launch_bounds__(kPackThreads) void prune24_pack_kernel(const uint8_
 #pragma unroll
   for (int u = tid; u < kTiles * kTileU4; u += kPackThreads)
     if (u < n_tiles * kTileU4) values[t0 * kTileU4 + u] = sv[u];
-  if (tid < n_tiles * 8) ((u32x4_t*)meta)[t0 * 8 + tid] = ((const u32x4_t*)sm)[tid];
+  // metadata block (tr, tk0 / 8): slot tid's 16 bytes (bf16), or the half of them for tiles
+  // tk0 .. tk0 + 3 (fp32: with zeros for the other half when no workgroup covers it)
+  uint8_t* mblock = (uint8_t*)meta + ((size_t)tr * TKB + tk0 / 8) * 1024;
+  if (tid < 64) {
+    if constexpr (kTiles == 8) {
+      *(u32x4_t*)(mblock + tid * 16) = ((const u32x4_t*)sm)[tid];
+    } else {
+      const u32x2_t half = ((const u32x2_t*)sm)[tid];
+      if (tk0 % 8 == 0 && tk0 + 4 >= TK) *(u32x4_t*)(mblock + tid * 16) = u32x4_t{half[0], half[1], 0u, 0u};
+      else *(u32x2_t*)(mblock + tid * 16 + (tk0 % 8) * 2) = half;
+    }
+  }
 }
 
 dim3 pack_grid(int64_t n_out, int64_t n_in, bool bf16) {
@@ -253,14 +267,14 @@ template <bool SCALED, int NM = 0>
 hipError_t launch_pack(const void* R, const float* d, int64_t n_out, int64_t n_in, bool bf16, void* values,
                        uint32_t* meta, hipStream_t stream, int n_keep = 2) {
   constexpr int CPT = kPackChunksPerThread;
-  const int TK = (int)ceil_div(n_in, 64);
+  const int TK = (int)ceil_div(n_in, 64), TKB = (TK + 7) / 8;
   const dim3 grid = pack_grid(n_out, n_in, bf16);
   if (bf16)
     prune24_pack_kernel<true, SCALED, CPT, NM><<<grid, dim3(kPackThreads), 0, stream>>>(
-        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta, n_keep);
+        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, TKB, (u32x4_t*)values, meta, n_keep);
   else
     prune24_pack_kernel<false, SCALED, CPT, NM><<<grid, dim3(kPackThreads), 0, stream>>>(
-        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, (u32x4_t*)values, meta, n_keep);
+        (const uint8_t*)R, d, (int)n_out, (int)n_in, TK, TKB, (u32x4_t*)values, meta, n_keep);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ __device__ __forceinline__ void reconstruct_group(const void* __restrict__ value
   // packed tiles of 16 rows x 64 columns: tile (n / 16, g / 16), slot n % 16 + 16 * (gi / 4)
   const int TK = (K + 63) / 64, gi = g % 16;
   const size_t tile = (size_t)(n / 16) * TK + g / 16;
-  const uint32_t nib = (meta[tile * 32 + (gi / 8) * 16 + n % 16] >> (4 * (gi % 8))) & 0xFu;
+  const uint32_t nib = (meta_unit(meta, meta_blocks(TK), n / 16, g / 16, (int)(n % 16) + 16 * (gi / 4)) >> (4 * (gi % 4))) & 0xFu;
   const int a = (int)(nib & 3u), b = (int)(nib >> 2);
   const size_t e = (tile * 64 + (size_t)(n % 16) + 16 * (gi / 4)) * 8 + 2 * (gi % 4);
   float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -87,11 +87,12 @@ __device__ __forceinline__ void fma_tail(float (&acc)[CPL][16], const float (&v)
 template <bool BF16, int CPL>
 __global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
     const void* __restrict__ W, const void* __restrict__ U, const void* __restrict__ V, int n_out, int K, int r,
-    int TK, int col_blocks, u32x4_t* __restrict__ values, uint32_t* __restrict__ meta) {
+    int TK, int TKB, int col_blocks, u32x4_t* __restrict__ values, uint32_t* __restrict__ meta) {
+  static_assert(kResWaves * CPL == 8, "a workgroup's tiles are one metadata block");
   constexpr int kTileU32 = BF16 ? 256 : 512;  // one packed tile's values in 32-bit words
   __shared__ f32x4_t us[16 * kRJ / 4];        // U rows of the tile row, one rank block, float32
   __shared__ uint32_t img[kResWaves][kTileU32];
-  __shared__ uint32_t mimg[kResWaves][32];
+  __shared__ uint16_t mimg[64 * 8];  // the block's metadata image: unit (slot L, tile t) at L * 8 + t
   __shared__ __align__(16) uint32_t ebuf[kResWaves][16 * 64];  // rounded rows of a tile (storage bits)
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -173,12 +174,12 @@ __global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
       const int slot = i + 16 * (gg >> 2);
       if constexpr (BF16) img[wave][slot * 4 + (gg & 3)] = va | (vb << 16);
       else *(u32x2_t*)&img[wave][slot * 8 + 2 * (gg & 3)] = u32x2_t{va, vb};
-      // nibble gg % 8 of word gg / 8 of row i: the eight lanes gg % 8 = 0..7 share it
+      // the unit of slot i + 16 (gg / 4) in this tile: nibble at bits 4 (gg % 4); the four lanes
+      // gg % 4 = 0..3 share it
       uint32_t word = nib;
       word |= (uint32_t)__shfl_down((int)word, 1) << 4;
       word |= (uint32_t)__shfl_down((int)word, 2) << 8;
-      word |= (uint32_t)__shfl_down((int)word, 4) << 16;
-      if ((lane & 7) == 0) mimg[wave][(gg >> 3) * 16 + i] = word;
+      if ((lane & 3) == 0) mimg[(i + 16 * (gg >> 2)) * 8 + wave * CPL + s] = (uint16_t)word;
     }
     // this wave's LDS writes are complete before its own reads below, and those before the next
     // tile's writes (LDS operations of one wave execute in order)
@@ -187,8 +188,14 @@ __global__ __launch_bounds__(64 * kResWaves) void residual_pack_kernel(
       constexpr int kTileU4 = kTileU32 / 4;
 #pragma unroll
       for (int q = lane; q < kTileU4; q += 64) values[((size_t)tr * TK + tk) * kTileU4 + q] = ((const u32x4_t*)img[wave])[q];
-      if (lane < 8) ((u32x4_t*)meta)[((size_t)tr * TK + tk) * 8 + lane] = ((const u32x4_t*)mimg[wave])[lane];
     }
+  }
+  // every wave's units are in the block image (tiles past TK hold zero nibbles); wave 0 stores
+  // the block
+  __syncthreads();
+  if (wave == 0) {
+    const int tb = (tk0 - wave * CPL) / 8;
+    ((u32x4_t*)meta)[((size_t)tr * TKB + tb) * 64 + lane] = ((const u32x4_t*)mimg)[lane];
   }
 }
 
@@ -208,14 +215,14 @@ bool residual_grids_fit(int64_t n_out, int64_t n_in) {
 hipError_t launch_prune24_pack_residual(const void* W, const void* U, const void* V, int64_t n_out, int64_t n_in,
                                         int64_t r, bool bf16, void* values, uint32_t* meta, hipStream_t stream) {
   constexpr int CPL = kResColsPerLane;
-  const int TK = (int)ceil_div(n_in, 64), cb = residual_col_blocks(n_in);
+  const int TK = (int)ceil_div(n_in, 64), TKB = (TK + 7) / 8, cb = residual_col_blocks(n_in);
   const dim3 grid = residual_grid(n_out, n_in);
   if (bf16)
     residual_pack_kernel<true, CPL><<<grid, dim3(64 * kResWaves), 0, stream>>>(W, U, V, (int)n_out, (int)n_in, (int)r,
-                                                                              TK, cb, (u32x4_t*)values, meta);
+                                                                              TK, TKB, cb, (u32x4_t*)values, meta);
   else
     residual_pack_kernel<false, CPL><<<grid, dim3(64 * kResWaves), 0, stream>>>(W, U, V, (int)n_out, (int)n_in,
-                                                                               (int)r, TK, cb, (u32x4_t*)values, meta);
+                                                                               (int)r, TK, TKB, cb, (u32x4_t*)values, meta);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ def host_as_device(monkeypatch):
 def layer(M=32, n_in=128, n_out=48, r=16, dt=bf):
     TR, TK = binding.tiles(n_out, n_in)
     return dict(X=torch.zeros(M, n_in, dtype=dt), values=torch.zeros(TR, TK, 64, 8, dtype=dt),
-                meta=torch.zeros(TR, TK, 2, 16, dtype=torch.int32), U=torch.zeros(n_out, r, dtype=dt),
+                meta=torch.zeros(binding.meta_shape(n_out, n_in), dtype=torch.int32), U=torch.zeros(n_out, r, dtype=dt),
                 V=torch.zeros(r, n_in, dtype=dt), Y=torch.zeros(M, n_out, dtype=f32),
                 ws=torch.zeros(1 << 20, dtype=torch.uint8), n_out=n_out)
 
@@ -56,8 +56,8 @@ def test_correct_shapes_reach_the_library():
     dict(V=None),                                          # U without V
     dict(values=torch.zeros(3, 2, 64, 4, dtype=bf)),       # values too small for the tile grid
     dict(values=torch.zeros(3, 2, 64, 8, dtype=f32)),      # values dtype != X dtype
-    dict(meta=torch.zeros(3, 2, 2, 8, dtype=torch.int32)), # metadata too small
-    dict(meta=torch.zeros(3, 2, 2, 16, dtype=torch.int64)),  # metadata not 32-bit
+    dict(meta=torch.zeros(3, 1, 64, 2, dtype=torch.int32)),  # metadata too small
+    dict(meta=torch.zeros(3, 1, 64, 4, dtype=torch.int64)),  # metadata not 32-bit
     dict(Y=torch.zeros(32, 48, dtype=bf)),                 # float32 Y expected
     dict(Y=torch.zeros(32, 32, dtype=f32)),                # Y too small
     dict(Y=torch.zeros(48, 32, dtype=f32).t()),            # not contiguous
@@ -94,7 +94,7 @@ def test_packs_reject():
     with pytest.raises(ValueError):
         binding.prune24_pack(R, torch.zeros(3, 2, 64, 4, dtype=bf), d["meta"], stream=S)
     with pytest.raises(ValueError):
-        binding.prune24_pack(R, d["values"], torch.zeros(3, 1, 2, 16, dtype=torch.int32), stream=S)
+        binding.prune24_pack(R, d["values"], torch.zeros(3, 1, 32, 4, dtype=torch.int32), stream=S)
     with pytest.raises(ValueError):
         binding.prune_nm_pack(R, 2, 8, d["values"].float(), d["meta"], stream=S)
     with pytest.raises(ValueError):

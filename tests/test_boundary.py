@@ -107,7 +107,7 @@ def test_packed_bytes():
     f = binding.lib().splr_packed_bytes
     vb, mb = ctypes.c_size_t(), ctypes.c_size_t()
     assert f(17, 96, 1, ctypes.byref(vb), ctypes.byref(mb)) == OK
-    assert (vb.value, mb.value) == (2 * 2 * 512 * 2, 2 * 2 * 32 * 4)
+    assert (vb.value, mb.value) == (2 * 2 * 512 * 2, 2 * 1 * 1024)   # 2 tile rows x 1 metadata block of 1 KiB
     assert f(4096, 4096, 0, ctypes.byref(vb), ctypes.byref(mb)) == OK
     assert (vb.value, mb.value) == (4096 * 4096 // 2 * 4, 4096 * 4096 // 8)
     assert f(16, 48, 1, ctypes.byref(vb), ctypes.byref(mb)) == SHAPE

@@ -109,6 +109,19 @@ def test_named_sampled_rows(cfg):
         check_layer(L, c.dtype, f"{cfg}/{L.name}", rows=rows)
 
 
+# shapes that take the 512-row prefill tile (at least 256 tiles of 512 rows x 128 tokens): ragged
+# tokens, rows and K (a 32-column tail), K shorter than the unrolled loop (padding steps), partial
+# rank blocks; compared on one row in every 128-token tile
+WIDE = [(4100, 2080, 4100, 80), (8192, 96, 4104, 16), (4096, 448, 8192, 0), (4224, 4096, 4096, 128)]
+
+
+@pytest.mark.parametrize("M,n_in,n_out,r", WIDE)
+def test_bf16_wide_tile(M, n_in, n_out, r):
+    assert -(-n_out // 512) * -(-M // 128) >= 256
+    L = inputs.random_case(M, n_in, n_out, r, "bf16", seed=M + n_in + n_out + r, n_outliers=2)
+    check_layer(L, "bf16", f"bf16 wide {M}x{n_in}->{n_out} r{r}", rows=sampled_rows(M, 11))
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("M", [16, 200])
 def test_special_cases(dtype, M):
@@ -159,6 +172,27 @@ def test_integer_exact_bitwise(M):
     vd, md = binding.prune24_pack(to_dev(R, dtype))
     Y = binding.linear(to_dev(X, dtype), vd, md, to_dev(U, dtype), to_dev(V, dtype)).cpu().numpy()
     assert np.array_equal(Y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("r", [16, 80])
+def test_integer_exact_bitwise_wide_tile(r):
+    """The 512-row prefill tile on small integers (every sum exact in float32): sampled rows equal
+    the oracle exactly, and two runs agree bit for bit."""
+    dtype, M, n_in, n_out = "bf16", 4096, 544, 4096
+    print(f"[linear] integer wide tile r={r}", flush=True)
+    X = inputs.small_integers((M, n_in), -4, 4, dtype, seed=r, tensor_id=0)
+    U = inputs.small_integers((n_out, r), -2, 2, dtype, seed=r, tensor_id=2)
+    V = inputs.small_integers((r, n_in), -2, 2, dtype, seed=r, tensor_id=3)
+    R = inputs.small_integers((n_out, n_in), -4, 4, dtype, seed=r, tensor_id=1)
+    rows = sampled_rows(M, 12)
+    v_ref, m_ref = oracle.prune24_pack(R, dtype)
+    ref = oracle.linear(X, v_ref, m_ref, n_out, U, V, dtype, rows=rows)
+    vd, md = binding.prune24_pack(to_dev(R, dtype))
+    Xd, Ud, Vd = to_dev(X, dtype), to_dev(U, dtype), to_dev(V, dtype)
+    Y = binding.linear(Xd, vd, md, Ud, Vd).cpu().numpy()
+    Y2 = binding.linear(Xd, vd, md, Ud, Vd).cpu().numpy()
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32))
+    assert np.array_equal(Y[rows].astype(np.float64), ref)
 
 
 def test_balanced_scale_lowrank():

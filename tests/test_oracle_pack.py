@@ -202,31 +202,43 @@ def test_tiled_layout_positions(dtype):
 
     Layout (our reading; the pages fix no storage format): tiles of 16 rows x 64 input columns;
     group g of row n lives in tile (n // 16, g // 16), at slot L = n % 16 + 16 * ((g % 16) // 4),
-    entries 2 * (g % 4) and 2 * (g % 4) + 1; its nibble is at bits 4 * (g % 8) of metadata word
-    ((g % 16) // 8, n % 16) of the tile. Padding is zero."""
-    n_out, n_in = 17, 96                   # 2 x 2 tiles, ragged in both directions
+    entries 2 * (g % 4) and 2 * (g % 4) + 1. Metadata: blocks of 8 tile columns per tile row,
+    meta[tile row, tk // 8, L, (tk % 8) // 2], nibble at bits 16 * (tk % 2) + 4 * (g % 4).
+    Padding is zero."""
+    n_out, n_in = 17, 96                   # 2 x 2 tiles, ragged in both directions; one block
     g = np.random.default_rng(5)
     f = g.standard_normal((n_out, n_in)) + 3.0  # all positive, no ties
     R = inputs.from_f64(f, dtype)
     kept, nib, values, meta = pack_logical(R, dtype)
-    assert values.shape == (2, 2, 64, 8) and meta.shape == (2, 2, 2, 16)
-    cases = [  # (row, group) -> (tile row, tile col, slot, entry, meta word, meta row, nibble shift)
+    assert values.shape == (2, 2, 64, 8) and meta.shape == (2, 1, 64, 4)
+    cases = [  # (row, group) -> (tile row, tile col, slot, entry, meta block, meta word, nibble shift)
         ((0, 0), (0, 0, 0, 0, 0, 0, 0)),
-        ((5, 13), (0, 0, 53, 2, 1, 5, 20)),
-        ((16, 17), (1, 1, 0, 2, 0, 0, 4)),
-        ((3, 20), (0, 1, 19, 0, 0, 3, 16)),
-        ((9, 7), (0, 0, 25, 6, 0, 9, 28)),
+        ((5, 13), (0, 0, 53, 2, 0, 0, 4)),
+        ((16, 17), (1, 1, 0, 2, 0, 0, 20)),
+        ((3, 20), (0, 1, 19, 0, 0, 0, 16)),
+        ((9, 7), (0, 0, 25, 6, 0, 0, 12)),
     ]
-    for (n, grp), (tr, tk, slot, e, w, mr, sh) in cases:
+    for (n, grp), (tr, tk, slot, e, tb, w, sh) in cases:
         assert values[tr, tk, slot, e] == kept[n, 2 * grp] and values[tr, tk, slot, e + 1] == kept[n, 2 * grp + 1]
-        assert (meta[tr, tk, w, mr] >> sh) & 0xF == nib[n, grp]
-    # column padding: the second tile column holds groups 16..23 only (slots 0..31, word 0)
-    assert not values[:, 1, 32:, :].any() and not meta[:, 1, 1, :].any()
+        assert (meta[tr, tb, slot, w] >> sh) & 0xF == nib[n, grp]
+    # column padding: the second tile column holds groups 16..23 only (slots 0..31); tile columns
+    # 2..7 of the block do not exist
+    assert not values[:, 1, 32:, :].any() and not (meta[:, 0, 32:, 0] >> 16).any()
+    assert not meta[:, :, :, 1:].any()
     # row padding: only row 16 exists in the second tile row
     rows_used = np.zeros(64, dtype=bool)
     rows_used[[0, 16, 32, 48]] = True
     assert not values[1][:, ~rows_used, :].any()
-    assert not meta[1][:, :, 1:].any()
+    assert not meta[1][:, ~rows_used, :].any()
+
+    # a second block and the upper words of a slot: 9 tile columns
+    R2 = inputs.from_f64(g.standard_normal((16, 576)) + 3.0, dtype)
+    kept2, nib2, _, meta2 = pack_logical(R2, dtype)
+    assert meta2.shape == (1, 2, 64, 4)
+    for (n, grp), (tb, slot, w, sh) in [((2, 86), (0, 18, 2, 24)), ((7, 143), (1, 55, 0, 12)),
+                                        ((15, 127), (0, 63, 3, 28)), ((0, 48), (0, 0, 1, 16))]:
+        assert (meta2[0, tb, slot, w] >> sh) & 0xF == nib2[n, grp]
+    assert not (meta2[0, 1, :, 0] >> 16).any() and not meta2[0, 1, :, 1:].any()
 
 
 def _fixture_cases():

@@ -50,7 +50,7 @@ def test_noalloc_rejects_oversized():
     U = torch.zeros((16, 1024), dtype=torch.bfloat16, device="cuda")
     TR, TK = binding.tiles(16, 64)
     vals = torch.zeros((TR, TK, 64, 8), dtype=torch.bfloat16, device="cuda")
-    meta = torch.zeros((TR, TK, 2, 16), dtype=torch.int32, device="cuda")
+    meta = torch.zeros(binding.meta_shape(16, 64), dtype=torch.int32, device="cuda")
     Y = torch.empty((16384, 16), dtype=torch.float32, device="cuda")
     assert binding.workspace_bytes(16384, 16, 64, 1024, torch.bfloat16) > 32 << 20
     with pytest.raises(binding.SplrError, match="SPLR_ERR_SCRATCH"):
