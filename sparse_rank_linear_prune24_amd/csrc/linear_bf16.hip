@@ -615,6 +615,84 @@ __device__ __forceinline__ void accumulator_fence(f32x4_t (&acc)[NI][NJ]) {
     for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
+// Operand fences: the registers passed through one were last written before it (vector-ALU
+// instructions included), and 8 wait states pass before any later instruction touches them. Placed
+// between a vector-ALU write and the first matrix-core read of a register, and after the last
+// matrix-core read of an index register before anything may overwrite it.
+template <typename A, typename B>
+__device__ __forceinline__ void operand_fence(A& a, B& b) {
+  asm volatile("s_nop 7" : "+v"(a), "+v"(b));
+}
+template <typename A, typename B, typename C, typename D>
+__device__ __forceinline__ void operand_fence(A& a, B& b, C& c, D& d) {
+  asm volatile("s_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// U's fragment rows for one 64-rank block of the rank-r term: row nrow0 + 16 i + lane % 16, ranks
+// j0 + 16 (lane / 16) .. +15 (zeros past n_out or r), as loaded; split() gives the (0,1) and (2,3)
+// halves of every group of four ranks, the A operands of the two structured-sparse MFMAs that
+// together make one dense product.
+template <int NI>
+struct UFragments {
+  u32x4_t d[NI][2];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ U, int n_out, int r, int j0, int nrow0, int lane) {
+    const int ju = j0 + 16 * (lane >> 4);
+    const u32x4_t zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int n = nrow0 + 16 * i + (lane & 15);
+      const bool ok = n < n_out && ju < r;
+      const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
+      d[i][0] = ok ? *(const u32x4_t*)p : zero;
+      d[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
+    }
+  }
+  __device__ __forceinline__ bf16x8_t pair01(int i) const {
+    return as_bf16x8(u32x4_t{d[i][0][0], d[i][0][2], d[i][1][0], d[i][1][2]});
+  }
+  __device__ __forceinline__ bf16x8_t pair23(int i) const {
+    return as_bf16x8(u32x4_t{d[i][0][1], d[i][0][3], d[i][1][1], d[i][1][3]});
+  }
+};
+
+// acc[i][j] (rows nrow0 + 16 i + ..., tokens 16 j + ...) += U[n][j0 .. j0+63] . T[token][j0 .. j0+63]
+// with the accumulators in the accumulator registers (smfmac_acc): the rank-r term of
+// lowrank_block, for the kernels that keep their accumulators there. U comes as loaded fragments,
+// T's bfloat16 pair from the LDS planes hi / lo one token fragment at a time. The MFMAs of a token
+// fragment run over the row fragments innermost, so consecutive MFMAs write different accumulators.
+template <int NI, int NJ>
+__device__ __forceinline__ void lowrank_block_acc(f32x4_t (&acc)[NI][NJ], const UFragments<NI>& uf,
+                                                  const u32x4_t* hi, const u32x4_t* lo, int lane) {
+  static_assert(NI % 2 == 0, "U fragments fenced two rows at a time");
+  const int sub = lane & 15, quad = lane >> 4;
+  bf16x8_t u01[NI], u23[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    u01[i] = uf.pair01(i);
+    u23[i] = uf.pair23(i);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; i += 2) operand_fence(u01[i], u23[i], u01[i + 1], u23[i + 1]);
+  uint32_t i01 = 0x4444u, i23 = 0xEEEEu;
+  operand_fence(i01, i23);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int row = (16 * j + sub) * kXPitchU4;
+    bf16x16_t th = cat16(as_bf16x8(hi[row + quad]), as_bf16x8(hi[row + 4 + quad]));
+    bf16x16_t tl = cat16(as_bf16x8(lo[row + quad]), as_bf16x8(lo[row + 4 + quad]));
+    operand_fence(th, tl);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u01[i], th, i01);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u23[i], th, i23);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u01[i], tl, i01);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u23[i], tl, i23);
+  }
+  operand_fence(i01, i23);  // the index registers outlive the last MFMA that reads them
+}
+
 // Prefill kernel with the accumulators in the matrix-core accumulator registers: workgroup tile
 // 16*NI*4 rows x 128 tokens, 4 waves, each owning 16*NI rows (NI S fragments) x all 128 tokens, so
 // 4*NI*8 accumulator registers per lane (NI = 8: 512 rows and 256 registers). Per 64-column K step
@@ -639,7 +717,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(P >= 2 && 16 % P == 0, "S prefetch distance dividing the unroll");
   constexpr int kUnroll = 16;  // two metadata blocks: every S, X-register and metadata ring index is constant
   constexpr int kSlot = BM * kXPitchU4;  // one LDS slot, 16-byte units
+  constexpr int kPreBlocks = 2;          // 64-rank blocks of the rank-r term run before the main loop
   __shared__ u32x4_t xs[3 * kSlot];
+  __shared__ u32x4_t tp[2 * kPreBlocks * kSlot];  // T's bfloat16 pair (hi, lo) of those blocks
 
   // XCD-aware tile order (as in the 256 x 128 kernel)
   const int b = blockIdx.x;
@@ -756,6 +836,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     lds_barrier();
   };
 
+  // The first two 64-rank blocks of the rank-r term run first (the accumulators start from U T^T),
+  // with every load they need issued together: T's float32 partials of both blocks (all slices
+  // when there are at most two), then U's fragments of block 0 once block 0's T pair is in LDS.
+  const int nrow0 = n0 + wave * 16 * NI;
+  const int r_pre = min(r, 64 * kPreBlocks);
+  accumulator_fence(acc);  // the zeros written above, before the first smfmac_acc reads them
+  if (r_pre > 0) {
+    TPairBuilder<BM, 64 * WAVES, 2> tb0, tb1;
+    tb0.init(Tpart, slices, M, r, m0, 0, threadIdx.x);
+    tb1.init(Tpart, slices, M, r, m0, 64, threadIdx.x);  // ranks >= r read as zeros
+    tb0.issue(0);
+    tb1.issue(0);
+    __builtin_amdgcn_sched_barrier(0);
+    tb0.finish(tp, tp + kSlot);
+    UFragments<NI> uf0, uf1;
+    uf0.load(U, n_out, r, 0, nrow0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    tb1.finish(tp + 2 * kSlot, tp + 3 * kSlot);
+    lds_barrier();
+    if (r_pre > 64) uf1.load(U, n_out, r, 64, nrow0, lane);
+    lowrank_block_acc<NI, NJ>(acc, uf0, tp, tp + kSlot, lane);
+    if (r_pre > 64) lowrank_block_acc<NI, NJ>(acc, uf1, tp + 2 * kSlot, tp + 3 * kSlot, lane);
+  }
+
   // Prologue: virtual steps v = -VS .. -1 issue what a step would (X of step v+2 into LDS, S of
   // step v+P-1, X of step v+2+PX), so the loop starts with the steady state's loads in flight; the
   // first metadata block goes first.
@@ -772,23 +876,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   });
   lds_barrier();
   static_for<LA>([&](auto jj) { bx[decltype(jj)::value] = read_b(0, decltype(jj)::value); });
-  accumulator_fence(acc);  // the zeros written above, before the first smfmac_acc reads them
   __builtin_amdgcn_sched_barrier(0);
   for (int kc0 = 0; kc0 < nk_pad; kc0 += kUnroll) {
     const int s0 = kc0 % 3;
     static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, s0, u); });
   }
-  accumulator_fence(acc);  // the last smfmac_acc results, before the rank-r term and the stores
-
-  // rank-r term, 64 ranks at a time: T's pair in slots 0 and 1 (the last step's barrier retired
-  // every LDS access of the loop), U fragments from memory
-  const int nrow0 = n0 + wave * 16 * NI;
-  for (int j0 = 0; j0 < r; j0 += 64) {
+  // ranks past the first kPreBlocks blocks, 64 at a time: T's pair in slots 0 and 1 (the last
+  // step's barrier retired every LDS access of the loop), U fragments from memory
+  for (int j0 = r_pre; j0 < r; j0 += 64) {
+    UFragments<NI> uf;
+    uf.load(U, n_out, r, j0, nrow0, lane);
     build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs, xs + kSlot, threadIdx.x);
     lds_barrier();
-    lowrank_block<NI, NJ>(acc, U, xs, xs + kSlot, n_out, r, j0, nrow0, lane);
+    lowrank_block_acc<NI, NJ>(acc, uf, xs, xs + kSlot, lane);
     lds_barrier();
   }
+  accumulator_fence(acc);  // the last smfmac_acc results, before the stores
   store_tile<NI, NJ, EPI == kEpiDirectNT>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
 }
 
