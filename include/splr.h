@@ -272,6 +272,38 @@ splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, c
                                      const void* V, int64_t n_out, int64_t n_in, int64_t r,
                                      splr_dtype_t dtype, float* W_hat, hipStream_t stream);
 
+/*
+ * Cholesky QR building blocks of the low-rank step of the data-free alternating minimisation
+ * (HASSLE-free page, §4.2: the low-rank update is the rank-r truncated SVD of W - S, computed here
+ * by subspace iteration on a k-column basis, k = r + oversampling). One orthonormalisation of a
+ * float32 basis Y [n][k] is G = Y^T Y (splr_gram_f64), G = R^T R and Y R^-1 (splr_chol_rinv, then
+ * a float32 matrix product); both stay on the device, so the loop synchronises with the host once
+ * per step at most.
+ *
+ * splr_gram_workspace_bytes -- device workspace splr_gram_f64 needs for (n, k) (0 if out of range).
+ *
+ * splr_gram_f64 -- G = Y^T Y in float64 (every product of two float32 values is exact in float64;
+ * rows are summed in a fixed order, so the result is deterministic).
+ *   Y         [n][k] float32, row-major (device), 4-byte aligned
+ *   G         [k][k] float64 output, both triangles written (device), 8-byte aligned
+ *   workspace device memory of at least splr_gram_workspace_bytes(n, k) bytes, 8-byte aligned;
+ *             its contents on entry do not matter
+ * Errors: NULL Y or G -> SPLR_ERR_NULL; n < 1, n > 2^20, k < 1 or k > 192 -> SPLR_ERR_SHAPE;
+ *         workspace NULL or too small -> SPLR_ERR_WORKSPACE; misaligned pointer -> SPLR_ERR_ALIGN.
+ *
+ * splr_chol_rinv -- R^-1 for the Cholesky factor of G = R^T R (R upper triangular, positive
+ * diagonal), computed in float64 and written as float32.
+ *   G    [k][k] float64 symmetric positive definite (device); only its lower triangle is read
+ *   Rinv [k][k] float32 output (device): upper triangular, zeros below the diagonal
+ * A G that is not numerically positive definite gives NaN entries (no error is reported).
+ * Errors: NULL pointer -> SPLR_ERR_NULL; k < 1 or k > 192 -> SPLR_ERR_SHAPE; misaligned pointer
+ *         (G 8 bytes, Rinv 4 bytes) -> SPLR_ERR_ALIGN.
+ */
+size_t splr_gram_workspace_bytes(int64_t n, int64_t k);
+splr_status_t splr_gram_f64(const float* Y, int64_t n, int64_t k, double* G, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+splr_status_t splr_chol_rinv(const double* G, int64_t k, float* Rinv, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* splr_status_string(splr_status_t status);
 

@@ -27,7 +27,7 @@ STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DT
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE", 7: "SPLR_ERR_SCRATCH"}
 EXPORTS = ("splr_prune24_pack", "splr_prune_nm_pack", "splr_linear_ex", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
            "splr_linear_stage1", "splr_linear_stage2", "splr_linear_noalloc", "splr_dense_reconstruct",
-           "splr_status_string", "splr_version")
+           "splr_gram_workspace_bytes", "splr_gram_f64", "splr_chol_rinv", "splr_status_string", "splr_version")
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 _lib = None
@@ -70,6 +70,12 @@ def lib() -> ctypes.CDLL:
         L.splr_linear_noalloc.restype = _I32
         L.splr_dense_reconstruct.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]
         L.splr_dense_reconstruct.restype = _I32
+        L.splr_gram_workspace_bytes.argtypes = [_I64, _I64]
+        L.splr_gram_workspace_bytes.restype = _SZ
+        L.splr_gram_f64.argtypes = [_P, _I64, _I64, _P, _P, _SZ, _P]
+        L.splr_gram_f64.restype = _I32
+        L.splr_chol_rinv.argtypes = [_P, _I64, _P, _P]
+        L.splr_chol_rinv.restype = _I32
         L.splr_status_string.argtypes = [_I32]
         L.splr_status_string.restype = ctypes.c_char_p
         L.splr_version.argtypes = []
@@ -389,6 +395,47 @@ def dense_reconstruct(values: torch.Tensor, meta: torch.Tensor, U: Optional[torc
     _check("splr_dense_reconstruct",
            lib().splr_dense_reconstruct(_dev(values, "values"), _dev(meta, "meta"), _dev(U, "U"), _dev(V, "V"),
                                         n_out, n_in, r, _dtype_code(values), _dev(out, "out"), _stream(stream)))
+    return out
+
+
+MAX_CHOL_K = 192
+
+
+def gram_f64(Y: torch.Tensor, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """G = Y^T Y in float64 for float32 Y [n, k] (k <= 192), on the device (splr_gram_f64)."""
+    n, k = _matrix(Y, "Y")
+    if not 1 <= k <= MAX_CHOL_K:
+        raise ValueError(f"Y has {k} columns; splr_gram_f64 takes 1 .. {MAX_CHOL_K}")
+    _expect(Y, "Y", torch.float32, n * k, Y.device)
+    need = int(lib().splr_gram_workspace_bytes(n, k))
+    if need == 0:
+        raise ValueError(f"Y of shape {(n, k)} is out of range for splr_gram_f64")
+    with torch.cuda.stream(_the_stream(stream)):
+        if out is None:
+            out = torch.empty((k, k), dtype=torch.float64, device=Y.device)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=Y.device)
+    _expect(out, "out", torch.float64, k * k, Y.device, (k, k))
+    if not _is_device(workspace) or workspace.device != Y.device or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor on Y's device")
+    _check("splr_gram_f64", lib().splr_gram_f64(_dev(Y, "Y"), n, k, _dev(out, "out"), _dev(workspace, "workspace"),
+                                                workspace.numel(), _stream(stream)))
+    return out
+
+
+def chol_rinv(G: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """R^-1 (float32, upper triangular) for the Cholesky factor of float64 G = R^T R [k, k]
+    (splr_chol_rinv); NaN entries when G is not numerically positive definite."""
+    k, k2 = _matrix(G, "G")
+    if k != k2 or not 1 <= k <= MAX_CHOL_K:
+        raise ValueError(f"G must be square with 1 .. {MAX_CHOL_K} rows, got {(k, k2)}")
+    _expect(G, "G", torch.float64, k * k, G.device)
+    if out is None:
+        with torch.cuda.stream(_the_stream(stream)):
+            out = torch.empty((k, k), dtype=torch.float32, device=G.device)
+    _expect(out, "out", torch.float32, k * k, G.device, (k, k))
+    _check("splr_chol_rinv", lib().splr_chol_rinv(_dev(G, "G"), k, _dev(out, "out"), _stream(stream)))
     return out
 
 

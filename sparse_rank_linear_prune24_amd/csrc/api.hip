@@ -277,6 +277,29 @@ splr_status_t splr_dense_reconstruct(const void* values, const uint32_t* meta, c
                                                  stream));
 }
 
+size_t splr_gram_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 1 || n > kMaxCols || k < 1 || k > splr::kMaxCholK) return 0;
+  return round_up(splr::gram_workspace_bytes(n, k), 256);
+}
+
+splr_status_t splr_gram_f64(const float* Y, int64_t n, int64_t k, double* G, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!Y || !G) return SPLR_ERR_NULL;
+  if (n < 1 || n > kMaxCols || k < 1 || k > splr::kMaxCholK) return SPLR_ERR_SHAPE;
+  if (!workspace || workspace_bytes < splr_gram_workspace_bytes(n, k)) return SPLR_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(Y) & 3u) || (reinterpret_cast<uintptr_t>(G) & 7u) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 7u))
+    return SPLR_ERR_ALIGN;
+  return from_hip(splr::launch_gram_f64(Y, n, k, G, workspace, stream));
+}
+
+splr_status_t splr_chol_rinv(const double* G, int64_t k, float* Rinv, hipStream_t stream) {
+  if (!G || !Rinv) return SPLR_ERR_NULL;
+  if (k < 1 || k > splr::kMaxCholK) return SPLR_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(G) & 7u) || (reinterpret_cast<uintptr_t>(Rinv) & 3u)) return SPLR_ERR_ALIGN;
+  return from_hip(splr::launch_chol_rinv(G, k, Rinv, stream));
+}
+
 const char* splr_status_string(splr_status_t status) {
   switch (status) {
     case SPLR_OK: return "SPLR_OK";

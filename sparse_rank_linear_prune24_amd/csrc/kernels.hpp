@@ -57,6 +57,14 @@ hipError_t launch_dense_reconstruct(const void* values, const uint32_t* meta, co
                                     int64_t n_out, int64_t n_in, int64_t r, bool bf16, float* W_hat,
                                     hipStream_t stream);
 
+// Cholesky QR building blocks of the low-rank step's subspace iteration (k <= kMaxCholK):
+// G = Y^T Y in float64 for float32 Y [n][k] (workspace: gram_workspace_bytes), and R^-1 (float32,
+// upper triangular, k x k) for G = R^T R.
+constexpr int kMaxCholK = 192;
+size_t gram_workspace_bytes(int64_t n, int64_t k);
+hipError_t launch_gram_f64(const float* Y, int64_t n, int64_t k, double* G, void* workspace, hipStream_t stream);
+hipError_t launch_chol_rinv(const double* G, int64_t k, float* Rinv, hipStream_t stream);
+
 // Token count up to which splr_linear takes the HBM-streaming (decode) kernel.
 constexpr int64_t kDecodeMaxTokens = 64;
 

@@ -241,3 +241,28 @@ def test_linear_noalloc_validation():
     assert ws(16384, 4096, 4096, 1024, 1) > 32 << 20 and ws(16384, 4096, 4096, 1024, 0) > 32 << 20
     assert call(M=16384, n_in=4096, n_out=4096, r=1024) == SCRATCH
     assert call(M=16384, n_in=4096, n_out=4096, r=1024, dt=0) == SCRATCH
+
+
+def test_cholqr_validation():
+    lib = binding.lib()
+    assert lib.splr_gram_workspace_bytes(4096, 80) == 128 * 80 * 80 * 8
+    assert lib.splr_gram_workspace_bytes(33, 5) % 256 == 0 and lib.splr_gram_workspace_bytes(33, 5) >= 2 * 25 * 8
+    assert lib.splr_gram_workspace_bytes(0, 8) == 0 and lib.splr_gram_workspace_bytes(8, 193) == 0
+    g = lib.splr_gram_f64
+    need = lib.splr_gram_workspace_bytes(64, 8)
+    assert g(None, 64, 8, A, A, need, None) == NULL
+    assert g(A, 64, 8, None, A, need, None) == NULL
+    assert g(A, 0, 8, A, A, need, None) == SHAPE
+    assert g(A, 64, 0, A, A, need, None) == SHAPE
+    assert g(A, 64, 193, A, A, need, None) == SHAPE
+    assert g(A, 64, 8, A, None, need, None) == WORKSPACE
+    assert g(A, 64, 8, A, A, need - 1, None) == WORKSPACE
+    assert g(A + 2, 64, 8, A, A, need, None) == ALIGN
+    assert g(A, 64, 8, A + 4, A, need, None) == ALIGN
+    c = lib.splr_chol_rinv
+    assert c(None, 8, A, None) == NULL
+    assert c(A, 8, None, None) == NULL
+    assert c(A, 0, A, None) == SHAPE
+    assert c(A, 193, A, None) == SHAPE
+    assert c(A + 4, 8, A, None) == ALIGN
+    assert c(A, 8, A + 2, None) == ALIGN

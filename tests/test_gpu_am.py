@@ -119,3 +119,19 @@ def test_low_rank_steps_match_truncated_svd(dtype):
               f"{s[r - 1] / s[r]:.2f}", flush=True)
         assert s[r - 1] / s[r] > 3
         assert err <= bound, f"step {t}: {err:.3e} > {bound:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_graph_replays_equal_eager_steps(dtype):
+    """The loop's HIP-graph mode (two graphs per step around the host round trip, captured after
+    the first step) gives the eager loop's results bit for bit at every step: the objective of every
+    replay (each one computed after the step, with the host's eigen-solve and synchronisations
+    between replays) and the final packed S and factors."""
+    n_out, n_in, r, iters = 256, 512, 16, 6
+    print(f"[am graphs] dtype={dtype} {n_out}x{n_in} r={r} iters={iters}", flush=True)
+    W = to_dev(weight(n_out, n_in, r, dtype, seed=5), dtype)
+    eager = am.alternating_minimization(W, r, iters, graphs=False)
+    graph = am.alternating_minimization(W, r, iters, graphs=True)
+    assert graph["objective"] == eager["objective"]
+    for name in ("values", "meta", "U", "V"):
+        assert torch.equal(graph[name], eager[name]), name
