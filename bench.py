@@ -58,8 +58,10 @@ MALL_DEFEAT_BYTES = 640 << 20  # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 REPEAT_SMALL = 8              # back-to-back launches per timed group when a step is small
 
-# library call -> source file of the kernel it launches (the traffic figures are tied to it)
-KERNEL_SOURCE = {"pack": "pack.hip", "stage2": "linear_bf16.hip"}
+# kernel -> the source files it is built from (the traffic figures are tied to their hash)
+KERNEL_SOURCE = {"pack": ("pack.hip", "common.hpp"),
+                 "stage2": ("linear_bf16.hip", "tile_common.hpp", "common.hpp"),
+                 "decode": ("decode.hip", "tile_common.hpp", "common.hpp")}
 
 
 def parse():
@@ -99,10 +101,23 @@ def stage2_work(L, itemsize, decode):
     return L.M * L.n_out * L.n_in + 2 * L.M * L.n_out * L.r
 
 
-def source_sha(name):
-    path = os.path.join(ROOT, "sparse_rank_linear_prune24_amd", "csrc", name)
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def prefill_kernels(layers):
+    """Which stage-2 kernel each layer's shape takes: the 512-row tile when the grid still has a
+    tile for every CU (256), else the 256-row one (the library's own rule)."""
+    names = {}
+    for L in layers:
+        wide = -(-L.n_out // 512) * -(-L.M // 128) >= 256
+        names.setdefault("linear_prefill_wide_kernel" if wide else "linear_prefill_kernel", []).append(L.name)
+    return "; ".join(f"{k} ({', '.join(v)})" for k, v in names.items())
+
+
+def source_sha(names):
+    """First 16 hex digits of the SHA-256 over the files (name, NUL, contents, NUL, in order)."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "sparse_rank_linear_prune24_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read() + b"\0")
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(kernel, workload):
@@ -313,14 +328,14 @@ def main():
     elif decode:
         ach = s2_work / s2_s / 1e9
         roofline = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                        frac=round(ach / PEAK_HBM_GBPS, 4), traffic=recorded_traffic("stage2", wl),
+                        frac=round(ach / PEAK_HBM_GBPS, 4), traffic=recorded_traffic("decode", wl),
                         kernel="linear_decode_kernel", work="bytes: packed values, metadata, U, X, T, Y")
     else:
         peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
         ach = s2_work / s2_s / 1e12
         roofline = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
                         frac=round(ach / peak, 4), traffic=recorded_traffic("stage2", wl),
-                        kernel="linear_prefill_kernel",
+                        kernel=prefill_kernels(layers) if dtype == "bf16" else "linear_f32_kernel",
                         work="algorithmic FLOP: kept 2:4 products (M n_out n_in) + rank-r epilogue (2 M n_out r)",
                         dense_equiv_TFLOPs=round(flop_step / s2_s / 1e12, 1))
 

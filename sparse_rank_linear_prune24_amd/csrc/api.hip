@@ -156,6 +156,9 @@ splr_status_t check_linear(const void* X, int64_t M, int64_t n_in, const void* v
 splr_status_t run_stage2(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                          int64_t n_out, const void* U, int64_t r, splr_dtype_t dtype, void* Y, bool y_bf16,
                          void* workspace, hipStream_t stream) {
+  if (dtype == SPLR_BF16 && M <= splr::kDecodeMaxTokens)
+    return from_hip(splr::launch_linear_decode(X, M, n_in, values, meta, n_out, U, r, (const float*)workspace,
+                                               splr::lowrank_slices(M, n_in, r, true), Y, y_bf16, stream));
   if (dtype == SPLR_BF16)
     return from_hip(splr::launch_linear_bf16(X, M, n_in, values, meta, n_out, U, r, (const float*)workspace,
                                              splr::lowrank_slices(M, n_in, r, true), Y, y_bf16, stream));

@@ -49,6 +49,11 @@ hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in,
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                               int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
                               bool y_bf16, hipStream_t stream);
+// The same for M <= kDecodeMaxTokens (decode kernel).
+bool decode_grids_fit(int64_t M, int64_t n_out);
+hipError_t launch_linear_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                                int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
+                                bool y_bf16, hipStream_t stream);
 hipError_t launch_linear_f32(const float* X, int64_t M, int64_t n_in, const float* values, const uint32_t* meta,
                              int64_t n_out, const float* U, int64_t r, const float* T, void* Y, bool y_bf16,
                              hipStream_t stream);

@@ -19,328 +19,21 @@
 // constant index operands. T (float32) enters as a bfloat16 high part plus a bfloat16 correction.
 // Y is stored once.
 //
-// Kernels:
-//   prefill -- workgroup tile 16*NI*4 rows x 16*NJ tokens, 4 waves, each owning 16*NI rows and all
-//              tokens, so every S fragment is used by one wave and goes global -> registers; X is
-//              shared through a two-slot LDS ring; P K steps of loads in flight; one barrier per
-//              K step; workgroups remapped so the tiles that one XCD (own L2) runs share X and S.
-//   decode  -- few tokens: HBM-bound on S. A workgroup owns 16 rows; its 4 waves take interleaved
-//              64-column K steps, stream S straight into registers and X through a private LDS
-//              slot each, and combine their partial accumulators through LDS in a fixed order.
-#include <type_traits>
-#include <utility>
-
+// Kernels (M > 64 tokens; fewer tokens take the decode kernel in decode.hip):
+//   prefill      -- workgroup tile 256 rows x 128 tokens, 4 waves, each owning 64 rows and all
+//                   tokens, so every S fragment is used by one wave and goes global -> registers;
+//                   X is shared through a two-slot LDS ring; P K steps of loads in flight; one
+//                   barrier per K step; workgroups remapped so the tiles that one XCD (own L2)
+//                   runs share X and S.
+//   prefill wide -- 512 rows x 128 tokens with the accumulators in the matrix-core accumulator
+//                   registers, raw buffer loads, a three-slot X ring; taken when the grid still
+//                   has a tile for every CU.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile_common.hpp"
 
 namespace splr {
 namespace {
-
-// LDS row pitch of staged X in 16-byte units (128 bytes + 32 pad). With this pitch the B-fragment
-// reads (16 rows x one 16-byte chunk per quarter wave) run at the full ds_read_b128 rate on gfx950;
-// a 16-byte pad leaves them 2-way bank conflicted.
-constexpr int kXPitchU4 = 10;
-// ranks (in blocks of 64) whose T pair the stage-2 kernels build before their main loop; larger r
-// builds it block by block after the loop
-constexpr int kPreRankBlocks = 1;
-
-
-// LDS writes of this wave complete, then workgroup barrier. One asm statement with a memory
-// clobber: the compiler moves no LDS access across it, and (unlike __syncthreads(), whose fence
-// drains every outstanding global load) it leaves the register prefetches in flight.
-// The builtin wait after it is free at run time; it tells the compiler's wait-count tracking that no
-// LDS access is outstanding, so it adds no conservative waits after the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
-}
-
-constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
-constexpr int lcm_int(int a, int b) { return a / gcd_int(a, b) * b; }
-
-// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}), in order
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// ----------------------------------------------------------------------------------- epilogue
-
-// Builds T rows m0 .. m0+ROWS-1, ranks j0 .. j0+63, as the bfloat16 pair (hi = RNE(T), lo =
-// RNE(T - hi)) in two LDS planes with the X row pitch (bytes 16c .. 16c+15 of a row hold ranks
-// j0 + 8c .. +7). T is the sum of `slices` float32 partials [slices][M][r], added in slice order.
-// All NT threads take part; thread t handles 4 consecutive ranks of a row per item, so one wave
-// load covers 4 rows x 256 contiguous bytes. Ranks >= r give zeros; rows past M repeat row M-1
-// (never stored). issue() starts the loads of a round of slices, finish() adds them (and any
-// further rounds) and writes the LDS planes, so the first round can overlap other work.
-template <int ROWS, int NT, int G = 0>
-struct TPairBuilder {
-  static constexpr int kQuads = ROWS * 16;  // 4 ranks each
-  static constexpr int kIters = (kQuads + NT - 1) / NT;
-  // slices per round: G, else as many as keep <= 16 loads in flight per thread
-  static constexpr int kGroup = G > 0 ? G : (kIters >= 8 ? 1 : 16 / kIters);
-  const float* src[kIters];
-  bool ok[kIters];
-  f32x4_t sum[kIters];
-  f32x4_t v[kIters][kGroup];
-  size_t stride;
-  int slices, tid;
-
-  __device__ __forceinline__ void init(const float* __restrict__ Tpart, int n_slices, int M, int r, int m0, int j0,
-                                       int t) {
-    stride = (size_t)M * r;
-    slices = n_slices;
-    tid = t;
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int q = tid + it * NT;
-      const int row = q >> 4, j = j0 + 4 * (q & 15);
-      ok[it] = q < kQuads && j < r;
-      src[it] = Tpart + (size_t)min(m0 + row, M - 1) * r + (ok[it] ? j : 0);
-      sum[it] = f32x4_t{0, 0, 0, 0};
-    }
-  }
-  // loads are unconditional (clamped, valid addresses) and masked when added: no lane branches
-  __device__ __forceinline__ void issue(int z0) {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it)
-#pragma unroll
-      for (int u = 0; u < kGroup; ++u)
-        v[it][u] = *(const f32x4_t*)(src[it] + (size_t)(z0 + u < slices ? z0 + u : 0) * stride);
-  }
-  __device__ __forceinline__ void accumulate(int z0) {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it)
-#pragma unroll
-      for (int u = 0; u < kGroup; ++u) sum[it] += (ok[it] && z0 + u < slices) ? v[it][u] : f32x4_t{0, 0, 0, 0};
-  }
-  __device__ __forceinline__ void finish(u32x4_t* hi, u32x4_t* lo) {
-    accumulate(0);
-    for (int z0 = kGroup; z0 < slices; z0 += kGroup) {
-      issue(z0);
-      // every load of the round is issued before the first use (under register pressure the
-      // scheduler would otherwise pair each load with its use and serialise the latencies)
-      __builtin_amdgcn_sched_barrier(0);
-      accumulate(z0);
-    }
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int q = tid + it * NT;
-      if (q >= kQuads) continue;
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = float_to_bf16_bits(sum[it][e]);
-        l[e] = float_to_bf16_bits(sum[it][e] - bf16_bits_to_float(h[e]));
-      }
-      const int o = (q >> 4) * 2 * kXPitchU4 + (q & 15);  // in 8-byte units
-      ((u32x2_t*)hi)[o] = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      ((u32x2_t*)lo)[o] = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-    }
-  }
-};
-
-template <int ROWS, int NT>
-__device__ __forceinline__ void build_t_pair(const float* __restrict__ Tpart, int slices, int M, int r, int m0,
-                                             int j0, u32x4_t* hi, u32x4_t* lo, int tid) {
-  TPairBuilder<ROWS, NT> tb;
-  tb.init(Tpart, slices, M, r, m0, j0, tid);
-  tb.issue(0);
-  __builtin_amdgcn_sched_barrier(0);
-  tb.finish(hi, lo);
-}
-
-// Stages U rows n0 .. n0+ROWS-1, ranks j0 .. j0+63 in LDS (X row pitch, bytes 16c .. 16c+15 of a row
-// = ranks j0 + 8c .. +7) with row-contiguous loads (8 rows x 128 bytes per wave load); rows past
-// n_out and ranks >= r are zero. issue() / finish() as for the T pair.
-template <int ROWS, int NT>
-struct UStager {
-  static constexpr int kChunks = ROWS * 8;
-  static constexpr int kIters = (kChunks + NT - 1) / NT;
-  u32x4_t v[kIters];
-  bool ok[kIters];
-  int tid;
-  __device__ __forceinline__ void issue(const uint16_t* __restrict__ U, int n_out, int r, int n0, int j0, int t) {
-    tid = t;
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int c = tid + it * NT;
-      const int row = c >> 3, j = j0 + 8 * (c & 7);
-      ok[it] = c < kChunks && n0 + row < n_out && j < r;
-      v[it] = *(const u32x4_t*)(U + (size_t)min(n0 + row, n_out - 1) * r + (j < r ? j : 0));
-    }
-  }
-  __device__ __forceinline__ void finish(u32x4_t* dst) {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int c = tid + it * NT;
-      if (c < kChunks) dst[(c >> 3) * kXPitchU4 + (c & 7)] = ok[it] ? v[it] : u32x4_t{0, 0, 0, 0};
-    }
-  }
-};
-
-// acc[i][j] (rows n = nrow0 + 16 i + ..., tokens = LDS rows 16 j + ...) += U[n][j0 .. j0+63] .
-// T[token][j0 .. j0+63], with T as the LDS pair built by build_t_pair. Dense U is the sum of two 2:4
-// operands with fixed patterns (ranks 0,1 and 2,3 of each group of four), and T = hi + lo, so each
-// fragment takes four structured-sparse MFMAs.
-// U comes from `ulds` when given (rows of the block staged by UStager, this wave's first row at
-// `urow0`), else from global memory.
-template <int NI, int NJ>
-__device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint16_t* __restrict__ U,
-                                              const u32x4_t* hi, const u32x4_t* lo, int n_out, int r, int j0,
-                                              int nrow0, int lane, const u32x4_t* ulds = nullptr, int urow0 = 0) {
-  const int sub = lane & 15, quad = lane >> 4;
-  const u32x4_t zero = {0, 0, 0, 0};
-  // A operand: U[n][j0 + 16q .. +15] split into the (0,1) and (2,3) positions of each group
-  const int ju = j0 + 16 * quad;
-  u32x4_t ud[NI][2];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (ulds) {
-      const int row = (urow0 + 16 * i + sub) * kXPitchU4 + 2 * quad;
-      ud[i][0] = ulds[row];
-      ud[i][1] = ulds[row + 1];
-    } else {
-      const int n = nrow0 + 16 * i + sub;
-      const bool ok = n < n_out && ju < r;
-      const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
-      ud[i][0] = ok ? *(const u32x4_t*)p : zero;
-      ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
-    }
-  }
-  // B operand: T[token][j0 + 8q .. +7] and T[token][j0 + 32 + 8q .. +7]
-  bf16x16_t th[NJ], tl[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int row = (16 * j + sub) * kXPitchU4;
-    th[j] = cat16(as_bf16x8(hi[row + quad]), as_bf16x8(hi[row + 4 + quad]));
-    tl[j] = cat16(as_bf16x8(lo[row + quad]), as_bf16x8(lo[row + 4 + quad]));
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const bf16x8_t u01 = as_bf16x8(u32x4_t{ud[i][0][0], ud[i][0][2], ud[i][1][0], ud[i][1][2]});
-    const bf16x8_t u23 = as_bf16x8(u32x4_t{ud[i][0][1], ud[i][0][3], ud[i][1][1], ud[i][1][3]});
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      acc[i][j] = smfmac16x16x64(u01, th[j], acc[i][j], 0x4444);
-      acc[i][j] = smfmac16x16x64(u23, th[j], acc[i][j], 0xEEEE);
-      acc[i][j] = smfmac16x16x64(u01, tl[j], acc[i][j], 0x4444);
-      acc[i][j] = smfmac16x16x64(u23, tl[j], acc[i][j], 0xEEEE);
-    }
-  }
-}
-
-// Store acc[i][j] (rows n = nrow0 + 16 i + 4*(lane/16) + 0..3, token m = mrow0 + 16 j + lane%16), as
-// float32, or (y_bf16) rounded to bfloat16 (to nearest even); NT: non-temporal vector stores.
-template <int NI, int NJ, bool NT = false>
-__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* __restrict__ Yv, int y_bf16, int M,
-                                           int n_out, int nrow0, int mrow0, int lane) {
-  const bool vec_ok = (n_out & 3) == 0;
-  if (y_bf16) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int m = mrow0 + 16 * j + (lane & 15);
-      if (m >= M) continue;
-      uint16_t* yrow = (uint16_t*)Yv + (size_t)m * n_out;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int n = nrow0 + 16 * i + 4 * (lane >> 4);
-        uint32_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(acc[i][j][e]);
-        if (vec_ok && n + 3 < n_out) {
-          const u32x2_t w = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-          if constexpr (NT) __builtin_nontemporal_store(w, (u32x2_t*)(yrow + n));
-          else *(u32x2_t*)(yrow + n) = w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < n_out) yrow[n + e] = (uint16_t)h[e];
-        }
-      }
-    }
-    return;
-  }
-  float* __restrict__ Y = (float*)Yv;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int m = mrow0 + 16 * j + (lane & 15);
-    if (m >= M) continue;
-    float* yrow = Y + (size_t)m * n_out;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int n = nrow0 + 16 * i + 4 * (lane >> 4);
-      if (vec_ok && n + 3 < n_out) {
-        if constexpr (NT) __builtin_nontemporal_store(acc[i][j], (f32x4_t*)(yrow + n));
-        else *(f32x4_t*)(yrow + n) = acc[i][j];
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          if (n + s < n_out) yrow[n + s] = acc[i][j][s];
-      }
-    }
-  }
-}
-
-// Store acc[i][j] like store_tile, but through a per-wave LDS buffer `buf` (64 tokens x 64 rows of
-// float32, row pitch kYPitch floats) so that the global stores are row-contiguous: the wave writes
-// its accumulators for 64 tokens into the buffer (16-byte writes, a 16-lane phase on distinct
-// banks), reads them back as 256-byte segments of token rows and stores four token rows per
-// instruction, which runs faster than storing the fragment order (16 token rows x 64 bytes per
-// instruction). All addressing is derived here from the lane and the tile origin.
-constexpr int kYPitch = 68;
-constexpr int kRowsEpilogueMaxTiles = 256;  // one workgroup per CU of MI355X
-constexpr double kNonTemporalYBytes = 192.0 * (1 << 20);
-template <int NI, int NJ>
-__device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[NI][NJ], float* buf, void* __restrict__ Yv,
-                                                int y_bf16, int M, int n_out, int nrow0, int mrow0) {
-  static_assert(NI == 4 && NJ % 4 == 0, "a wave owns 64 rows; tokens go through the buffer 64 at a time");
-  const int lane = threadIdx.x & 63;
-  const int wr = (lane & 15) * kYPitch + 4 * (lane >> 4);   // write: token lane%16, rows 4*(lane/16)
-  const int rd = (lane >> 4) * kYPitch + 4 * (lane & 15);   // read: token lane/16, rows 4*(lane%16)
-  const int n = nrow0 + 4 * (lane & 15);
-  const bool vec_ok = (n_out & 3) == 0 && n + 3 < n_out;
-#pragma unroll
-  for (int h = 0; h < NJ / 4; ++h) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int i = 0; i < NI; ++i) *(f32x4_t*)(buf + wr + 16 * jj * kYPitch + 16 * i) = acc[i][4 * h + jj];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const f32x4_t v = *(const f32x4_t*)(buf + rd + 4 * t * kYPitch);
-      const int m = mrow0 + 64 * h + 4 * t + (lane >> 4);
-      if (m >= M) continue;
-      if (y_bf16) {
-        uint16_t* yrow = (uint16_t*)Yv + (size_t)m * n_out;
-        uint32_t hb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hb[e] = float_to_bf16_bits(v[e]);
-        if (vec_ok) {
-          *(u32x2_t*)(yrow + n) = u32x2_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < n_out) yrow[n + e] = (uint16_t)hb[e];
-        }
-      } else {
-        float* yrow = (float*)Yv + (size_t)m * n_out;
-        if (vec_ok) {
-          *(f32x4_t*)(yrow + n) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < n_out) yrow[n + e] = v[e];
-        }
-      }
-    }
-  }
-}
-
 // ----------------------------------------------------------------------------------- prefill
 
 // EPI: how Y is stored -- kEpiDirect (fragment order), kEpiRows (row-contiguous through LDS),
@@ -895,144 +588,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   store_tile<NI, NJ, EPI == kEpiDirectNT>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
 }
 
-// ----------------------------------------------------------------------------------- decode
-
-template <int MB, int P, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
-    const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16, int M, int K,
-    int n_out, int r) {
-  constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
-  __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
-  __shared__ f32x4_t red[(WAVES - 1) * MB * 64];
-  __shared__ u32x4_t tpair[2 * kPreRankBlocks][16 * MB * kXPitchU4];  // as in the prefill kernel
-  // the wave index is uniform across the wave; readfirstlane lets the compiler see that (scalar
-  // loop control instead of exec-mask loops)
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sub = lane & 15, quad = lane >> 4;
-  const int tr = blockIdx.x, m0 = blockIdx.y * 16 * MB;
-  const int TK = (K + 63) / 64;
-
-  const u32x4_t* vsrc = values + (size_t)tr * TK * 64 + lane;
-  const uint16_t* msrc = (const uint16_t*)meta + ((size_t)tr * meta_blocks(TK) * 64 + lane) * 8;
-  const int xchunk = lane & 7;
-  const uint16_t* xsrc[kXLoads];
-  int xdst[kXLoads];
-#pragma unroll
-  for (int t = 0; t < kXLoads; ++t) {
-    const int tloc = 8 * t + (lane >> 3);
-    xsrc[t] = X + (size_t)min(m0 + tloc, M - 1) * K + 8 * xchunk;
-    xdst[t] = tloc * kXPitchU4 + xchunk;
-  }
-  u32x4_t* st = xs[wave];
-
-  f32x4_t acc[1][MB];
-#pragma unroll
-  for (int j = 0; j < MB; ++j) acc[0][j] = f32x4_t{0, 0, 0, 0};
-
-  // This wave's steps are kc = wave, wave + 4, ...; a ring of P steps of loads stays in flight:
-  // slot u holds step s0 + u and is refilled with step s0 + u + P as soon as it has been consumed.
-  // Branch-free: steps past the wave's last one load a clamped step and contribute through a
-  // zeroed S operand.
-  const int my_steps = (TK - wave + WAVES - 1) / WAVES;
-  const int n_pad = max(1, (my_steps + P - 1) / P) * P;  // at least the final round (a wave may have no steps)
-  u32x4_t sa[P], xr[P][kXLoads];
-  uint32_t sw[P];
-  auto load = [&](int s, u32x4_t& va, uint32_t& wa, u32x4_t (&xv)[kXLoads]) {
-    const int kc = min(wave + s * WAVES, TK - 1);
-    va = vsrc[(size_t)kc * 64];
-    wa = msrc[(size_t)(kc >> 3) * 512 + (kc & 7)];
-    int col = kc * 64;
-    if (col + 8 * xchunk >= K) col -= 32;  // half tail step: re-read valid columns (S is zero there)
-#pragma unroll
-    for (int t = 0; t < kXLoads; ++t) xv[t] = *(const u32x4_t*)(xsrc[t] + col);
-  };
-
-  // T's pair: its loads go out first, the ring's next, and the pair is written to LDS while the
-  // ring's loads are in flight (published by the barrier after the loop)
-  const bool t_pre = r <= 64 * kPreRankBlocks;
-  TPairBuilder<16 * MB, 64 * WAVES> tb;
-  if (t_pre && r > 0) {
-    tb.init(Tpart, slices, M, r, m0, 0, threadIdx.x);
-    tb.issue(0);
-  }
-  static_for<P>([&](auto uu) {  // issued in slot order (fenced), as the loop refills them
-    constexpr int u = decltype(uu)::value;
-    load(u, sa[u], sw[u], xr[u]);
-    asm volatile("" ::: "memory");
-  });
-  if (t_pre && r > 0) tb.finish(tpair[0], tpair[1]);
-
-  auto step = [&](int s, auto uu, auto refill) {
-    constexpr int u = decltype(uu)::value;
-#pragma unroll
-    for (int t = 0; t < kXLoads; ++t) st[xdst[t]] = xr[u][t];
-    const uint32_t keep = s < my_steps ? ~0u : 0u;  // wave-uniform
-    const bf16x8_t a = as_bf16x8(sa[u] & keep);
-    const int idx = (int)(sw[u] & keep);
-    if constexpr (decltype(refill)::value) load(s + P, sa[u], sw[u], xr[u]);
-    // compiler-only fence: the refill stays in this step (not rotated into the next iteration,
-    // which would shorten the prefetch distance of this slot)
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      const int row = (16 * j + sub) * kXPitchU4;
-      const bf16x16_t bx = cat16(as_bf16x8(st[row + quad]), as_bf16x8(st[row + 4 + quad]));
-      acc[0][j] = smfmac16x16x64(a, bx, acc[0][j], idx);
-    }
-  };
-  // every round but the last refills its slots; the last round loads nothing past the end
-  for (int s0 = 0; s0 + P < n_pad; s0 += P)
-    static_for<P>([&](auto uu) { step(s0 + decltype(uu)::value, uu, std::true_type{}); });
-  static_for<P>([&](auto uu) { step(n_pad - P + decltype(uu)::value, uu, std::false_type{}); });
-
-  // fixed-order combination of the waves' partial sums (into wave 0)
-  if (wave > 0) {
-#pragma unroll
-    for (int j = 0; j < MB; ++j) red[((wave - 1) * MB + j) * 64 + lane] = acc[0][j];
-  }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w)
-#pragma unroll
-      for (int j = 0; j < MB; ++j) acc[0][j] += red[((w - 1) * MB + j) * 64 + lane];
-  }
-  // rank-r term, 64 ranks at a time: wave 0 adds U T^T, with T's pair from before the loop or, for
-  // larger r, built block by block by all waves
-  if (t_pre) {
-    if (wave == 0) {
-#pragma unroll
-      for (int b = 0; b < kPreRankBlocks; ++b)
-        if (64 * b < r) lowrank_block<1, MB>(acc, U, tpair[2 * b], tpair[2 * b + 1], n_out, r, 64 * b, tr * 16, lane);
-    }
-  } else {
-    for (int j0 = 0; j0 < r; j0 += 64) {
-      build_t_pair<16 * MB, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs[0], xs[1], threadIdx.x);
-      lds_barrier();
-      if (wave == 0) lowrank_block<1, MB>(acc, U, xs[0], xs[1], n_out, r, j0, tr * 16, lane);
-      lds_barrier();
-    }
-  }
-  if (wave == 0) store_tile<1, MB>(acc, Y, y_bf16, M, n_out, tr * 16, m0, lane);
-}
-
-dim3 decode_grid(int64_t M, int64_t n_out, int MB) {
-  return dim3((unsigned)ceil_div(n_out, 16), (unsigned)ceil_div(M, 16 * MB));
-}
-
-template <int MB>
-hipError_t launch_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                         int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
-                         int y_bf16, hipStream_t stream) {
-  constexpr int P = MB == 1 ? 8 : 4, W = 4;
-  const dim3 grid = decode_grid(M, n_out, MB);
-  linear_decode_kernel<MB, P, W><<<grid, dim3(64 * W), 0, stream>>>(
-      (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, y_bf16, (int)M,
-      (int)n_in, (int)n_out, (int)r);
-  return hipGetLastError();
-}
-
 // The 512-row tile when it still gives every CU of the chip at least one tile, else 256 rows.
 constexpr int64_t kWideMinTiles = 256;
 int64_t prefill_rows(int64_t M, int64_t n_out) {
@@ -1051,7 +606,7 @@ dim3 prefill_grid(int64_t M, int64_t n_out) {
 bool linear_grids_fit(int64_t M, int64_t n_in, int64_t n_out, int64_t r, bool bf16) {
   if (!lowrank_grids_fit(M, n_in, r, bf16)) return false;
   if (!bf16) return grid_fits(linear_f32_grid(M, n_out), 256);
-  if (M <= kDecodeMaxTokens) return grid_fits(decode_grid(M, n_out, M <= 16 ? 1 : (M <= 32 ? 2 : 4)), 256);
+  if (M <= kDecodeMaxTokens) return decode_grids_fit(M, n_out);
   return grid_fits(prefill_grid(M, n_out), 256);
 }
 
@@ -1059,10 +614,6 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
                               int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
                               bool y_bf16, hipStream_t stream) {
   const int yb = y_bf16 ? 1 : 0;
-  if (M <= 16) return launch_decode<1>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, yb, stream);
-  if (M <= 32) return launch_decode<2>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, yb, stream);
-  if (M <= kDecodeMaxTokens)
-    return launch_decode<4>(X, M, n_in, values, meta, n_out, U, r, Tpart, slices, Y, yb, stream);
 
   constexpr int NI = 4, NJ = 8, P = 4, PX = 2;
   constexpr int BM = 16 * NJ;
