@@ -26,7 +26,7 @@
 //                   barrier per K step; workgroups remapped so the tiles that one XCD (own L2)
 //                   runs share X and S.
 //   prefill wide -- 512 rows x 128 tokens with the accumulators in the matrix-core accumulator
-//                   registers, raw buffer loads, a three-slot X ring; taken when the grid still
+//                   registers, raw buffer loads, a five-slot X ring; taken when the grid still
 //                   has a tile for every CU.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -411,8 +411,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int kUnroll = 16;  // two metadata blocks: every S, X-register and metadata ring index is constant
   constexpr int kSlot = BM * kXPitchU4;  // one LDS slot, 16-byte units
   constexpr int kPreBlocks = 2;          // 64-rank blocks of the rank-r term run before the main loop
-  __shared__ u32x4_t xs[3 * kSlot];
-  __shared__ u32x4_t tp[2 * kPreBlocks * kSlot];  // T's bfloat16 pair (hi, lo) of those blocks
+  // X ring: kSlots slots, X of step kc written during step kc - kLead, one barrier every kBarEvery
+  // steps. A slot is rewritten kSlots - kLead steps after its last step, and data is first read
+  // (by the B-fragment lookahead) kLead - 1 steps after it was written: both gaps hold a barrier
+  // when they span kBarEvery steps.
+  constexpr int kSlots = 5, kLead = 3, kBarEvery = 2;
+  static_assert(kSlots - kLead >= kBarEvery && kLead - 1 >= kBarEvery && 16 % kBarEvery == 0, "ring");
+  static_assert(2 * kPreBlocks <= kSlots, "T planes alias the ring");
+  __shared__ u32x4_t xs[kSlots * kSlot];
+  u32x4_t* const tp = xs;  // T's bfloat16 pair (hi, lo) of those blocks, before the ring is used
 
   // XCD-aware tile order (as in the 256 x 128 kernel)
   const int b = blockIdx.x;
@@ -495,20 +502,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
 
-  // Step kc (u = kc mod 16, LDS slots rotating with kc mod 3): X of step kc is in slot kc % 3 and
-  // its first LA B fragments are in registers; X of step kc+1 is in slot (kc+1) % 3. Issue order,
-  // in 8 groups fenced from each other: each group first issues the B fragment read LA groups ahead
-  // (past the step's last group: the first fragments of step kc+1) and its share of the step's
-  // memory work (group 0: the LDS writes of X of step kc+2 into slot (kc+2) % 3, whose last reads
-  // finished before the previous barrier; groups 1 .. NI/4: four S loads of step kc+P-1 each; the
-  // next group: the X loads of step kc+2+PX and, at a block's first step, the next block's
-  // metadata), then its NI MFMAs. One barrier per step.
+  // Step kc (u = kc mod 16, LDS slots rotating with kc mod kSlots): X of step kc is in slot
+  // kc % kSlots and its first LA B fragments are in registers; X of step kc+1 is in the next slot.
+  // Issue order, in 8 groups fenced from each other: each group first issues the B fragment read LA
+  // groups ahead (past the step's last group: the first fragments of step kc+1) and its share of the
+  // step's memory work (group 0: the LDS writes of X of step kc+kLead, whose slot's last reads
+  // finished before an earlier barrier; groups 1 .. NI/4: four S loads of step kc+P-1 each; the
+  // next group: the X loads of step kc+kLead+PX and, at a block's first step, the next block's
+  // metadata), then its NI MFMAs. A barrier after every kBarEvery-th step.
   constexpr int kXGroup = NI / 4 + 1;
   static_assert(kXGroup < NJ, "every load has a group");
   auto step = [&](int kc, int s0, auto uu) {
     constexpr int u = decltype(uu)::value;
-    constexpr int d = u % P, dprev = (u + P - 1) % P, xq = (u + 2) % PX, mq = (u / 8) % 2;
-    const int cur = (s0 + u) % 3, nxt = (s0 + u + 1) % 3, wr = (s0 + u + 2) % 3;
+    constexpr int d = u % P, dprev = (u + P - 1) % P, xq = (u + kLead) % PX, mq = (u / 8) % 2;
+    const int cur = (s0 + u) % kSlots, nxt = (s0 + u + 1) % kSlots, wr = (s0 + u + kLead) % kSlots;
     static_for<NJ>([&](auto jj) {
       constexpr int j = decltype(jj)::value;
       if constexpr (j == 0) store_x(wr, xr[xq]);
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = 4 * (j - 1); i < 4 * j; ++i) load_s_frag(kc + P - 1, i, sa[dprev][i]);
       }
       if constexpr (j == kXGroup) {
-        load_x(kc + 2 + PX, xr[xq]);
+        load_x(kc + kLead + PX, xr[xq]);
         if constexpr (u % 8 == 0) load_m(kc / 8 + 1, mb[mq ^ 1]);
       }
 #pragma unroll
@@ -526,7 +533,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         smfmac_acc<u % 2>(acc[i][j], as_bf16x8(sa[d][i]), bx[j % (LA + 1)], mb[mq][i][(u % 8) / 2]);
       __builtin_amdgcn_sched_barrier(0);
     });
-    lds_barrier();
+    if constexpr (u % kBarEvery == kBarEvery - 1) lds_barrier();
   };
 
   // The first two 64-rank blocks of the rank-r term run first (the accumulators start from U T^T),
@@ -551,27 +558,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (r_pre > 64) uf1.load(U, n_out, r, 64, nrow0, lane);
     lowrank_block_acc<NI, NJ>(acc, uf0, tp, tp + kSlot, lane);
     if (r_pre > 64) lowrank_block_acc<NI, NJ>(acc, uf1, tp + 2 * kSlot, tp + 3 * kSlot, lane);
+    lds_barrier();  // every wave's reads of the T planes are done before the ring overwrites them
   }
 
   // Prologue: virtual steps v = -VS .. -1 issue what a step would (X of step v+2 into LDS, S of
   // step v+P-1, X of step v+2+PX), so the loop starts with the steady state's loads in flight; the
   // first metadata block goes first.
   load_m(0, mb[0]);
-  constexpr int VS = (P - 1 > PX + 2) ? P - 1 : PX + 2;
+  constexpr int VS = (P - 1 > PX + kLead) ? P - 1 : PX + kLead;
   static_for<VS>([&](auto ii) {
     constexpr int v = decltype(ii)::value - VS;
-    if constexpr (v >= -2) store_x(v + 2, xr[(v + 2 + PX) % PX]);
+    if constexpr (v >= -kLead) store_x(v + kLead, xr[(v + kLead + PX) % PX]);
     if constexpr (v + P - 1 >= 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) load_s_frag(v + P - 1, i, sa[(v + P - 1) % P][i]);
     }
-    if constexpr (v + 2 + PX >= 0) load_x(v + 2 + PX, xr[(v + 2 + PX) % PX]);
+    if constexpr (v + kLead + PX >= 0) load_x(v + kLead + PX, xr[(v + kLead + PX) % PX]);
   });
   lds_barrier();
   static_for<LA>([&](auto jj) { bx[decltype(jj)::value] = read_b(0, decltype(jj)::value); });
   __builtin_amdgcn_sched_barrier(0);
   for (int kc0 = 0; kc0 < nk_pad; kc0 += kUnroll) {
-    const int s0 = kc0 % 3;
+    const int s0 = kc0 % kSlots;
     static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, s0, u); });
   }
   // ranks past the first kPreBlocks blocks, 64 at a time: T's pair in slots 0 and 1 (the last

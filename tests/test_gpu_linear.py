@@ -112,7 +112,10 @@ def test_named_sampled_rows(cfg):
 # shapes that take the 512-row prefill tile (at least 256 tiles of 512 rows x 128 tokens): ragged
 # tokens, rows and K (a 32-column tail), K shorter than the unrolled loop (padding steps), partial
 # rank blocks; compared on one row in every 128-token tile
-WIDE = [(4100, 2080, 4100, 80), (8192, 96, 4104, 16), (4096, 448, 8192, 0), (4224, 4096, 4096, 128)]
+# the 512-row tile: ragged rows and tokens, K tails, rank 0, one and two 64-rank blocks before the
+# main loop (16, 80, 128) and further blocks after it (144: a partial one; 192)
+WIDE = [(4100, 2080, 4100, 80), (8192, 96, 4104, 16), (4096, 448, 8192, 0), (4224, 4096, 4096, 128),
+        (4096, 1056, 4100, 192), (4160, 544, 4096, 144)]
 
 
 @pytest.mark.parametrize("M,n_in,n_out,r", WIDE)
@@ -174,7 +177,7 @@ def test_integer_exact_bitwise(M):
     assert np.array_equal(Y.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("r", [16, 80])
+@pytest.mark.parametrize("r", [16, 80, 144, 256])
 def test_integer_exact_bitwise_wide_tile(r):
     """The 512-row prefill tile on small integers (every sum exact in float32): sampled rows equal
     the oracle exactly, and two runs agree bit for bit."""
