@@ -329,7 +329,8 @@ def main():
         ach = s2_work / s2_s / 1e9
         roofline = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                         frac=round(ach / PEAK_HBM_GBPS, 4), traffic=recorded_traffic("decode", wl),
-                        kernel="linear_decode_kernel", work="bytes: packed values, metadata, U, X, T, Y")
+                        kernel="linear_decode_kernel" if dtype == "bf16" else "linear_f32_kernel",
+                        work="bytes: packed values, metadata, U, X, T, Y")
     else:
         peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
         ach = s2_work / s2_s / 1e12
