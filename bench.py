@@ -440,7 +440,8 @@ def measure_next(binding, inputs, layers, stream, dev, args, to_dev):
     (outside the timed step), rotating over enough copies of that layer that no call finds its data
     in the Infinity Cache: the activation-aware pack (keys |R| |d|, d = column norms of the layer's
     activations), the 2:8 projection stored in the 2:4 layout, the fused residual + pack (R = W - U V
-    formed in the kernel), the layer product with a bfloat16 Y (splr_linear_ex) and steps of the
+    formed in the kernel), the layer product with a bfloat16 Y (splr_linear_ex), stage 2 with S
+    decompressed on chip and dense MFMA against the structured-sparse stage 2, and steps of the
     data-free alternating minimisation."""
     import torch
     n = max(8, args.steps // 2)
@@ -500,6 +501,25 @@ def measure_next(binding, inputs, layers, stream, dev, args, to_dev):
         res["linear_bf16_y"] = entry("splr_linear_ex (y_dtype bfloat16)", "mfma",
                                      "dense-equivalent FLOP 2 M n_out n_in", us=round(ms * 1e3, 2),
                                      dense_equiv_TFLOPs=round(2 * L.M * L.n_out * L.n_in / (ms * 1e-3) / 1e12, 1))
+
+        # the measured choice for the sparse product: stage 2 with the structured-sparse MFMA (what
+        # splr_linear runs) against S decompressed to dense bfloat16 on chip + dense MFMA, on the same
+        # first-stage output (stage 1 run once per copy beforehand)
+        for c in cp:
+            binding.linear_stage1(c["X"], c["V"], c["ws"], stream=stream)
+        y32 = [torch.empty((L.M, L.n_out), dtype=torch.float32, device=dev) for _ in range(2)]
+        choice = {}
+        for kind, fn in (("smfmac", binding.linear_stage2), ("dense", binding.linear_stage2_dense)):
+            ms = time_per_call(lambda i: fn(cp[i % nc]["X"], cp[i % nc]["values"], cp[i % nc]["meta"], cp[i % nc]["U"],
+                                            cp[i % nc]["ws"], n_out=L.n_out, out=y32[i % 2], stream=stream),
+                               n, stream, spin)
+            choice[kind + "_us"] = round(ms * 1e3, 2)
+            choice[kind + "_dense_equiv_TFLOPs"] = round(2 * L.M * L.n_out * L.n_in / (ms * 1e-3) / 1e12, 1)
+        res["stage2_smfmac_vs_dense"] = entry(
+            "splr_linear_stage2 against splr_linear_stage2_dense", "mfma",
+            "dense-equivalent FLOP 2 M n_out n_in; the dense path issues twice the matrix-core instructions",
+            **choice, dense_over_smfmac=round(choice["dense_us"] / choice["smfmac_us"], 3))
+        del y32
     s0 = cp[0]
 
     # data-free alternating minimisation on the first layer: per-step time (untracked) and the

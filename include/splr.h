@@ -237,6 +237,28 @@ splr_status_t splr_linear_stage2(const void* X, int64_t M, int64_t n_in, const v
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * splr_linear_stage2_dense -- splr_linear_stage2 with the sparse product X S^T computed the other
+ * way gfx950 can run it: each lane expands its packed S operand (the two kept values of every group
+ * of four and their positions) to dense bfloat16 in registers, and dense MFMAs
+ * (v_mfma_f32_16x16x32_bf16, twice as many as structured-sparse ones) multiply it with the same
+ * LDS-staged X tiles; S is decompressed on chip only, never written out.  Tiles, loads, rank-r
+ * epilogue and Y store are those of the prefill kernel with the 512-row tile (its 256-row form,
+ * four waves, when 512-row tiles would leave CUs idle), for every M.  The layer product itself is
+ * the one splr_linear computes (LoSparse page, §3.2); this entry exists as the measured alternative
+ * to the structured-sparse instruction, which splr_linear uses.
+ *
+ *   Arguments: as splr_linear_stage2 (T from splr_linear_stage1 in `workspace`).
+ *   Arithmetic: the same bfloat16 products accumulated in float32, summed in another order than
+ *          splr_linear_stage2, so the two agree to rounding (bit for bit where every partial sum is
+ *          exact, e.g. small-integer inputs).  Bitwise reproducible run to run.
+ * Errors: as splr_linear_stage2; dtype other than SPLR_BF16 -> SPLR_ERR_DTYPE.
+ */
+splr_status_t splr_linear_stage2_dense(const void* X, int64_t M, int64_t n_in, const void* values,
+                                       const uint32_t* meta, int64_t n_out, const void* U, int64_t r,
+                                       splr_dtype_t dtype, float* Y, const void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * splr_linear_noalloc -- splr_linear without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, allocation-free serving loops, harnesses
  * that forbid hipMalloc).  The first-stage workspace lives in a device array inside the library,

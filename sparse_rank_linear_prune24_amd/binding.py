@@ -26,7 +26,7 @@ SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE", 7: "SPLR_ERR_SCRATCH"}
 EXPORTS = ("splr_prune24_pack", "splr_prune_nm_pack", "splr_linear_ex", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
-           "splr_linear_stage1", "splr_linear_stage2", "splr_linear_noalloc", "splr_dense_reconstruct",
+           "splr_linear_stage1", "splr_linear_stage2", "splr_linear_stage2_dense", "splr_linear_noalloc", "splr_dense_reconstruct",
            "splr_gram_workspace_bytes", "splr_gram_f64", "splr_chol_rinv", "splr_status_string", "splr_version")
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.splr_linear_stage1.restype = _I32
         L.splr_linear_stage2.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P]
         L.splr_linear_stage2.restype = _I32
+        L.splr_linear_stage2_dense.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P]
+        L.splr_linear_stage2_dense.restype = _I32
         L.splr_linear_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P]
         L.splr_linear_noalloc.restype = _I32
         L.splr_dense_reconstruct.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]
@@ -358,6 +360,21 @@ def linear_stage2(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: 
            lib().splr_linear_stage2(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
                                     _dev(U, "U"), r, _dtype_code(X), _dev(out, "out"), _dev(workspace, "workspace"),
                                     ws_bytes, _stream(stream)))
+    return out
+
+
+def linear_stage2_dense(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],
+                        workspace: Optional[torch.Tensor], n_out: Optional[int] = None,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """linear_stage2 with S expanded to dense bfloat16 on chip and multiplied by dense MFMA
+    (splr_linear_stage2_dense; bfloat16 only): the measured alternative to the structured-sparse
+    instruction."""
+    M, n_in, n_out, r, out, workspace, ws_bytes = _linear_args(X, values, meta, U, None, n_out, out, workspace, stream,
+                                                               with_workspace=False, need_v=False)
+    _check("splr_linear_stage2_dense",
+           lib().splr_linear_stage2_dense(_dev(X, "X"), M, n_in, _dev(values, "values"), _dev(meta, "meta"), n_out,
+                                          _dev(U, "U"), r, _dtype_code(X), _dev(out, "out"),
+                                          _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
     return out
 
 

@@ -208,6 +208,19 @@ splr_status_t splr_linear_stage2(const void* X, int64_t M, int64_t n_in, const v
   return run_stage2(X, M, n_in, values, meta, n_out, U, r, dtype, Y, false, const_cast<void*>(workspace), stream);
 }
 
+splr_status_t splr_linear_stage2_dense(const void* X, int64_t M, int64_t n_in, const void* values,
+                                       const uint32_t* meta, int64_t n_out, const void* U, int64_t r,
+                                       splr_dtype_t dtype, float* Y, const void* workspace, size_t ws_bytes,
+                                       hipStream_t stream) {
+  const splr_status_t s =
+      check_linear(X, M, n_in, values, meta, n_out, U, nullptr, r, dtype, Y, workspace, ws_bytes, true, false);
+  if (s != SPLR_OK) return s;
+  if (dtype != SPLR_BF16) return SPLR_ERR_DTYPE;
+  if (!splr::linear_dense_grids_fit(M, n_out)) return SPLR_ERR_SHAPE;
+  return from_hip(splr::launch_linear_bf16_dense(X, M, n_in, values, meta, n_out, U, r, (const float*)workspace,
+                                                 splr::lowrank_slices(M, n_in, r, true), Y, stream));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- splr_linear_noalloc

@@ -49,6 +49,13 @@ hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in,
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                               int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
                               bool y_bf16, hipStream_t stream);
+// Stage 2 with S decompressed to dense bfloat16 in registers and dense MFMA (the alternative to the
+// structured-sparse instruction, any M; same tiles and pipeline as the prefill kernels' 512-row
+// design: 512 rows and eight waves when that gives every CU a tile, else 256 rows and four).
+bool linear_dense_grids_fit(int64_t M, int64_t n_out);
+hipError_t launch_linear_bf16_dense(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                                    int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
+                                    hipStream_t stream);
 // The same for M <= kDecodeMaxTokens (decode kernel).
 bool decode_grids_fit(int64_t M, int64_t n_out);
 hipError_t launch_linear_decode(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,

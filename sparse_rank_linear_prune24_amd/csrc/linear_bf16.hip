@@ -295,6 +295,25 @@ __device__ __forceinline__ void smfmac_acc(f32x4_t& acc, bf16x8_t a, bf16x16_t b
   else
     asm volatile("v_smfmac_f32_16x16x64_bf16 %0, %1, %2, %3 abid:1" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
 }
+// Y[16 x 16] += A[16 x 32] . B[32 x 16], dense bfloat16 MFMA on an accumulator-register fragment
+// (the decompress-then-dense variant of the sparse product). Same output layout as smfmac_acc.
+__device__ __forceinline__ void mfma_dense_acc(f32x4_t& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Decompression of a lane's packed operand: the dense bfloat16 values of two consecutive groups of
+// four columns, from their kept pairs k0, k1 (the first kept value in the low half) and their
+// nibbles in bits 0-3 and 4-7 of nib (a | b << 2 with a < b the kept positions; nibble 0 only in
+// padding, whose kept values are zero). Returns the eight columns as four words of two bfloat16.
+__device__ __forceinline__ u32x4_t expand_groups(uint32_t k0, uint32_t k1, uint32_t nib) {
+  auto group = [](uint32_t k, uint32_t n) -> uint64_t {
+    const uint32_t a = (n & 3u) * 16u, b = ((n >> 2) & 3u) * 16u;
+    return ((uint64_t)(k & 0xFFFFu) << a) | ((uint64_t)(k >> 16) << b);
+  };
+  const uint64_t g0 = group(k0, nib & 15u), g1 = group(k1, (nib >> 4) & 15u);
+  return u32x4_t{(uint32_t)g0, (uint32_t)(g0 >> 32), (uint32_t)g1, (uint32_t)(g1 >> 32)};
+}
+
 // Wait states between accumulator writes by ordinary instructions and smfmac_acc (or the reverse),
 // followed by an empty asm per accumulator that every later use depends on, so the compiler cannot
 // move an accumulator read or write across the wait states (64 > the pass count of the 16x16x64
@@ -397,7 +416,7 @@ __device__ __forceinline__ void lowrank_block_acc(f32x4_t (&acc)[NI][NJ], const 
 // group's B fragment is read from LDS LA groups ahead of its NI MFMAs; X goes through a five-slot
 // LDS ring with a barrier every second step. The first two 64-rank blocks of the rank-r term run
 // before the main loop (their T pairs in four of the ring's slots); further blocks after it.
-template <int NI, int LA, int P, int EPI, int WAVES = 4>
+template <int NI, int LA, int P, int EPI, int WAVES = 4, bool DENSE = false>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4))) void
 linear_prefill_wide_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
@@ -474,6 +493,7 @@ linear_prefill_wide_kernel(
   u32x4_t sa[P][NI];
   u32x4_t mb[2][NI];  // metadata of the current and the next block of 8 steps
   bf16x16_t bx[LA + 1];
+  bf16x8_t bh[LA + 1];  // DENSE: B half fragments (32 columns), LA groups ahead
   const int x_end = x_rows * K * 2, v_end = rows_here * s_stride, m_end = rows_here * m_stride;
   auto load_x = [&](int kc, u32x4_t (&v)[kXLoads]) {
     // half tail step: re-read valid columns (S is zero there); per lane, as the chunk decides
@@ -497,6 +517,11 @@ linear_prefill_wide_kernel(
   auto read_b = [&](int slot, int j) {
     const int row = slot * kSlot + (16 * j + sub) * kXPitchU4;
     return cat16(as_bf16x8(xs[row + quad]), as_bf16x8(xs[row + 4 + quad]));
+  };
+  // DENSE: columns 16 quad + 8 h .. +7 of the step for token fragment j, the B operand of the
+  // half-h dense MFMA (the lane's A half holds the same columns of its row)
+  auto read_bh = [&](int slot, int j, int h) {
+    return as_bf16x8(xs[slot * kSlot + (16 * j + sub) * kXPitchU4 + 2 * quad + h]);
   };
   f32x4_t acc[NI][NJ];
 #pragma unroll
@@ -533,6 +558,46 @@ linear_prefill_wide_kernel(
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         smfmac_acc<u % 2>(acc[i][j], as_bf16x8(sa[d][i]), bx[j % (LA + 1)], mb[mq][i][(u % 8) / 2]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (u % kBarEvery == kBarEvery - 1) lds_barrier();
+  };
+  // DENSE step: the same memory work, but the product of a step runs as two halves of 32 columns.
+  // At the start of each half every fragment's kept pairs are expanded to dense bfloat16 with the
+  // step's nibbles (vector ALU, registers only); then 8 groups, one per token fragment, each read
+  // the B half fragment LA groups ahead and run NI dense MFMAs: 16 groups and 2*NI*NJ MFMAs a step.
+  auto step_dense = [&](int kc, int s0, auto uu) {
+    constexpr int u = decltype(uu)::value;
+    constexpr int d = u % P, dprev = (u + P - 1) % P, xq = (u + kLead) % PX, mq = (u / 8) % 2;
+    const int cur = (s0 + u) % kSlots, nxt = (s0 + u + 1) % kSlots, wr = (s0 + u + kLead) % kSlots;
+    u32x4_t ea[NI];
+    static_for<2 * NJ>([&](auto gg) {
+      constexpr int g = decltype(gg)::value, h = g / NJ, j = g % NJ, gn = g + LA;
+      if constexpr (j == 0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const uint32_t nib = (mb[mq][i][(u % 8) / 2] >> (16 * (u % 2) + 8 * h)) & 0xFFu;
+          ea[i] = expand_groups(sa[d][i][2 * h], sa[d][i][2 * h + 1], nib);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; i += 2) operand_fence(ea[i], ea[i + 1]);  // vector-ALU writes, then MFMA reads
+      }
+      if constexpr (g == 0) store_x(wr, xr[xq]);
+      bh[gn % (LA + 1)] = gn < 2 * NJ ? read_bh(cur, gn % NJ, gn / NJ) : read_bh(nxt, gn - 2 * NJ, 0);
+      if constexpr (g >= 1 && g < kXGroup) {
+#pragma unroll
+        for (int i = 4 * (g - 1); i < 4 * g; ++i) load_s_frag(kc + P - 1, i, sa[dprev][i]);
+      }
+      if constexpr (g == kXGroup) {
+        load_x(kc + kLead + PX, xr[xq]);
+        if constexpr (u % 8 == 0) load_m(kc / 8 + 1, mb[mq ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) mfma_dense_acc(acc[i][j], as_bf16x8(ea[i]), bh[g % (LA + 1)]);
+      if constexpr (j == NJ - 1) {
+#pragma unroll
+        for (int i = 0; i < NI; i += 2) operand_fence(ea[i], ea[i + 1]);  // last MFMA reads, then rewrites
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (u % kBarEvery == kBarEvery - 1) lds_barrier();
@@ -578,11 +643,22 @@ linear_prefill_wide_kernel(
     if constexpr (v + kLead + PX >= 0) load_x(v + kLead + PX, xr[(v + kLead + PX) % PX]);
   });
   lds_barrier();
-  static_for<LA>([&](auto jj) { bx[decltype(jj)::value] = read_b(0, decltype(jj)::value); });
+  static_for<LA>([&](auto jj) {
+    constexpr int g = decltype(jj)::value;
+    if constexpr (DENSE)
+      bh[g] = read_bh(0, g % NJ, g / NJ);
+    else
+      bx[g] = read_b(0, g);
+  });
   __builtin_amdgcn_sched_barrier(0);
   for (int kc0 = 0; kc0 < nk_pad; kc0 += kUnroll) {
     const int s0 = kc0 % kSlots;
-    static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, s0, u); });
+    static_for<kUnroll>([&](auto u) {
+      if constexpr (DENSE)
+        step_dense(kc0 + decltype(u)::value, s0, u);
+      else
+        step(kc0 + decltype(u)::value, s0, u);
+    });
   }
   // ranks past the first kPreBlocks blocks, 64 at a time: T's pair in slots 0 and 1 (the last
   // step's barrier retired every LDS access of the loop), U fragments from memory
@@ -669,6 +745,37 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
     linear_prefill_kernel<NI, NJ, P, PX, kEpiDirect><<<grid, block, 0, stream>>>(
         (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
         (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+  return hipGetLastError();
+}
+
+bool linear_dense_grids_fit(int64_t M, int64_t n_out) { return grid_fits(prefill_grid(M, n_out), 256); }
+
+hipError_t launch_linear_bf16_dense(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                                    int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
+                                    hipStream_t stream) {
+  constexpr int BM = 128;
+  const int BN = (int)prefill_rows(M, n_out);
+  const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
+  const dim3 grid = prefill_grid(M, n_out);
+  const int per_xcd = (int)grid.x / 8;
+  const int group_m = 4;
+  const bool y_nt = (double)M * n_out * 4 > kNonTemporalYBytes;
+  const auto args = [&](auto kernel, int waves) {
+    kernel<<<grid, dim3(64 * waves), 0, stream>>>((const uint16_t*)X, (const u32x4_t*)values, meta,
+                                                  (const uint16_t*)U, Tpart, slices, Y, 0, (int)M, (int)n_in,
+                                                  (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+  };
+  if (BN == 512) {
+    if (y_nt)
+      args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirectNT, 8, true>, 8);
+    else
+      args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirect, 8, true>, 8);
+  } else {
+    if (y_nt)
+      args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirectNT, 4, true>, 4);
+    else
+      args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirect, 4, true>, 4);
+  }
   return hipGetLastError();
 }
 

@@ -170,6 +170,24 @@ def test_stage_validation():
     assert s2(A, 16, 64, A, A, 32, MIS, 16, 1, A, A, wsb, None) == ALIGN
     assert s2(A, 16, 64, A, A, 32, A, 16, 1, A, None, wsb, None) == WORKSPACE
 
+def test_stage2_dense_validation():
+    """splr_linear_stage2_dense: stage 2's checks, and bfloat16 only."""
+    lib = binding.lib()
+    d = lib.splr_linear_stage2_dense
+    wsb = lib.splr_linear_workspace_bytes(16, 32, 64, 16, 1)
+    assert d(None, 16, 64, A, A, 32, A, 16, 1, A, A, wsb, None) == NULL
+    assert d(A, 16, 64, None, A, 32, A, 16, 1, A, A, wsb, None) == NULL
+    assert d(A, 16, 64, A, A, 32, None, 16, 1, A, A, wsb, None) == NULL
+    assert d(A, 16, 64, A, A, 32, A, 16, 1, None, A, wsb, None) == NULL
+    assert d(A, 16, 40, A, A, 32, A, 16, 1, A, A, wsb, None) == SHAPE
+    assert d(A, 16, 64, A, A, 0, A, 16, 1, A, A, wsb, None) == SHAPE
+    assert d(A, 16, 64, A, A, 32, A, 24, 1, A, A, wsb, None) == SHAPE
+    assert d(A, 16, 64, A, A, 32, A, 16, 1, A, MIS, wsb, None) == ALIGN
+    assert d(A, 16, 64, A, A, 32, A, 16, 1, A, None, wsb, None) == WORKSPACE
+    assert d(A, 16, 64, A, A, 32, A, 16, 3, A, A, wsb, None) == DTYPE
+    wsf = lib.splr_linear_workspace_bytes(16, 32, 64, 16, 0)
+    assert d(A, 16, 64, A, A, 32, A, 16, 0, A, A, wsf, None) == DTYPE
+
 
 def test_reconstruct_validation():
     f = binding.lib().splr_dense_reconstruct
@@ -218,6 +236,8 @@ def test_largest_sizes_pass_validation():
             assert lib.splr_linear(A, M, cols, A, A, n_out, A, A, 1024, dt, A, A, big, None) == HIP, (dt, M, n_out)
             assert lib.splr_linear_stage1(A, M, cols, A, 1024, dt, A, big, None) == HIP
             assert lib.splr_linear_stage2(A, M, cols, A, A, n_out, A, 1024, dt, A, A, big, None) == HIP
+            if dt == 1:
+                assert lib.splr_linear_stage2_dense(A, M, cols, A, A, n_out, A, 1024, dt, A, A, big, None) == HIP
         assert lib.splr_linear(A, rows, cols, A, A, cols + 16, A, A, 1024, dt, A, A, big, None) == SHAPE
 
 
