@@ -102,13 +102,13 @@ def stage2_work(L, itemsize, decode):
 
 
 def prefill_kernels(layers):
-    """Which stage-2 kernel each layer's shape takes: the 512-row tile when the grid still has a
-    tile for every CU (256), else the 256-row one (the library's own rule)."""
+    """Which stage-2 tile each layer's shape takes: 512 rows when the grid still has a tile for
+    every CU (256), else 256 rows (the library's own rule); both are linear_prefill_wide_kernel."""
     names = {}
     for L in layers:
         wide = -(-L.n_out // 512) * -(-L.M // 128) >= 256
-        names.setdefault("linear_prefill_wide_kernel" if wide else "linear_prefill_kernel", []).append(L.name)
-    return "; ".join(f"{k} ({', '.join(v)})" for k, v in names.items())
+        names.setdefault("512-row tile" if wide else "256-row tile", []).append(L.name)
+    return "linear_prefill_wide_kernel: " + "; ".join(f"{k} ({', '.join(v)})" for k, v in names.items())
 
 
 def source_sha(names):

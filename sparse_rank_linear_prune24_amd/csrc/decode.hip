@@ -19,7 +19,7 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
   constexpr int kXLoads = 2 * MB;  // 8 tokens x 128 bytes per load instruction, 16*MB tokens
   __shared__ u32x4_t xs[WAVES][16 * MB * kXPitchU4];
   __shared__ f32x4_t red[(WAVES - 1) * MB * 64];
-  __shared__ u32x4_t tpair[2 * kPreRankBlocks][16 * MB * kXPitchU4];  // as in the prefill kernel
+  __shared__ u32x4_t tpair[2 * kPreRankBlocks][16 * MB * kXPitchU4];  // T's bfloat16 pair (hi, lo)
   // the wave index is uniform across the wave; readfirstlane lets the compiler see that (scalar
   // loop control instead of exec-mask loops)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

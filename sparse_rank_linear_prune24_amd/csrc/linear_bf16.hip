@@ -12,22 +12,20 @@
 // row-major: it is loaded with row-contiguous (coalesced) 16-byte loads and staged in LDS with a
 // padded 160-byte row pitch, from which the B fragments are read without bank conflicts.
 //
-// The rank-r term is folded into the same accumulators with the same instruction (before the main
-// loop when r <= 64, so that it overlaps the loop's first loads; block by block after it otherwise):
-// dense U is the sum of two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of every group
-// of four ranks), so acc += U_tile T_tile^T is two structured-sparse MFMAs per 64 ranks with
-// constant index operands. T (float32) enters as a bfloat16 high part plus a bfloat16 correction.
-// Y is stored once.
+// The rank-r term is folded into the same accumulators with the same instruction (its first 128
+// ranks before the main loop, so that they overlap the loop's first loads; further blocks of 64
+// after it): dense U is the sum of two 2:4 matrices with fixed patterns (positions 0,1 and 2,3 of
+// every group of four ranks), so acc += U_tile T_tile^T is two structured-sparse MFMAs per 64
+// ranks with constant index operands. T (float32) enters as a bfloat16 high part plus a bfloat16
+// correction. Y is stored once.
 //
-// Kernels (M > 64 tokens; fewer tokens take the decode kernel in decode.hip):
-//   prefill      -- workgroup tile 256 rows x 128 tokens, 4 waves, each owning 64 rows and all
-//                   tokens, so every S fragment is used by one wave and goes global -> registers;
-//                   X is shared through a two-slot LDS ring; P K steps of loads in flight; one
-//                   barrier per K step; workgroups remapped so the tiles that one XCD (own L2)
-//                   runs share X and S.
-//   prefill wide -- 512 rows x 128 tokens with the accumulators in the matrix-core accumulator
-//                   registers, raw buffer loads, a five-slot X ring; taken when the grid still
-//                   has a tile for every CU.
+// One kernel template for M > 64 tokens (fewer tokens take the decode kernel in decode.hip): a
+// workgroup tile of 512 rows x 128 tokens, or 256 rows when 512-row tiles would leave CUs idle;
+// eight waves, two per SIMD, each owning 16 NI rows and all 128 tokens with its accumulators in
+// the matrix-core accumulator registers, so every S fragment is used by one wave and goes global
+// -> registers (raw buffer loads); X is shared through a five-slot LDS ring; workgroups are
+// remapped so the tiles that one XCD (own L2) runs share X and S. Its DENSE form expands S to
+// dense bfloat16 in registers and runs dense MFMAs instead (the measured alternative).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_common.hpp"
@@ -36,258 +34,22 @@ namespace splr {
 namespace {
 // ----------------------------------------------------------------------------------- prefill
 
-// EPI: how Y is stored -- kEpiDirect (fragment order), kEpiRows (row-contiguous through LDS),
-// kEpiDirectNT (fragment order, non-temporal)
-constexpr int kEpiDirect = 0, kEpiRows = 1, kEpiDirectNT = 2;
-template <int NI, int NJ, int P, int PX, int EPI>
-__global__ __launch_bounds__(256) void linear_prefill_kernel(
-    const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16,
-    int M, int K, int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
-  constexpr int WAVES = 4;
-  constexpr int BN = 16 * NI * WAVES;
-  constexpr int BM = 16 * NJ;
-  constexpr int kXLoads = BM / (8 * WAVES);  // X load instructions per wave per step (8 tokens each)
-  static_assert(BM % (8 * WAVES) == 0, "X stage must split evenly over the waves");
-  static_assert(P >= 2 && PX >= 2 && P % 2 == 0 && PX % 2 == 0, "prefetch distances must be even");
-  constexpr int kUnroll = lcm_int(P, PX);  // unroll factor: every register slot index is a constant
-  // the two LDS slots are separate objects, so the compiler may move reads of one past writes of
-  // the other
-  __shared__ u32x4_t xs0[BM * kXPitchU4];
-  __shared__ u32x4_t xs1[BM * kXPitchU4];
-  // T's bfloat16 pair for this tile's tokens (hi, lo planes per 64 ranks), built before the main
-  // loop when r <= 64 * kPreRankBlocks (registers are free then and the loads overlap the start),
-  // and this tile's U rows when r <= 64
-  __shared__ u32x4_t tpair[2 * kPreRankBlocks][BM * kXPitchU4];
-  __shared__ u32x4_t ulds[BN * kXPitchU4];
-
-  // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a contiguous range of
-  // logical tiles, walked in groups of `group_m` token tiles, so its tiles share X and S rows.
-  const int b = blockIdx.x;
-  const int logical = (b & 7) * tiles_per_xcd + (b >> 3);
-  if (logical >= tiles_n * tiles_m) return;
-  const int per_group = group_m * tiles_n;
-  const int g = logical / per_group;
-  const int first_m = g * group_m;
-  const int gsize = min(group_m, tiles_m - first_m);
-  const int in_group = logical - g * per_group;
-  const int m0 = (first_m + in_group % gsize) * BM;
-  const int n0 = (in_group / gsize) * BN;
-
-  // the wave index is uniform across the wave; readfirstlane lets the compiler see that (scalar
-  // loop control instead of exec-mask loops)
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sub = lane & 15, quad = lane >> 4;
-  const int TK = (K + 63) / 64, TR = (n_out + 15) / 16;
-  const int nk_pad = (TK + kUnroll - 1) / kUnroll * kUnroll;
-
-  // S fragments of this wave: tile rows (clamped; rows past n_out are zero padding or unused)
-  const u32x4_t* vsrc[NI];
-  const uint16_t* msrc[NI];  // this lane's 16 index bits of tile column 0: unit 0 of its slot (= lane)
-  const int TKB = meta_blocks(TK);
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int tr = min(n0 / 16 + wave * NI + i, TR - 1);
-    vsrc[i] = values + (size_t)tr * TK * 64 + lane;
-    msrc[i] = (const uint16_t*)meta + ((size_t)tr * TKB * 64 + lane) * 8;
-  }
-  // X rows this lane loads: token m0 + wave*BM/4 + 8 t + lane/8, 16-byte chunk lane%8 of a step
-  const int xchunk = lane & 7;
-  const uint16_t* xsrc[kXLoads];
-  int xdst[kXLoads];
-#pragma unroll
-  for (int t = 0; t < kXLoads; ++t) {
-    const int tloc = wave * (BM / WAVES) + 8 * t + (lane >> 3);
-    xsrc[t] = X + (size_t)min(m0 + tloc, M - 1) * K + 8 * xchunk;
-    xdst[t] = tloc * kXPitchU4 + xchunk;
-  }
-
-  u32x4_t xr[PX][kXLoads];  // X register ring: X of step kc is loaded PX steps before it goes to LDS
-  u32x4_t sa[P][NI];
-  uint32_t sw[P][NI];  // index operands, zero-extended 16-bit loads
-  bf16x16_t bx[2][NJ];
-  auto load_x = [&](int kc, u32x4_t (&v)[kXLoads]) {
-    int col = min(kc, TK - 1) * 64;
-    if (col + 8 * xchunk >= K) col -= 32;  // half tail step: re-read valid columns (S is zero there)
-#pragma unroll
-    for (int t = 0; t < kXLoads; ++t) v[t] = *(const u32x4_t*)(xsrc[t] + col);
-  };
-  auto load_s = [&](int kc, u32x4_t (&va)[NI], uint32_t (&wa)[NI]) {
-    const int kk = min(kc, TK - 1);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      va[i] = vsrc[i][(size_t)kk * 64];
-      wa[i] = msrc[i][(size_t)(kk >> 3) * 512 + (kk & 7)];
-    }
-  };
-  auto store_x = [&](u32x4_t* slot, const u32x4_t (&v)[kXLoads]) {
-#pragma unroll
-    for (int t = 0; t < kXLoads; ++t) slot[xdst[t]] = v[t];
-  };
-  auto read_b = [&](const u32x4_t* slot, bf16x16_t (&b)[NJ]) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int row = (16 * j + sub) * kXPitchU4;
-      b[j] = cat16(as_bf16x8(slot[row + quad]), as_bf16x8(slot[row + 4 + quad]));
-    }
-  };
-  f32x4_t acc[NI][NJ];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
-
-  // Software pipeline, one barrier per K step. At step kc (S register slot kc % P, X register slot
-  // (kc+2) % PX, LDS slot and B register parity b = kc % 2): the B fragments of step kc are already
-  // in registers bx[b], X of step kc+1 is in LDS slot b^1, X of step kc+2 is in registers. The step
-  // writes X of step kc+2 into LDS slot b (whose reads, of step kc, completed before the previous
-  // barrier), reads the B fragments of step kc+1 into bx[b^1] while its MFMAs run, refills the S
-  // slot of step kc-1 with step kc+P-1 and the X register slot with step kc+2+PX, and ends with the
-  // barrier. The instruction order inside a step is pinned (LDS writes, then LDS reads and global
-  // loads each paired with an MFMA), and no instruction crosses a step boundary. Padding steps
-  // (kc >= TK) zero the S operand.
-  auto step = [&](int kc, auto uu, auto masked) {
-    constexpr int u = decltype(uu)::value;
-    constexpr int d = u % P, b = u & 1, dprev = (u + P - 1) % P, xq = (u + 2) % PX;
-    store_x(b ? xs1 : xs0, xr[xq]);
-    read_b(b ? xs0 : xs1, bx[b ^ 1]);
-    const uint32_t keep = (!decltype(masked)::value || kc < TK) ? ~0u : 0u;
-    bf16x8_t a[NI];
-    int idx[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      a[i] = decltype(masked)::value ? as_bf16x8(sa[d][i] & keep) : as_bf16x8(sa[d][i]);
-      idx[i] = (int)(sw[d][i] & keep);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < NI; ++i) acc[i][j] = smfmac16x16x64(a[i], bx[b][j], acc[i][j], idx[i]);
-    load_s(kc + P - 1, sa[dprev], sw[dprev]);
-    load_x(kc + 2 + PX, xr[xq]);
-    // pinned order: the LDS writes, LDS reads and global loads are spread evenly over the MFMAs,
-    // one after each MFMA, in kXLoads rounds of (1 LDS write, 2*NJ/kXLoads LDS reads, the loads'
-    // share), so that no queue fills and blocks the in-order issue of the MFMAs
-    constexpr int kReads = 2 * NJ, kLoads = 2 * NI + kXLoads, kMfma = NI * NJ, kRounds = kXLoads;
-    static_assert(kReads % kRounds == 0 && kLoads % kRounds == 0, "even spread");
-    static_assert(kRounds * (1 + kReads / kRounds + kLoads / kRounds) <= kMfma, "one MFMA per memory op");
-#pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-#pragma unroll
-      for (int t = 0; t < kReads / kRounds; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < kLoads / kRounds; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kRounds * (1 + (kReads + kLoads) / kRounds), 0);
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // rank-r operands staged before the main loop: loads issued here, finished after the loop's
-  // prologue has issued its own loads (published by the prologue's barriers)
-  const bool t_pre = r <= 64 * kPreRankBlocks, u_pre = r <= 64;
-  TPairBuilder<BM, 64 * WAVES, 2> tb[kPreRankBlocks];
-  UStager<BN, 64 * WAVES> us;
-  if (t_pre) {
-#pragma unroll
-    for (int b = 0; b < kPreRankBlocks; ++b)
-      if (64 * b < r) {
-        tb[b].init(Tpart, slices, M, r, m0, 64 * b, threadIdx.x);
-        tb[b].issue(0);
-      }
-  }
-  if (u_pre && r > 0) us.issue(U, n_out, r, n0, 0, threadIdx.x);
-
-  // Prologue: virtual steps v = -VS .. -1 issue exactly what a step would (X of step v+2 into LDS,
-  // S of step v+P-1, X of step v+2+PX), so the loop is entered with the loads in flight in the same
-  // order as in the steady state and the wait counts the compiler derives need no extra waits.
-  constexpr int VS = (P - 1 > PX + 2) ? P - 1 : PX + 2;
-  static_for<VS>([&](auto ii) {
-    constexpr int v = decltype(ii)::value - VS;
-    if constexpr (v >= -2) store_x(((v + 2) & 1) ? xs1 : xs0, xr[(v + 2 + PX) % PX]);
-    if constexpr (v + P - 1 >= 0) load_s(v + P - 1, sa[(v + P - 1) % P], sw[(v + P - 1) % P]);
-    if constexpr (v + 2 + PX >= 0) load_x(v + 2 + PX, xr[(v + 2 + PX) % PX]);
-  });
-  if (t_pre) {
-#pragma unroll
-    for (int b = 0; b < kPreRankBlocks; ++b)
-      if (64 * b < r) tb[b].finish(tpair[2 * b], tpair[2 * b + 1]);
-  }
-  if (u_pre && r > 0) us.finish(ulds);
-  lds_barrier();
-  const int nrow0 = n0 + wave * 16 * NI;
-  // rank-r term first when T's pair is already in LDS: its MFMAs run while the main loop's first
-  // loads are in flight (the accumulators start from U T^T instead of zero)
-  if (t_pre) {
-#pragma unroll
-    for (int b = 0; b < kPreRankBlocks; ++b)
-      if (64 * b < r)
-        lowrank_block<NI, NJ>(acc, U, tpair[2 * b], tpair[2 * b + 1], n_out, r, 64 * b, nrow0, lane,
-                              u_pre ? ulds : nullptr, wave * 16 * NI);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  read_b(xs0, bx[0]);
-  lds_barrier();  // every wave's reads of slot 0 are done before step 0 overwrites it
-  __builtin_amdgcn_sched_barrier(0);
-  const int nk_full = TK / kUnroll * kUnroll;  // steps that need no masking
-  for (int kc0 = 0; kc0 < nk_full; kc0 += kUnroll)
-    static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, u, std::false_type{}); });
-  for (int kc0 = nk_full; kc0 < nk_pad; kc0 += kUnroll)
-    static_for<kUnroll>([&](auto u) { step(kc0 + decltype(u)::value, u, std::true_type{}); });
-
-  // larger r: the rank-r term, 64 ranks at a time, after the loop; the workgroup builds T's pair
-  // block by block in the now free X slots (the last step's barrier has retired every read of them)
-  // and stages the block's U rows in the U slot (unused before the loop when r > 64), the loads of
-  // both in flight together
-  if (!t_pre) {
-    for (int j0 = 0; j0 < r; j0 += 64) {
-      TPairBuilder<BM, 64 * WAVES, 2> tbp;
-      UStager<BN, 64 * WAVES> usp;
-      tbp.init(Tpart, slices, M, r, m0, j0, threadIdx.x);
-      tbp.issue(0);
-      usp.issue(U, n_out, r, n0, j0, threadIdx.x);
-      __builtin_amdgcn_sched_barrier(0);
-      tbp.finish(xs0, xs1);
-      usp.finish(ulds);
-      lds_barrier();
-      lowrank_block<NI, NJ>(acc, U, xs0, xs1, n_out, r, j0, nrow0, lane, ulds, wave * 16 * NI);
-      lds_barrier();
-    }
-  }
-  if constexpr (EPI == kEpiRows) {
-    // Y leaves through LDS (every slot is free now: the last barrier above retired all reads of
-    // them); waves 0, 1 use the T pair slot, waves 2, 3 the U slot
-    static_assert(2 * 64 * kYPitch * 4 <= (int)sizeof(tpair) && 2 * 64 * kYPitch * 4 <= (int)sizeof(ulds),
-                  "epilogue buffers fit");
-    float* ybuf = (wave < 2 ? (float*)&tpair[0][0] : (float*)&ulds[0]) + (wave & 1) * 64 * kYPitch;
-    store_tile_rows<NI, NJ>(acc, ybuf, Y, y_bf16, M, n_out, nrow0, m0);
-  } else {
-    store_tile<NI, NJ, EPI == kEpiDirectNT>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
-  }
-}
-
-// ----------------------------------------------------------------------------------- prefill, wide tile
+// EPI: how Y is stored -- kEpiDirect (fragment order), kEpiDirectNT (fragment order, non-temporal)
+constexpr int kEpiDirect = 0, kEpiDirectNT = 2;
 
 // Word 3 of a raw buffer descriptor on gfx9-family GPUs: 32-bit data format, no swizzle, no index
 // stride (plain byte-addressed loads).
 constexpr int kBufferFlags = 0x00020000;
 
 // The structured-sparse MFMA with its accumulator pinned to the matrix-core accumulator registers
-// (the compiler would otherwise spread 256 accumulators over both register files and copy them
+// (the compiler would otherwise spread the accumulators over both register files and copy them
 // every step). ABID selects the half of the 32-bit index register the instruction reads (a
 // metadata word holds the indices of two tile columns). Hazard rules this relies on, kept by the
 // kernel below: the A, B and index operands come straight from loads (the waits for loads precede
-// the instruction; no vector-ALU instruction writes an operand), an accumulator is written by these
-// instructions only and 64 instructions apart, and anything else touches the accumulators only
-// across accumulator_fence().
+// the instruction; a vector-ALU write of an operand is followed by operand_fence), an accumulator
+// is written by these instructions only (accumulating into the same registers with the same
+// instruction needs no wait states, as the compiler's own back-to-back chains show) and anything
+// else touches the accumulators only across accumulator_fence().
 template <int ABID>
 __device__ __forceinline__ void smfmac_acc(f32x4_t& acc, bf16x8_t a, bf16x16_t b, uint32_t idx) {
   if constexpr (ABID == 0)
@@ -407,16 +169,16 @@ __device__ __forceinline__ void lowrank_block_acc(f32x4_t (&acc)[NI][NJ], const 
 
 // Prefill kernel with the accumulators in the matrix-core accumulator registers: workgroup tile
 // 16*NI*WAVES rows x 128 tokens, each wave owning 16*NI rows (NI S fragments) x all 128 tokens, so
-// NI*8 accumulator fragments = 32*NI accumulator registers per lane. With WAVES = 8 (two waves per
-// SIMD, NI = 4: 512 rows) each wave has 128 accumulator and 128 arch registers, and one wave's
-// loads, LDS traffic and barrier waits overlap the other's MFMAs; WAVES = 4 (NI = 8) is the same
-// tile with one wave per SIMD and 256 + 256 registers. Per 64-column K step a CU loads 4 KiB of S
-// values per 16 rows and 16 KiB of X, and each lane loads its metadata once per 8 steps: one
-// 16-byte word group per fragment holds its indices for a whole metadata block. Each 16-token
-// group's B fragment is read from LDS LA groups ahead of its NI MFMAs; X goes through a five-slot
-// LDS ring with a barrier every second step. The first two 64-rank blocks of the rank-r term run
-// before the main loop (their T pairs in four of the ring's slots); further blocks after it.
-template <int NI, int LA, int P, int EPI, int WAVES = 4, bool DENSE = false>
+// NI*8 accumulator fragments = 32*NI accumulator registers per lane. As launched, WAVES = 8 (two
+// waves per SIMD, so one wave's loads, LDS traffic and barrier waits overlap the other's MFMAs) with
+// NI = 4 (512 rows; 128 accumulator + 128 arch registers per wave) or NI = 2 (256 rows); WAVES = 4
+// is one wave per SIMD. Per 64-column K step a CU loads 1 KiB of S values per 16 rows and 16 KiB of
+// X, and each lane loads its metadata once per 8 steps: one 16-byte word group per fragment holds
+// its indices for a whole metadata block. Each 16-token group's B fragment is read from LDS LA
+// groups ahead of its NI MFMAs; X goes through a five-slot LDS ring with a barrier every second
+// step. The first two 64-rank blocks of the rank-r term run before the main loop (their T pairs in
+// four of the ring's slots); further blocks after it.
+template <int NI, int LA, int P, int EPI, int WAVES = 8, bool DENSE = false>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4))) void
 linear_prefill_wide_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
@@ -426,7 +188,7 @@ linear_prefill_wide_kernel(
   static_assert(WAVES == 4 || WAVES == 8, "one or two waves per SIMD");
   constexpr int BN = 16 * NI * WAVES;  // 512 or 256 rows
   constexpr int BM = 16 * NJ;          // 128 tokens
-  static_assert(NI % 4 == 0 && LA >= 1 && LA < NJ, "S loads in groups of four fragments");
+  static_assert(NI % 2 == 0 && LA >= 1 && LA < NJ, "S loads in groups of up to four fragments");
   constexpr int kXLoads = BM / (8 * WAVES);
   static_assert(P >= 2 && 16 % P == 0, "S prefetch distance dividing the unroll");
   constexpr int kUnroll = 16;  // two metadata blocks: every S, X-register and metadata ring index is constant
@@ -537,7 +299,7 @@ linear_prefill_wide_kernel(
   // finished before an earlier barrier; groups 1 .. NI/4: four S loads of step kc+P-1 each; the
   // next group: the X loads of step kc+kLead+PX and, at a block's first step, the next block's
   // metadata), then its NI MFMAs. A barrier after every kBarEvery-th step.
-  constexpr int kXGroup = NI / 4 + 1;
+  constexpr int kXGroup = (NI + 3) / 4 + 1;
   static_assert(kXGroup < NJ, "every load has a group");
   auto step = [&](int kc, int s0, auto uu) {
     constexpr int u = decltype(uu)::value;
@@ -549,7 +311,7 @@ linear_prefill_wide_kernel(
       bx[(j + LA) % (LA + 1)] = j + LA < NJ ? read_b(cur, j + LA) : read_b(nxt, j + LA - NJ);
       if constexpr (j >= 1 && j < kXGroup) {
 #pragma unroll
-        for (int i = 4 * (j - 1); i < 4 * j; ++i) load_s_frag(kc + P - 1, i, sa[dprev][i]);
+        for (int i = 4 * (j - 1); i < (4 * j < NI ? 4 * j : NI); ++i) load_s_frag(kc + P - 1, i, sa[dprev][i]);
       }
       if constexpr (j == kXGroup) {
         load_x(kc + kLead + PX, xr[xq]);
@@ -586,7 +348,7 @@ linear_prefill_wide_kernel(
       bh[gn % (LA + 1)] = gn < 2 * NJ ? read_bh(cur, gn % NJ, gn / NJ) : read_bh(nxt, gn - 2 * NJ, 0);
       if constexpr (g >= 1 && g < kXGroup) {
 #pragma unroll
-        for (int i = 4 * (g - 1); i < 4 * g; ++i) load_s_frag(kc + P - 1, i, sa[dprev][i]);
+        for (int i = 4 * (g - 1); i < (4 * g < NI ? 4 * g : NI); ++i) load_s_frag(kc + P - 1, i, sa[dprev][i]);
       }
       if constexpr (g == kXGroup) {
         load_x(kc + kLead + PX, xr[xq]);
@@ -700,51 +462,36 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
                               int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
                               bool y_bf16, hipStream_t stream) {
   const int yb = y_bf16 ? 1 : 0;
-
-  constexpr int NI = 4, NJ = 8, P = 4, PX = 2;
-  constexpr int BM = 16 * NJ;
+  constexpr int BM = 128;
   const int BN = (int)prefill_rows(M, n_out);
   const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
-  const int n_tiles = tiles_n * tiles_m;
   const dim3 grid = prefill_grid(M, n_out);
   const int per_xcd = (int)grid.x / 8;
   const int group_m = 4;
-  // When every tile runs at once (one workgroup per CU), the Y stores of all tiles come at the end
-  // together and are exposed: the row-contiguous epilogue stores them faster. With several tiles per
-  // CU the stores overlap the next tile's loop, and with r > 64 the extra registers of that
-  // epilogue cost spills in the rank-r blocks after the loop: there the direct epilogue is faster.
   // A Y larger than three quarters of the 256 MB Infinity Cache is stored non-temporally: kept in the
   // cache it evicts the S and X rows that later tile groups re-read (measured: -6 to -11 % on
   // 4096/8192 tokens x 14336 outputs; +5 % slower on 8192 x 4096, 134 MB, so the threshold sits
   // between).
   const bool y_nt = (double)M * n_out * (y_bf16 ? 2 : 4) > kNonTemporalYBytes;
-  const dim3 block(256);
+  // eight waves, two per SIMD, each owning 16 NI rows x 128 tokens: NI = 4 for the 512-row tile, 2 for
+  // the 256-row one (measured against one wave per SIMD with twice the rows: 3-6 % faster on the
+  // 512-row tiles, 8 % on the 256-row tiles)
+  const auto launch = [&](auto kernel) {
+    kernel<<<grid, dim3(512), 0, stream>>>((const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U,
+                                           Tpart, slices, Y, yb, (int)M, (int)n_in, (int)n_out, (int)r, tiles_n,
+                                           tiles_m, per_xcd, group_m);
+  };
   if (BN == 512) {
-    // eight waves, two per SIMD, 64 rows each (measured against four waves of 128 rows: 3-6 % faster
-    // on the 8192-token layers; Y bit-identical)
-    constexpr int kWideWaves = 8, kWideNI = 512 / (16 * kWideWaves);
     if (y_nt)
-      linear_prefill_wide_kernel<kWideNI, 1, 2, kEpiDirectNT, kWideWaves><<<grid, dim3(64 * kWideWaves), 0, stream>>>(
-          (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
-          (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+      launch(linear_prefill_wide_kernel<4, 1, 2, kEpiDirectNT, 8>);
     else
-      linear_prefill_wide_kernel<kWideNI, 1, 2, kEpiDirect, kWideWaves><<<grid, dim3(64 * kWideWaves), 0, stream>>>(
-          (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
-          (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
-    return hipGetLastError();
+      launch(linear_prefill_wide_kernel<4, 1, 2, kEpiDirect, 8>);
+  } else {
+    if (y_nt)
+      launch(linear_prefill_wide_kernel<2, 1, 2, kEpiDirectNT, 8>);
+    else
+      launch(linear_prefill_wide_kernel<2, 1, 2, kEpiDirect, 8>);
   }
-  if (n_tiles <= kRowsEpilogueMaxTiles && r <= 64)
-    linear_prefill_kernel<NI, NJ, P, PX, kEpiRows><<<grid, block, 0, stream>>>(
-        (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
-        (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
-  else if (y_nt)
-    linear_prefill_kernel<NI, NJ, P, PX, kEpiDirectNT><<<grid, block, 0, stream>>>(
-        (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
-        (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
-  else
-    linear_prefill_kernel<NI, NJ, P, PX, kEpiDirect><<<grid, block, 0, stream>>>(
-        (const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U, Tpart, slices, Y, yb, (int)M,
-        (int)n_in, (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
   return hipGetLastError();
 }
 
@@ -772,9 +519,9 @@ hipError_t launch_linear_bf16_dense(const void* X, int64_t M, int64_t n_in, cons
       args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirect, 8, true>, 8);
   } else {
     if (y_nt)
-      args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirectNT, 4, true>, 4);
+      args(linear_prefill_wide_kernel<2, 1, 2, kEpiDirectNT, 8, true>, 8);
     else
-      args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirect, 4, true>, 4);
+      args(linear_prefill_wide_kernel<2, 1, 2, kEpiDirect, 8, true>, 8);
   }
   return hipGetLastError();
 }

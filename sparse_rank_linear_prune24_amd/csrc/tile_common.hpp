@@ -1,6 +1,6 @@
 // Device helpers shared by the layer-product kernels (prefill in linear_bf16.hip, decode in
 // decode.hip): the LDS barrier that keeps register prefetches in flight, compile-time loops, the
-// T pair builder and U stager of the rank-r term, the rank-r MFMA block and the Y stores.
+// T pair builder of the rank-r term, the rank-r MFMA block and the Y store.
 #pragma once
 
 #include <type_traits>
@@ -15,8 +15,8 @@ namespace {
 // reads (16 rows x one 16-byte chunk per quarter wave) run at the full ds_read_b128 rate on gfx950;
 // a 16-byte pad leaves them 2-way bank conflicted.
 constexpr int kXPitchU4 = 10;
-// ranks (in blocks of 64) whose T pair the stage-2 kernels build before their main loop; larger r
-// builds it block by block after the loop
+// ranks (in blocks of 64) whose T pair the decode kernel builds before its K loop; larger r builds
+// it block by block after the loop
 constexpr int kPreRankBlocks = 1;
 
 
@@ -30,8 +30,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
 }
 
-constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
-constexpr int lcm_int(int a, int b) { return a / gcd_int(a, b) * b; }
 
 // f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}), in order
 template <typename F, int... I>
@@ -129,45 +127,15 @@ __device__ __forceinline__ void build_t_pair(const float* __restrict__ Tpart, in
   tb.finish(hi, lo);
 }
 
-// Stages U rows n0 .. n0+ROWS-1, ranks j0 .. j0+63 in LDS (X row pitch, bytes 16c .. 16c+15 of a row
-// = ranks j0 + 8c .. +7) with row-contiguous loads (8 rows x 128 bytes per wave load); rows past
-// n_out and ranks >= r are zero. issue() / finish() as for the T pair.
-template <int ROWS, int NT>
-struct UStager {
-  static constexpr int kChunks = ROWS * 8;
-  static constexpr int kIters = (kChunks + NT - 1) / NT;
-  u32x4_t v[kIters];
-  bool ok[kIters];
-  int tid;
-  __device__ __forceinline__ void issue(const uint16_t* __restrict__ U, int n_out, int r, int n0, int j0, int t) {
-    tid = t;
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int c = tid + it * NT;
-      const int row = c >> 3, j = j0 + 8 * (c & 7);
-      ok[it] = c < kChunks && n0 + row < n_out && j < r;
-      v[it] = *(const u32x4_t*)(U + (size_t)min(n0 + row, n_out - 1) * r + (j < r ? j : 0));
-    }
-  }
-  __device__ __forceinline__ void finish(u32x4_t* dst) {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int c = tid + it * NT;
-      if (c < kChunks) dst[(c >> 3) * kXPitchU4 + (c & 7)] = ok[it] ? v[it] : u32x4_t{0, 0, 0, 0};
-    }
-  }
-};
-
 // acc[i][j] (rows n = nrow0 + 16 i + ..., tokens = LDS rows 16 j + ...) += U[n][j0 .. j0+63] .
 // T[token][j0 .. j0+63], with T as the LDS pair built by build_t_pair. Dense U is the sum of two 2:4
 // operands with fixed patterns (ranks 0,1 and 2,3 of each group of four), and T = hi + lo, so each
 // fragment takes four structured-sparse MFMAs.
-// U comes from `ulds` when given (rows of the block staged by UStager, this wave's first row at
-// `urow0`), else from global memory.
+// U comes from global memory (rows past n_out and ranks >= r read as zero).
 template <int NI, int NJ>
 __device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint16_t* __restrict__ U,
                                               const u32x4_t* hi, const u32x4_t* lo, int n_out, int r, int j0,
-                                              int nrow0, int lane, const u32x4_t* ulds = nullptr, int urow0 = 0) {
+                                              int nrow0, int lane) {
   const int sub = lane & 15, quad = lane >> 4;
   const u32x4_t zero = {0, 0, 0, 0};
   // A operand: U[n][j0 + 16q .. +15] split into the (0,1) and (2,3) positions of each group
@@ -175,17 +143,11 @@ __device__ __forceinline__ void lowrank_block(f32x4_t (&acc)[NI][NJ], const uint
   u32x4_t ud[NI][2];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    if (ulds) {
-      const int row = (urow0 + 16 * i + sub) * kXPitchU4 + 2 * quad;
-      ud[i][0] = ulds[row];
-      ud[i][1] = ulds[row + 1];
-    } else {
-      const int n = nrow0 + 16 * i + sub;
-      const bool ok = n < n_out && ju < r;
-      const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
-      ud[i][0] = ok ? *(const u32x4_t*)p : zero;
-      ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
-    }
+    const int n = nrow0 + 16 * i + sub;
+    const bool ok = n < n_out && ju < r;
+    const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
+    ud[i][0] = ok ? *(const u32x4_t*)p : zero;
+    ud[i][1] = ok ? *(const u32x4_t*)(p + 8) : zero;
   }
   // B operand: T[token][j0 + 8q .. +7] and T[token][j0 + 32 + 8q .. +7]
   bf16x16_t th[NJ], tl[NJ];
@@ -261,60 +223,8 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* _
   }
 }
 
-// Store acc[i][j] like store_tile, but through a per-wave LDS buffer `buf` (64 tokens x 64 rows of
-// float32, row pitch kYPitch floats) so that the global stores are row-contiguous: the wave writes
-// its accumulators for 64 tokens into the buffer (16-byte writes, a 16-lane phase on distinct
-// banks), reads them back as 256-byte segments of token rows and stores four token rows per
-// instruction, which runs faster than storing the fragment order (16 token rows x 64 bytes per
-// instruction). All addressing is derived here from the lane and the tile origin.
-constexpr int kYPitch = 68;
-constexpr int kRowsEpilogueMaxTiles = 256;  // one workgroup per CU of MI355X
+// Y bytes above which the prefill kernels store Y non-temporally
 constexpr double kNonTemporalYBytes = 192.0 * (1 << 20);
-template <int NI, int NJ>
-__device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[NI][NJ], float* buf, void* __restrict__ Yv,
-                                                int y_bf16, int M, int n_out, int nrow0, int mrow0) {
-  static_assert(NI == 4 && NJ % 4 == 0, "a wave owns 64 rows; tokens go through the buffer 64 at a time");
-  const int lane = threadIdx.x & 63;
-  const int wr = (lane & 15) * kYPitch + 4 * (lane >> 4);   // write: token lane%16, rows 4*(lane/16)
-  const int rd = (lane >> 4) * kYPitch + 4 * (lane & 15);   // read: token lane/16, rows 4*(lane%16)
-  const int n = nrow0 + 4 * (lane & 15);
-  const bool vec_ok = (n_out & 3) == 0 && n + 3 < n_out;
-#pragma unroll
-  for (int h = 0; h < NJ / 4; ++h) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int i = 0; i < NI; ++i) *(f32x4_t*)(buf + wr + 16 * jj * kYPitch + 16 * i) = acc[i][4 * h + jj];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const f32x4_t v = *(const f32x4_t*)(buf + rd + 4 * t * kYPitch);
-      const int m = mrow0 + 64 * h + 4 * t + (lane >> 4);
-      if (m >= M) continue;
-      if (y_bf16) {
-        uint16_t* yrow = (uint16_t*)Yv + (size_t)m * n_out;
-        uint32_t hb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hb[e] = float_to_bf16_bits(v[e]);
-        if (vec_ok) {
-          *(u32x2_t*)(yrow + n) = u32x2_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < n_out) yrow[n + e] = (uint16_t)hb[e];
-        }
-      } else {
-        float* yrow = (float*)Yv + (size_t)m * n_out;
-        if (vec_ok) {
-          *(f32x4_t*)(yrow + n) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < n_out) yrow[n + e] = v[e];
-        }
-      }
-    }
-  }
-}
 
 }  // namespace
 }  // namespace splr
