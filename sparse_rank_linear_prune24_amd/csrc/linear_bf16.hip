@@ -34,8 +34,67 @@ namespace splr {
 namespace {
 // ----------------------------------------------------------------------------------- prefill
 
-// EPI: how Y is stored -- kEpiDirect (fragment order), kEpiDirectNT (fragment order, non-temporal)
-constexpr int kEpiDirect = 0, kEpiDirectNT = 2;
+// EPI: how Y is stored -- bit 0: through LDS as whole token rows (else in fragment order), bit 1:
+// non-temporal stores
+constexpr int kEpiDirect = 0, kEpiRows = 1, kEpiDirectNT = 2, kEpiRowsNT = 3;
+
+// Stores a wave's accumulators acc[i][j] (rows nrow0 + 16 i + 4 (lane / 16) + 0..3, tokens
+// m0 + 16 j + lane % 16) through `buf`, a private LDS region of the wave (32 tokens x (16 NI + 4)
+// floats), 32 tokens at a time: each global store instruction then writes whole token rows of the
+// wave's 16 NI outputs (64 NI contiguous bytes per token), i.e. whole cache lines, where the fragment
+// order writes 16-byte pieces of 16 token rows. float32, or (y_bf16) rounded to bfloat16 (to
+// nearest even); NT: non-temporal stores. The wave reads only what it wrote, in order, so no barrier
+// is needed between the phases.
+template <int NI, int NJ, bool NT>
+__device__ __forceinline__ void store_tile_rows_lds(const f32x4_t (&acc)[NI][NJ], float* buf, void* __restrict__ Yv,
+                                                    int y_bf16, int M, int n_out, int nrow0, int m0, int lane) {
+  constexpr int R = 16 * NI, kPitch = R + 4, kTok = 32;
+  constexpr int kLanesPerTok = R / 4, kTokPerRead = 64 / kLanesPerTok;
+  static_assert(NJ % 2 == 0 && kTok % kTokPerRead == 0, "32 tokens a round");
+  const int q = lane >> 4, sb = lane & 15;
+  const int rl = lane % kLanesPerTok, tl = lane / kLanesPerTok;
+  const int n = nrow0 + 4 * rl;
+  const bool vec_ok = (n_out & 3) == 0 && n + 3 < n_out;
+#pragma unroll
+  for (int c = 0; c < NJ / 2; ++c) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) *(f32x4_t*)(buf + (16 * jj + sb) * kPitch + 16 * i + 4 * q) = acc[i][2 * c + jj];
+#pragma unroll
+    for (int k = 0; k < kTok / kTokPerRead; ++k) {
+      const int t = k * kTokPerRead + tl;
+      const f32x4_t v = *(const f32x4_t*)(buf + t * kPitch + 4 * rl);
+      const int m = m0 + 32 * c + t;
+      if (m >= M) continue;
+      if (y_bf16) {
+        uint16_t* yrow = (uint16_t*)Yv + (size_t)m * n_out;
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = float_to_bf16_bits(v[e]);
+        if (vec_ok) {
+          const u32x2_t w = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          if constexpr (NT) __builtin_nontemporal_store(w, (u32x2_t*)(yrow + n));
+          else *(u32x2_t*)(yrow + n) = w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < n_out) yrow[n + e] = (uint16_t)h[e];
+        }
+      } else {
+        float* yrow = (float*)Yv + (size_t)m * n_out;
+        if (vec_ok) {
+          if constexpr (NT) __builtin_nontemporal_store(v, (f32x4_t*)(yrow + n));
+          else *(f32x4_t*)(yrow + n) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < n_out) yrow[n + e] = v[e];
+        }
+      }
+    }
+  }
+}
 
 // Word 3 of a raw buffer descriptor on gfx9-family GPUs: 32-bit data format, no swizzle, no index
 // stride (plain byte-addressed loads).
@@ -433,7 +492,14 @@ linear_prefill_wide_kernel(
     lds_barrier();
   }
   accumulator_fence(acc);  // the last smfmac_acc results, before the stores
-  store_tile<NI, NJ, EPI == kEpiDirectNT>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
+  if constexpr ((EPI & kEpiRows) != 0) {
+    static_assert(WAVES * 32 * (16 * NI + 4) * 4 <= (int)sizeof(xs), "a private buffer per wave");
+    lds_barrier();  // every wave's reads of the ring are done before it is reused
+    store_tile_rows_lds<NI, NJ, (EPI & kEpiDirectNT) != 0>(acc, (float*)xs + wave * 32 * (16 * NI + 4), Y, y_bf16, M,
+                                                          n_out, nrow0, m0, lane);
+  } else {
+    store_tile<NI, NJ, (EPI & kEpiDirectNT) != 0>(acc, Y, y_bf16, M, n_out, nrow0, m0, lane);
+  }
 }
 
 // The 512-row tile when it still gives every CU of the chip at least one tile, else 256 rows.
@@ -468,10 +534,12 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   const dim3 grid = prefill_grid(M, n_out);
   const int per_xcd = (int)grid.x / 8;
   const int group_m = 4;
-  // A Y larger than three quarters of the 256 MB Infinity Cache is stored non-temporally: kept in the
-  // cache it evicts the S and X rows that later tile groups re-read (measured: -6 to -11 % on
-  // 4096/8192 tokens x 14336 outputs; +5 % slower on 8192 x 4096, 134 MB, so the threshold sits
-  // between).
+  // A Y larger than three quarters of the 256 MB Infinity Cache is stored non-temporally (kept in the
+  // cache it evicts the S and X rows that later tile groups re-read), and as whole token rows through
+  // LDS: non-temporal 16-byte fragment pieces would leave partial cache lines (a 470 MB Y counted as
+  // 727 MB of writes). Measured against fragment stores: -5.5 % at 4096/8192 tokens x 14336 outputs.
+  // Smaller Y: row stores for the 256-row tiles, whose one or two rounds leave the final stores
+  // exposed (-1 to -3 %); fragment stores for the 512-row tiles (the row transpose measured +1-2 %).
   const bool y_nt = (double)M * n_out * (y_bf16 ? 2 : 4) > kNonTemporalYBytes;
   // eight waves, two per SIMD, each owning 16 NI rows x 128 tokens: NI = 4 for the 512-row tile, 2 for
   // the 256-row one (measured against one wave per SIMD with twice the rows: 3-6 % faster on the
@@ -483,14 +551,11 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   };
   if (BN == 512) {
     if (y_nt)
-      launch(linear_prefill_wide_kernel<4, 1, 2, kEpiDirectNT, 8>);
+      launch(linear_prefill_wide_kernel<4, 1, 2, kEpiRowsNT, 8>);
     else
       launch(linear_prefill_wide_kernel<4, 1, 2, kEpiDirect, 8>);
-  } else {
-    if (y_nt)
-      launch(linear_prefill_wide_kernel<2, 1, 2, kEpiDirectNT, 8>);
-    else
-      launch(linear_prefill_wide_kernel<2, 1, 2, kEpiDirect, 8>);
+  } else {  // fewer than 256 tiles of 512 rows: Y is below 17 M elements, never non-temporal
+    launch(linear_prefill_wide_kernel<2, 1, 2, kEpiRows, 8>);
   }
   return hipGetLastError();
 }
@@ -514,14 +579,11 @@ hipError_t launch_linear_bf16_dense(const void* X, int64_t M, int64_t n_in, cons
   };
   if (BN == 512) {
     if (y_nt)
-      args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirectNT, 8, true>, 8);
+      args(linear_prefill_wide_kernel<4, 1, 2, kEpiRowsNT, 8, true>, 8);
     else
       args(linear_prefill_wide_kernel<4, 1, 2, kEpiDirect, 8, true>, 8);
   } else {
-    if (y_nt)
-      args(linear_prefill_wide_kernel<2, 1, 2, kEpiDirectNT, 8, true>, 8);
-    else
-      args(linear_prefill_wide_kernel<2, 1, 2, kEpiDirect, 8, true>, 8);
+    args(linear_prefill_wide_kernel<2, 1, 2, kEpiRows, 8, true>, 8);
   }
   return hipGetLastError();
 }
