@@ -431,17 +431,18 @@ linear_prefill_wide_kernel(
   const int r_pre = min(r, 64 * kPreBlocks);
   accumulator_fence(acc);  // the zeros written above, before the first smfmac_acc reads them
   if (r_pre > 0) {
+    const bool two = r_pre > 64;  // wave-uniform: the second block's T pair is built only when used
     TPairBuilder<BM, 64 * WAVES, 2> tb0, tb1;
     tb0.init(Tpart, slices, M, r, m0, 0, threadIdx.x);
     tb1.init(Tpart, slices, M, r, m0, 64, threadIdx.x);  // ranks >= r read as zeros
     tb0.issue(0);
-    tb1.issue(0);
+    if (two) tb1.issue(0);
     __builtin_amdgcn_sched_barrier(0);
     tb0.finish(tp, tp + kSlot);
     UFragments<NI> uf0, uf1;
     uf0.load(U, n_out, r, 0, nrow0, lane);
     __builtin_amdgcn_sched_barrier(0);
-    tb1.finish(tp + 2 * kSlot, tp + 3 * kSlot);
+    if (two) tb1.finish(tp + 2 * kSlot, tp + 3 * kSlot);
     lds_barrier();
     if (r_pre > 64) uf1.load(U, n_out, r, 64, nrow0, lane);
     lowrank_block_acc<NI, NJ>(acc, uf0, tp, tp + kSlot, lane);
