@@ -21,6 +21,11 @@ __device__ __forceinline__ void linear_f32_output(const float* __restrict__ X, c
   const float* v = values + (size_t)(n / 16) * TK * 512;  // this row's tile row
   const int TKB = meta_blocks(TK);
   float acc = 0.0f;
+  // unrolled so that the metadata, value and X loads of 16 groups are in flight together (measured
+  // at 32 tokens x 512 x 512: 36 -> 13 us; loading each group's four X values at once and picking
+  // two in registers instead of the indexed loads ran 29 us); the sum still runs over the groups in
+  // order
+#pragma unroll 16
   for (int grp = 0; grp < K / 4; ++grp) {
     const int tk = grp / 16, gi = grp % 16;
     const uint32_t nib = (meta_unit(meta, TKB, n / 16, tk, n % 16 + 16 * (gi / 4)) >> (4 * (gi % 4))) & 0xFu;
@@ -29,6 +34,7 @@ __device__ __forceinline__ void linear_f32_output(const float* __restrict__ X, c
     acc = fmaf(x[4 * grp + (nib >> 2)], kept[1], acc);
   }
   float lr = 0.0f;
+#pragma unroll 8
   for (int j = 0; j < r; ++j) lr = fmaf(T[(size_t)m * r + j], U[(size_t)n * r + j], lr);
   const float y = acc + lr;
   if (y_bf16) ((uint16_t*)Y)[(size_t)m * n_out + n] = (uint16_t)float_to_bf16_bits(y);
