@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--workload", default="C5",
                    help="C1..C5 (default: C5, the Llama-3-8B block linear set, 8192 tokens, rank 128)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    p.add_argument("--no-group", action="store_true",
+                   help="one stage-2 launch per layer (no grouped launch of equal-shape layers)")
     p.add_argument("--no-next", action="store_true", help="skip the measurements of the parts beyond the hot path")
     p.add_argument("--no-context", action="store_true", help="skip the same-run reference points (profiling runs)")
     p.add_argument("--cpu-rows", type=int, default=0, help="token rows of the oracle sample (0 = auto)")
@@ -101,13 +103,42 @@ def stage2_work(L, itemsize, decode):
     return L.M * L.n_out * L.n_in + 2 * L.M * L.n_out * L.r
 
 
-def prefill_kernels(layers):
-    """Which stage-2 tile each layer's shape takes: 512 rows when the grid still has a tile for
-    every CU (256), else 256 rows (the library's own rule); both are linear_prefill_wide_kernel."""
+def wide_tile(L, count=1):
+    """The library's tile rule: 512-row tiles when the launch's layers together give every CU
+    (256) a tile of 512 rows x 128 tokens, else 256 rows."""
+    return count * -(-L.n_out // 512) * -(-L.M // 128) >= 256
+
+
+def stage2_units(layers, decode):
+    """The step's stage-2 launches: adjacent layers of one shape go into one grouped launch
+    (splr_linear_stage2_group) when alone they would take 256-row tiles and together 512-row ones
+    (k_proj and v_proj of the block); every other layer is a launch of its own."""
+    units = []
+    for li, L in enumerate(layers):
+        prev = units[-1] if units else None
+        if (not decode and prev is not None and len(prev) < 4 and not wide_tile(L)
+                and (layers[prev[0]].n_in, layers[prev[0]].n_out, layers[prev[0]].r) == (L.n_in, L.n_out, L.r)
+                and all(not wide_tile(layers[j]) for j in prev)):
+            prev.append(li)
+        else:
+            units.append([li])
+    # keep a group only where it changes the tile
+    out = []
+    for u in units:
+        if len(u) > 1 and not wide_tile(layers[u[0]], len(u)):
+            out.extend([j] for j in u)
+        else:
+            out.append(u)
+    return out
+
+
+def prefill_kernels(layers, units):
+    """Which stage-2 tile each launch takes (both are linear_prefill_wide_kernel)."""
     names = {}
-    for L in layers:
-        wide = -(-L.n_out // 512) * -(-L.M // 128) >= 256
-        names.setdefault("512-row tile" if wide else "256-row tile", []).append(L.name)
+    for u in units:
+        L = layers[u[0]]
+        key = "512-row tile" if wide_tile(L, len(u)) else "256-row tile"
+        names.setdefault(key, []).append("+".join(layers[j].name for j in u) + (" grouped" if len(u) > 1 else ""))
     return "linear_prefill_wide_kernel: " + "; ".join(f"{k} ({', '.join(v)})" for k, v in names.items())
 
 
@@ -209,34 +240,49 @@ def main():
     def stage1(d):
         binding.linear_stage1(d["X"], d["V"], d["ws"], stream=stream)
 
-    def stage2(d):
-        binding.linear_stage2(d["X"], d["values"], d["meta"], d["U"], d["ws"], n_out=d["Y"].shape[1], out=d["Y"],
-                              stream=stream)
+    units = [[li] for li in range(n_layers)] if args.no_group else stage2_units(layers, decode)
 
-    fns = dict(pack=pack, stage1=stage1, stage2=stage2)
+    def stage2(s, unit):
+        """Stage 2 of the layers in `unit` (indices into the copy s): one launch either way."""
+        if len(unit) == 1:
+            d = s[unit[0]]
+            binding.linear_stage2(d["X"], d["values"], d["meta"], d["U"], d["ws"], n_out=d["Y"].shape[1],
+                                  out=d["Y"], stream=stream)
+        else:
+            ds = [s[j] for j in unit]
+            binding.linear_stage2_group([d["X"] for d in ds], [d["values"] for d in ds], [d["meta"] for d in ds],
+                                        [d["U"] for d in ds], [d["ws"] for d in ds], n_out=ds[0]["Y"].shape[1],
+                                        outs=[d["Y"] for d in ds], stream=stream)
+
+    def call(c, s, unit):
+        if c == "stage2":
+            stage2(s, unit)
+        else:
+            (pack if c == "pack" else stage1)(s[unit[0]])
 
     def step(i):
-        """Step i on `stream`, on copy i % copies: every layer's pack (prefill workloads), then every
-        layer's two stages."""
+        """Step i on `stream`, on copy i % copies: every layer's pack (prefill workloads), then for
+        each stage-2 launch the first stage of its layers and the launch."""
         s = sets[i % copies]
         if not decode:
             for d in s:
                 pack(d)
-        for d in s:
-            stage1(d)
-            stage2(d)
+        for unit in units:
+            for li in unit:
+                stage1(s[li])
+            stage2(s, unit)
 
     def step_timed(i, ev):
         """Step i of the per-kernel region: each call issued `repeat` times on `repeat` consecutive
-        copies (starting at copy i * repeat), ev[c][li] recorded after the group of call c of layer li.
-        The stages of one layer read the workspace of their own copy."""
+        copies (starting at copy i * repeat), ev[c][li] recorded after the group of call c whose
+        (first) layer is li. The stages of one layer read the workspace of their own copy."""
         base = i * repeat
-        order = ([("pack", li) for li in range(n_layers)] if not decode else []) + \
-                [(c, li) for li in range(n_layers) for c in ("stage1", "stage2")]
-        for c, li in order:
+        order = ([("pack", [li]) for li in range(n_layers)] if not decode else []) + \
+                [(c, u) for unit in units for c, u in [("stage1", [li]) for li in unit] + [("stage2", unit)]]
+        for c, unit in order:
             for j in range(repeat):
-                fns[c](sets[(base + j) % copies][li])
-            ev[calls.index(c)][li].record(stream)
+                call(c, sets[(base + j) % copies], unit)
+            ev[calls.index(c)][unit[0]].record(stream)
         return order
 
     with torch.cuda.stream(stream):
@@ -285,9 +331,9 @@ def main():
     call_ms = {c: np.zeros(n_layers) for c in ("pack", "stage1", "stage2")}
     prev = first
     for i, ev in enumerate(evs):
-        for c, li in orders[i]:
-            e = ev[calls.index(c)][li]
-            call_ms[c][li] += prev.elapsed_time(e)
+        for c, unit in orders[i]:
+            e = ev[calls.index(c)][unit[0]]
+            call_ms[c][unit[0]] += prev.elapsed_time(e)
             prev = e
     for c in calls:
         call_ms[c] = call_ms[c] / (args.steps * repeat)
@@ -305,14 +351,22 @@ def main():
     pbytes_step = sum(pack_bytes(L.n_in, L.n_out, isz) for L in layers)
     s2_work = sum(stage2_work(L, isz, decode) for L in layers)
 
+    # a grouped stage-2 launch is timed once; each of its layers is shown with an equal share
+    s2_share = np.zeros(n_layers)
+    groups = []
+    for unit in units:
+        s2_share[unit] = call_ms["stage2"][unit[0]] / len(unit)
+        if len(unit) > 1:
+            groups.append(dict(layers=[layers[j].name for j in unit], entry="splr_linear_stage2_group",
+                               stage2_us=round(call_ms["stage2"][unit[0]] * 1e3, 2)))
     per_layer = []
     for li, L in enumerate(layers):
         pb = pack_bytes(L.n_in, L.n_out, isz)
-        lin = call_ms["stage1"][li] + call_ms["stage2"][li]
+        lin = call_ms["stage1"][li] + s2_share[li]
         per_layer.append(dict(
             layer=L.name, pack_us=round(call_ms["pack"][li] * 1e3, 2),
             pack_GBps=round(pb / (call_ms["pack"][li] * 1e-3) / 1e9, 1),
-            stage1_us=round(call_ms["stage1"][li] * 1e3, 2), stage2_us=round(call_ms["stage2"][li] * 1e3, 2),
+            stage1_us=round(call_ms["stage1"][li] * 1e3, 2), stage2_us=round(s2_share[li] * 1e3, 2),
             linear_dense_equiv_TFLOPs=round(2 * L.M * L.n_out * L.n_in / (lin * 1e-3) / 1e12, 1),
             linear_weight_GBps=round(layer_bytes(L.n_in, L.n_out, L.r, isz) / (lin * 1e-3) / 1e9, 1)))
 
@@ -336,7 +390,7 @@ def main():
         ach = s2_work / s2_s / 1e12
         roofline = dict(bound="mfma", achieved=round(ach, 1), peak=peak, unit="TFLOP/s",
                         frac=round(ach / peak, 4), traffic=recorded_traffic("stage2", wl),
-                        kernel=prefill_kernels(layers) if dtype == "bf16" else "linear_f32_kernel",
+                        kernel=prefill_kernels(layers, units) if dtype == "bf16" else "linear_f32_kernel",
                         work="algorithmic FLOP: kept 2:4 products (M n_out n_in) + rank-r epilogue (2 M n_out r)",
                         dense_equiv_TFLOPs=round(flop_step / s2_s / 1e12, 1))
 
@@ -347,7 +401,9 @@ def main():
 
     step_desc = ("splr_linear (stage 1 + stage 2) on every layer; the layer's prune24_pack is timed beside the "
                  "step (kernels.per_layer.pack_us)" if decode else
-                 "prune24_pack on every layer's residual, then splr_linear (stage 1 + stage 2) on every layer")
+                 "prune24_pack on every layer's residual, then splr_linear (stage 1 + stage 2) on every layer"
+                 + ("; stage 2 of " + ", ".join("+".join(g["layers"]) for g in groups)
+                    + " as one grouped launch (splr_linear_stage2_group)" if groups else ""))
     out = dict(
         metric=METRIC, value=round(value, 2), unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
@@ -357,7 +413,7 @@ def main():
                     launch="graph replay" if graphs else "stream, queue pre-filled", parallelism="single GPU",
                     copies_rotated=copies, per_kernel_repeat=repeat),
         roofline=roofline,
-        kernels=dict(per_layer=per_layer,
+        kernels=dict(per_layer=per_layer, stage2_groups=groups,
                      pack_GBps=round(pbytes_step / (call_ms["pack"].sum() * 1e-3) / 1e9, 1),
                      linear_dense_equiv_TFLOPs=round(
                          flop_step / ((call_ms["stage1"].sum() + call_ms["stage2"].sum()) * 1e-3) / 1e12, 1),

@@ -259,6 +259,40 @@ splr_status_t splr_linear_stage2_dense(const void* X, int64_t M, int64_t n_in, c
                                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * splr_linear_group / splr_linear_stage2_group -- splr_linear (or its stage 2) for `count` layers
+ * of one shape at once, e.g. the two 1024-output projections of an attention block, whose forward
+ * passes are each the sum of the sparse and the low-rank product (LoSparse page, §3.2).  Stage 2
+ * of all the layers runs as one launch of the prefill kernel whose grid holds every layer's tiles,
+ * so layers too small to give each compute unit a 512-row tile on their own can still use that
+ * tile (k_proj and v_proj of a Llama-3-8B block at 8192 tokens: 128 tiles each, 256 together).
+ *
+ *   Arguments: host arrays of `count` device pointers (X, values, meta, U, V, Y, workspace), entry
+ *          i belonging to layer i; the sizes M, n_in, n_out, r and the dtype are shared, and each
+ *          layer's buffers mean what they mean for splr_linear.  U and V may be NULL (the arrays)
+ *          iff r == 0.  Every layer has its own workspace of at least `workspace_bytes`
+ *          (splr_linear_workspace_bytes of the shared sizes); the stage-2 form reads T there as
+ *          splr_linear_stage1 of that layer left it.  Outputs must not alias each other or any
+ *          input.
+ *   Results: Y[i] bit for bit what splr_linear (or splr_linear_stage2) gives for layer i alone.
+ *          splr_linear_group runs stage 1 of each layer in turn, then the grouped stage 2.  For
+ *          M <= 64 tokens and for float32 the layers run one after the other (the decode and
+ *          float32 kernels take a layer per launch).
+ * Errors: count outside 1..SPLR_GROUP_MAX -> SPLR_ERR_SHAPE; a NULL array -> SPLR_ERR_NULL;
+ *         otherwise as splr_linear for each layer (every layer checked before any HIP call).
+ */
+#define SPLR_GROUP_MAX 4
+splr_status_t splr_linear_group(int32_t count, const void* const* X, int64_t M, int64_t n_in,
+                                const void* const* values, const uint32_t* const* meta, int64_t n_out,
+                                const void* const* U, const void* const* V, int64_t r, splr_dtype_t dtype,
+                                float* const* Y, void* const* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+splr_status_t splr_linear_stage2_group(int32_t count, const void* const* X, int64_t M, int64_t n_in,
+                                       const void* const* values, const uint32_t* const* meta, int64_t n_out,
+                                       const void* const* U, int64_t r, splr_dtype_t dtype, float* const* Y,
+                                       const void* const* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * splr_linear_noalloc -- splr_linear without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, allocation-free serving loops, harnesses
  * that forbid hipMalloc).  The first-stage workspace lives in a device array inside the library,

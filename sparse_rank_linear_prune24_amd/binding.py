@@ -15,7 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -26,7 +26,8 @@ SPLR_FP32, SPLR_BF16 = 0, 1
 STATUS = {0: "SPLR_OK", 1: "SPLR_ERR_NULL", 2: "SPLR_ERR_SHAPE", 3: "SPLR_ERR_DTYPE", 4: "SPLR_ERR_ALIGN",
           5: "SPLR_ERR_HIP", 6: "SPLR_ERR_WORKSPACE", 7: "SPLR_ERR_SCRATCH"}
 EXPORTS = ("splr_prune24_pack", "splr_prune_nm_pack", "splr_linear_ex", "splr_prune24_pack_scaled", "splr_prune24_pack_residual", "splr_packed_bytes", "splr_linear_workspace_bytes", "splr_linear",
-           "splr_linear_stage1", "splr_linear_stage2", "splr_linear_stage2_dense", "splr_linear_noalloc", "splr_dense_reconstruct",
+           "splr_linear_stage1", "splr_linear_stage2", "splr_linear_stage2_dense", "splr_linear_group",
+           "splr_linear_stage2_group", "splr_linear_noalloc", "splr_dense_reconstruct",
            "splr_gram_workspace_bytes", "splr_gram_f64", "splr_chol_rinv", "splr_status_string", "splr_version")
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -68,6 +69,10 @@ def lib() -> ctypes.CDLL:
         L.splr_linear_stage2.restype = _I32
         L.splr_linear_stage2_dense.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P]
         L.splr_linear_stage2_dense.restype = _I32
+        L.splr_linear_group.argtypes = [_I32, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P, _SZ, _P]
+        L.splr_linear_group.restype = _I32
+        L.splr_linear_stage2_group.argtypes = [_I32, _P, _I64, _I64, _P, _P, _I64, _P, _I64, _I32, _P, _P, _SZ, _P]
+        L.splr_linear_stage2_group.restype = _I32
         L.splr_linear_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _P, _P]
         L.splr_linear_noalloc.restype = _I32
         L.splr_dense_reconstruct.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P]
@@ -361,6 +366,78 @@ def linear_stage2(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: 
                                     _dev(U, "U"), r, _dtype_code(X), _dev(out, "out"), _dev(workspace, "workspace"),
                                     ws_bytes, _stream(stream)))
     return out
+
+
+GROUP_MAX = 4  # SPLR_GROUP_MAX
+
+
+def _ptr_array(ts, name):
+    """A host array of the tensors' device pointers (None for a missing list)."""
+    if ts is None:
+        return None
+    return (ctypes.c_void_p * len(ts))(*[_dev(t, f"{name}[{i}]") for i, t in enumerate(ts)])
+
+
+def _group_args(Xs, values, metas, Us, Vs, n_out, outs, workspaces, stream, with_stage1):
+    """Checks every layer as the single-layer call would (allocating missing outputs and workspaces
+    on the call's stream) and that the layers share their sizes and type."""
+    count = len(Xs)
+    if not 1 <= count <= GROUP_MAX:
+        raise ValueError(f"a group holds 1..{GROUP_MAX} layers, got {count}")
+    for name, lst in (("values", values), ("meta", metas), ("U", Us), ("V", Vs), ("outs", outs),
+                      ("workspaces", workspaces)):
+        if lst is not None and len(lst) != count:
+            raise ValueError(f"{name} has {len(lst)} entries for {count} layers")
+    per = []
+    for i in range(count):
+        U = None if Us is None else Us[i]
+        V = None if Vs is None else Vs[i]
+        out = None if outs is None else outs[i]
+        ws = None if workspaces is None else workspaces[i]
+        per.append(_linear_args(Xs[i], values[i], metas[i], U, V if with_stage1 else None, n_out, out, ws, stream,
+                                with_workspace=with_stage1, need_v=with_stage1))
+    shape = per[0][:4]
+    if any(p[:4] != shape for p in per) or any(X.dtype != Xs[0].dtype for X in Xs):
+        raise ValueError("the layers of a group share M, n_in, n_out, r and the storage type")
+    M, n_in, n_out, r = shape
+    outs = [p[4] for p in per]
+    wss = [p[5] for p in per]
+    ws_bytes = min(p[6] for p in per)
+    return count, M, n_in, n_out, r, outs, wss, ws_bytes
+
+
+def linear_group(Xs: Sequence[torch.Tensor], values: Sequence[torch.Tensor], metas: Sequence[torch.Tensor],
+                 Us: Optional[Sequence[torch.Tensor]], Vs: Optional[Sequence[torch.Tensor]],
+                 n_out: Optional[int] = None, outs: Optional[Sequence[torch.Tensor]] = None,
+                 workspaces: Optional[Sequence[torch.Tensor]] = None, stream=None) -> List[torch.Tensor]:
+    """splr_linear for up to GROUP_MAX layers of one shape, stage 2 of all of them in one launch
+    (splr_linear_group); returns the layers' Y, each bit for bit its splr_linear result."""
+    count, M, n_in, n_out, r, outs, wss, ws_bytes = _group_args(Xs, values, metas, Us, Vs, n_out, outs, workspaces,
+                                                                stream, True)
+    ws_arr = _ptr_array(wss, "workspace") if r > 0 else (ctypes.c_void_p * count)()
+    _check("splr_linear_group",
+           lib().splr_linear_group(count, _ptr_array(Xs, "X"), M, n_in, _ptr_array(values, "values"),
+                                   _ptr_array(metas, "meta"), n_out, _ptr_array(Us, "U") if r > 0 else None,
+                                   _ptr_array(Vs, "V") if r > 0 else None, r, _dtype_code(Xs[0]),
+                                   _ptr_array(outs, "out"), ws_arr, ws_bytes, _stream(stream)))
+    return outs
+
+
+def linear_stage2_group(Xs: Sequence[torch.Tensor], values: Sequence[torch.Tensor], metas: Sequence[torch.Tensor],
+                        Us: Optional[Sequence[torch.Tensor]], workspaces: Optional[Sequence[torch.Tensor]],
+                        n_out: Optional[int] = None, outs: Optional[Sequence[torch.Tensor]] = None,
+                        stream=None) -> List[torch.Tensor]:
+    """linear_stage2 for up to GROUP_MAX layers of one shape in one launch (splr_linear_stage2_group),
+    each layer's T left in its workspace by linear_stage1."""
+    count, M, n_in, n_out, r, outs, wss, ws_bytes = _group_args(Xs, values, metas, Us, None, n_out, outs, workspaces,
+                                                                stream, False)
+    ws_arr = _ptr_array(wss, "workspace") if r > 0 else (ctypes.c_void_p * count)()
+    _check("splr_linear_stage2_group",
+           lib().splr_linear_stage2_group(count, _ptr_array(Xs, "X"), M, n_in, _ptr_array(values, "values"),
+                                          _ptr_array(metas, "meta"), n_out, _ptr_array(Us, "U") if r > 0 else None,
+                                          r, _dtype_code(Xs[0]), _ptr_array(outs, "out"), ws_arr, ws_bytes,
+                                          _stream(stream)))
+    return outs
 
 
 def linear_stage2_dense(X: torch.Tensor, values: torch.Tensor, meta: torch.Tensor, U: Optional[torch.Tensor],

@@ -166,6 +166,50 @@ splr_status_t run_stage2(const void* X, int64_t M, int64_t n_in, const void* val
                                           (const float*)U, r, (const float*)workspace, Y, y_bf16, stream));
 }
 
+// Layers of one shape: every layer is checked as splr_linear (or its stage 2) checks it before the
+// first HIP call; with stage 1 (with_stage1) each layer's T goes to its own workspace, then the
+// stage-2 products run as one launch when the prefill kernel takes them, else layer by layer.
+splr_status_t run_group(int32_t count, const void* const* X, int64_t M, int64_t n_in, const void* const* values,
+                        const uint32_t* const* meta, int64_t n_out, const void* const* U, const void* const* V,
+                        int64_t r, splr_dtype_t dtype, float* const* Y, const void* const* workspace,
+                        size_t ws_bytes, bool with_stage1, hipStream_t stream) {
+  static_assert(SPLR_GROUP_MAX == splr::kMaxGroup, "header and library agree");
+  if (count < 1 || count > splr::kMaxGroup) return SPLR_ERR_SHAPE;
+  if (!X || !values || !meta || !Y || !workspace || (r > 0 && !U) || (with_stage1 && r > 0 && !V))
+    return SPLR_ERR_NULL;
+  for (int32_t i = 0; i < count; ++i) {
+    const splr_status_t s =
+        check_linear(X[i], M, n_in, values[i], meta[i], n_out, r > 0 ? U[i] : nullptr,
+                     with_stage1 && r > 0 ? V[i] : nullptr, r, dtype, Y[i], workspace[i], ws_bytes, true, with_stage1);
+    if (s != SPLR_OK) return s;
+  }
+  const bool grouped = dtype == SPLR_BF16 && M > splr::kDecodeMaxTokens;
+  if (grouped && !splr::linear_group_grid_fits(M, n_out, count)) return SPLR_ERR_SHAPE;
+  if (with_stage1)
+    for (int32_t i = 0; i < count; ++i)
+      if (splr::launch_lowrank(X[i], V ? V[i] : nullptr, M, n_in, r, dtype == SPLR_BF16, const_cast<void*>(workspace[i]),
+                               stream) != hipSuccess)
+        return SPLR_ERR_HIP;
+  if (!grouped) {
+    for (int32_t i = 0; i < count; ++i) {
+      const splr_status_t s = run_stage2(X[i], M, n_in, values[i], meta[i], n_out, r > 0 ? U[i] : nullptr, r, dtype,
+                                         Y[i], false, const_cast<void*>(workspace[i]), stream);
+      if (s != SPLR_OK) return s;
+    }
+    return SPLR_OK;
+  }
+  const void* u[splr::kMaxGroup];
+  const float* t[splr::kMaxGroup];
+  void* y[splr::kMaxGroup];
+  for (int32_t i = 0; i < count; ++i) {
+    u[i] = r > 0 ? U[i] : nullptr;
+    t[i] = (const float*)workspace[i];
+    y[i] = Y[i];
+  }
+  return from_hip(splr::launch_linear_bf16_group(count, X, M, n_in, values, meta, n_out, u, r, t,
+                                                 splr::lowrank_slices(M, n_in, r, true), y, false, stream));
+}
+
 }  // namespace
 
 splr_status_t splr_linear(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
@@ -219,6 +263,22 @@ splr_status_t splr_linear_stage2_dense(const void* X, int64_t M, int64_t n_in, c
   if (!splr::linear_dense_grids_fit(M, n_out)) return SPLR_ERR_SHAPE;
   return from_hip(splr::launch_linear_bf16_dense(X, M, n_in, values, meta, n_out, U, r, (const float*)workspace,
                                                  splr::lowrank_slices(M, n_in, r, true), Y, stream));
+}
+
+splr_status_t splr_linear_stage2_group(int32_t count, const void* const* X, int64_t M, int64_t n_in,
+                                       const void* const* values, const uint32_t* const* meta, int64_t n_out,
+                                       const void* const* U, int64_t r, splr_dtype_t dtype, float* const* Y,
+                                       const void* const* workspace, size_t ws_bytes, hipStream_t stream) {
+  return run_group(count, X, M, n_in, values, meta, n_out, U, nullptr, r, dtype, Y, workspace, ws_bytes, false,
+                   stream);
+}
+
+splr_status_t splr_linear_group(int32_t count, const void* const* X, int64_t M, int64_t n_in,
+                                const void* const* values, const uint32_t* const* meta, int64_t n_out,
+                                const void* const* U, const void* const* V, int64_t r, splr_dtype_t dtype,
+                                float* const* Y, void* const* workspace, size_t ws_bytes, hipStream_t stream) {
+  return run_group(count, X, M, n_in, values, meta, n_out, U, V, r, dtype, Y, (const void* const*)workspace,
+                   ws_bytes, true, stream);
 }
 
 }  // extern "C"

@@ -49,6 +49,14 @@ hipError_t launch_lowrank(const void* X, const void* V, int64_t M, int64_t n_in,
 hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                               int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
                               bool y_bf16, hipStream_t stream);
+// The same for `layers` (1 .. kMaxGroup) layers of one shape in one launch, their tiles in one grid
+// (each layer's Y bit-identical to its own launch_linear_bf16); M > kDecodeMaxTokens.
+constexpr int kMaxGroup = 4;
+bool linear_group_grid_fits(int64_t M, int64_t n_out, int layers);
+hipError_t launch_linear_bf16_group(int layers, const void* const* X, int64_t M, int64_t n_in,
+                                    const void* const* values, const uint32_t* const* meta, int64_t n_out,
+                                    const void* const* U, int64_t r, const float* const* Tpart, int slices,
+                                    void* const* Y, bool y_bf16, hipStream_t stream);
 // Stage 2 with S decompressed to dense bfloat16 in registers and dense MFMA (the alternative to the
 // structured-sparse instruction, any M; same tiles and pipeline as the prefill kernels' 512-row
 // design: 512 rows and eight waves when that gives every CU a tile, else 256 rows and four).

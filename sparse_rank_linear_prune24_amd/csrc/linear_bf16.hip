@@ -226,6 +226,24 @@ __device__ __forceinline__ void lowrank_block_acc(f32x4_t (&acc)[NI][NJ], const 
   operand_fence(i01, i23);  // the index registers outlive the last MFMA that reads them
 }
 
+// Operands of up to kMaxGroup layers of one shape whose tiles share one grid (passed by value;
+// a single-layer launch is a group of one). A workgroup's layer follows from its tile index, so it
+// is uniform across the workgroup and is selected with scalar compares (no dynamic indexing, which
+// could move the table to private memory).
+struct LayerGroup {
+  const uint16_t* X[kMaxGroup];
+  const u32x4_t* values[kMaxGroup];
+  const uint32_t* meta[kMaxGroup];
+  const uint16_t* U[kMaxGroup];
+  const float* Tpart[kMaxGroup];
+  void* Y[kMaxGroup];
+};
+template <typename T>
+__device__ __forceinline__ T pick_layer(const T (&a)[kMaxGroup], int layer) {
+  static_assert(kMaxGroup == 4, "one compare per layer");
+  return layer == 0 ? a[0] : layer == 1 ? a[1] : layer == 2 ? a[2] : a[3];
+}
+
 // Prefill kernel with the accumulators in the matrix-core accumulator registers: workgroup tile
 // 16*NI*WAVES rows x 128 tokens, each wave owning 16*NI rows (NI S fragments) x all 128 tokens, so
 // NI*8 accumulator fragments = 32*NI accumulator registers per lane. As launched, WAVES = 8 (two
@@ -239,10 +257,8 @@ __device__ __forceinline__ void lowrank_block_acc(f32x4_t (&acc)[NI][NJ], const 
 // four of the ring's slots); further blocks after it.
 template <int NI, int LA, int P, int EPI, int WAVES = 8, bool DENSE = false>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4))) void
-linear_prefill_wide_kernel(
-    const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
-    const uint16_t* __restrict__ U, const float* __restrict__ Tpart, int slices, void* __restrict__ Y, int y_bf16,
-    int M, int K, int n_out, int r, int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
+linear_prefill_wide_kernel(const LayerGroup lg, int layers, int slices, int y_bf16, int M, int K, int n_out, int r,
+                           int tiles_n, int tiles_m, int tiles_per_xcd, int group_m) {
   constexpr int NJ = 8, PX = 2;
   static_assert(WAVES == 4 || WAVES == 8, "one or two waves per SIMD");
   constexpr int BN = 16 * NI * WAVES;  // 512 or 256 rows
@@ -263,10 +279,19 @@ linear_prefill_wide_kernel(
   __shared__ u32x4_t xs[kSlots * kSlot];
   u32x4_t* const tp = xs;  // T's bfloat16 pair (hi, lo) of those blocks, before the ring is used
 
-  // XCD-aware tile order (as in the 256 x 128 kernel)
+  // XCD-aware tile order: each XCD (own L2) runs a contiguous range of the tiles, layer after layer
   const int b = blockIdx.x;
-  const int logical = (b & 7) * tiles_per_xcd + (b >> 3);
-  if (logical >= tiles_n * tiles_m) return;
+  const int logical_all = (b & 7) * tiles_per_xcd + (b >> 3);
+  const int per_layer = tiles_n * tiles_m;
+  if (logical_all >= per_layer * layers) return;
+  const int layer = logical_all / per_layer;
+  const int logical = logical_all - layer * per_layer;
+  const uint16_t* __restrict__ X = pick_layer(lg.X, layer);
+  const u32x4_t* __restrict__ values = pick_layer(lg.values, layer);
+  const uint32_t* __restrict__ meta = pick_layer(lg.meta, layer);
+  const uint16_t* __restrict__ U = pick_layer(lg.U, layer);
+  const float* __restrict__ Tpart = pick_layer(lg.Tpart, layer);
+  void* __restrict__ Y = pick_layer(lg.Y, layer);
   const int per_group = group_m * tiles_n;
   const int g = logical / per_group;
   const int first_m = g * group_m;
@@ -503,17 +528,33 @@ linear_prefill_wide_kernel(
   }
 }
 
-// The 512-row tile when it still gives every CU of the chip at least one tile, else 256 rows.
+// The 512-row tile when the launch's layers together still give every CU of the chip at least one
+// tile, else 256 rows.
 constexpr int64_t kWideMinTiles = 256;
-int64_t prefill_rows(int64_t M, int64_t n_out) {
-  return ceil_div(n_out, 512) * ceil_div(M, 128) >= kWideMinTiles ? 512 : 256;
+int64_t prefill_rows(int64_t M, int64_t n_out, int layers) {
+  return layers * ceil_div(n_out, 512) * ceil_div(M, 128) >= kWideMinTiles ? 512 : 256;
 }
 
-// prefill: one workgroup per tile (512 or 256 rows x 128 tokens), tiles dealt to the 8 XCDs in
-// equal ranges
-dim3 prefill_grid(int64_t M, int64_t n_out) {
-  const int64_t n_tiles = ceil_div(n_out, prefill_rows(M, n_out)) * ceil_div(M, 128);
+// prefill: one workgroup per tile (512 or 256 rows x 128 tokens) of each layer, tiles dealt to the
+// 8 XCDs in equal ranges
+dim3 prefill_grid(int64_t M, int64_t n_out, int layers) {
+  const int64_t n_tiles = layers * ceil_div(n_out, prefill_rows(M, n_out, layers)) * ceil_div(M, 128);
   return dim3((unsigned)(8 * ceil_div(n_tiles, 8)));
+}
+
+LayerGroup make_group(int layers, const void* const* X, const void* const* values, const uint32_t* const* meta,
+                      const void* const* U, const float* const* Tpart, void* const* Y) {
+  LayerGroup g{};
+  for (int i = 0; i < kMaxGroup; ++i) {
+    const int l = i < layers ? i : layers - 1;  // unused entries repeat the last layer
+    g.X[i] = (const uint16_t*)X[l];
+    g.values[i] = (const u32x4_t*)values[l];
+    g.meta[i] = meta[l];
+    g.U[i] = (const uint16_t*)U[l];
+    g.Tpart[i] = Tpart[l];
+    g.Y[i] = Y[l];
+  }
+  return g;
 }
 
 }  // namespace
@@ -522,19 +563,25 @@ bool linear_grids_fit(int64_t M, int64_t n_in, int64_t n_out, int64_t r, bool bf
   if (!lowrank_grids_fit(M, n_in, r, bf16)) return false;
   if (!bf16) return grid_fits(linear_f32_grid(M, n_out), 256);
   if (M <= kDecodeMaxTokens) return decode_grids_fit(M, n_out);
-  return grid_fits(prefill_grid(M, n_out), 256);
+  return grid_fits(prefill_grid(M, n_out, 1), 256);
 }
 
-hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
-                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
-                              bool y_bf16, hipStream_t stream) {
+bool linear_group_grid_fits(int64_t M, int64_t n_out, int layers) {
+  return grid_fits(prefill_grid(M, n_out, layers), 256);
+}
+
+hipError_t launch_linear_bf16_group(int layers, const void* const* X, int64_t M, int64_t n_in,
+                                    const void* const* values, const uint32_t* const* meta, int64_t n_out,
+                                    const void* const* U, int64_t r, const float* const* Tpart, int slices,
+                                    void* const* Y, bool y_bf16, hipStream_t stream) {
   const int yb = y_bf16 ? 1 : 0;
   constexpr int BM = 128;
-  const int BN = (int)prefill_rows(M, n_out);
+  const int BN = (int)prefill_rows(M, n_out, layers);
   const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
-  const dim3 grid = prefill_grid(M, n_out);
+  const dim3 grid = prefill_grid(M, n_out, layers);
   const int per_xcd = (int)grid.x / 8;
   const int group_m = 4;
+  const LayerGroup lg = make_group(layers, X, values, meta, U, Tpart, Y);
   // A Y larger than three quarters of the 256 MB Infinity Cache is stored non-temporally (kept in the
   // cache it evicts the S and X rows that later tile groups re-read), and as whole token rows through
   // LDS: non-temporal 16-byte fragment pieces would leave partial cache lines (a 470 MB Y counted as
@@ -546,8 +593,7 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   // the 256-row one (measured against one wave per SIMD with twice the rows: 3-6 % faster on the
   // 512-row tiles, 8 % on the 256-row tiles)
   const auto launch = [&](auto kernel) {
-    kernel<<<grid, dim3(512), 0, stream>>>((const uint16_t*)X, (const u32x4_t*)values, meta, (const uint16_t*)U,
-                                           Tpart, slices, Y, yb, (int)M, (int)n_in, (int)n_out, (int)r, tiles_n,
+    kernel<<<grid, dim3(512), 0, stream>>>(lg, layers, slices, yb, (int)M, (int)n_in, (int)n_out, (int)r, tiles_n,
                                            tiles_m, per_xcd, group_m);
   };
   if (BN == 512) {
@@ -561,22 +607,28 @@ hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void
   return hipGetLastError();
 }
 
-bool linear_dense_grids_fit(int64_t M, int64_t n_out) { return grid_fits(prefill_grid(M, n_out), 256); }
+hipError_t launch_linear_bf16(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
+                              int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
+                              bool y_bf16, hipStream_t stream) {
+  return launch_linear_bf16_group(1, &X, M, n_in, &values, &meta, n_out, &U, r, &Tpart, slices, &Y, y_bf16, stream);
+}
+
+bool linear_dense_grids_fit(int64_t M, int64_t n_out) { return grid_fits(prefill_grid(M, n_out, 1), 256); }
 
 hipError_t launch_linear_bf16_dense(const void* X, int64_t M, int64_t n_in, const void* values, const uint32_t* meta,
                                     int64_t n_out, const void* U, int64_t r, const float* Tpart, int slices, void* Y,
                                     hipStream_t stream) {
   constexpr int BM = 128;
-  const int BN = (int)prefill_rows(M, n_out);
+  const int BN = (int)prefill_rows(M, n_out, 1);
   const int tiles_n = (int)ceil_div(n_out, BN), tiles_m = (int)ceil_div(M, BM);
-  const dim3 grid = prefill_grid(M, n_out);
+  const dim3 grid = prefill_grid(M, n_out, 1);
   const int per_xcd = (int)grid.x / 8;
   const int group_m = 4;
   const bool y_nt = (double)M * n_out * 4 > kNonTemporalYBytes;
+  const LayerGroup lg = make_group(1, &X, &values, &meta, &U, &Tpart, &Y);
   const auto args = [&](auto kernel, int waves) {
-    kernel<<<grid, dim3(64 * waves), 0, stream>>>((const uint16_t*)X, (const u32x4_t*)values, meta,
-                                                  (const uint16_t*)U, Tpart, slices, Y, 0, (int)M, (int)n_in,
-                                                  (int)n_out, (int)r, tiles_n, tiles_m, per_xcd, group_m);
+    kernel<<<grid, dim3(64 * waves), 0, stream>>>(lg, 1, slices, 0, (int)M, (int)n_in, (int)n_out, (int)r, tiles_n,
+                                                  tiles_m, per_xcd, group_m);
   };
   if (BN == 512) {
     if (y_nt)

@@ -189,6 +189,36 @@ def test_stage2_dense_validation():
     assert d(A, 16, 64, A, A, 32, A, 16, 0, A, A, wsf, None) == DTYPE
 
 
+def test_group_validation():
+    """splr_linear_group / splr_linear_stage2_group: the count, the pointer arrays, and every layer's
+    arguments as splr_linear checks them, all before any HIP call."""
+    lib = binding.lib()
+    g, g2 = lib.splr_linear_group, lib.splr_linear_stage2_group
+    arr = lambda *p: (ctypes.c_void_p * len(p))(*p)
+    wsb = lib.splr_linear_workspace_bytes(128, 512, 64, 16, 1)
+    two = arr(A, A)
+    # count
+    for c in (0, -1, binding.GROUP_MAX + 1):
+        assert g(c, two, 128, 64, two, two, 512, two, two, 16, 1, two, two, wsb, None) == SHAPE
+        assert g2(c, two, 128, 64, two, two, 512, two, 16, 1, two, two, wsb, None) == SHAPE
+    # missing arrays
+    assert g(2, None, 128, 64, two, two, 512, two, two, 16, 1, two, two, wsb, None) == NULL
+    assert g(2, two, 128, 64, two, two, 512, two, None, 16, 1, two, two, wsb, None) == NULL
+    assert g(2, two, 128, 64, two, two, 512, two, two, 16, 1, two, None, wsb, None) == NULL
+    assert g2(2, two, 128, 64, two, None, 512, two, 16, 1, two, two, wsb, None) == NULL
+    assert g2(2, two, 128, 64, two, two, 512, None, 16, 1, two, two, wsb, None) == NULL
+    # a missing or misaligned entry of the second layer
+    assert g2(2, two, 128, 64, two, arr(A, None), 512, two, 16, 1, two, two, wsb, None) == NULL
+    assert g2(2, two, 128, 64, two, two, 512, two, 16, 1, arr(A, MIS), two, wsb, None) == ALIGN
+    assert g(2, two, 128, 64, two, two, 512, two, arr(A, MIS), 16, 1, two, two, wsb, None) == ALIGN
+    # shapes, type and workspace, shared by the layers
+    assert g2(2, two, 128, 40, two, two, 512, two, 16, 1, two, two, wsb, None) == SHAPE
+    assert g2(2, two, 128, 64, two, two, 512, two, 24, 1, two, two, wsb, None) == SHAPE
+    assert g2(2, two, 128, 64, two, two, 512, two, 16, 3, two, two, wsb, None) == DTYPE
+    assert g2(2, two, 128, 64, two, two, 512, two, 16, 1, two, two, wsb - 1, None) == WORKSPACE
+    assert g2(2, two, 128, 64, two, two, 512, two, 16, 1, two, arr(A, None), wsb, None) == WORKSPACE
+
+
 def test_reconstruct_validation():
     f = binding.lib().splr_dense_reconstruct
     assert f(None, A, A, A, 4, 64, 16, 1, A, None) == NULL
