@@ -109,27 +109,35 @@ def wide_tile(L, count=1):
     return count * -(-L.n_out // 512) * -(-L.M // 128) >= 256
 
 
+def tile_rounds(L, count=1):
+    """Rounds of 256 CUs the stage-2 tiles of `count` layers shaped like L take in one launch."""
+    rows = 512 if wide_tile(L, count) else 256
+    return -(-count * -(-L.n_out // rows) * -(-L.M // 128) // 256)
+
+
 def stage2_units(layers, decode):
     """The step's stage-2 launches: adjacent layers of one shape go into one grouped launch
-    (splr_linear_stage2_group) when alone they would take 256-row tiles and together 512-row ones
-    (k_proj and v_proj of the block); every other layer is a launch of its own."""
-    units = []
+    (splr_linear_stage2_group, up to 4 layers) when that needs fewer rounds of tiles than launching
+    them one by one -- k_proj and v_proj of the block (alone 256-row tiles, together 512-row ones),
+    or layers whose tile count leaves a part-filled last round (gate and up at 4096 tokens: 3.5
+    rounds each, 7 together); every other layer is a launch of its own."""
+    runs = []
     for li, L in enumerate(layers):
-        prev = units[-1] if units else None
-        if (not decode and prev is not None and len(prev) < 4 and not wide_tile(L)
-                and (layers[prev[0]].n_in, layers[prev[0]].n_out, layers[prev[0]].r) == (L.n_in, L.n_out, L.r)
-                and all(not wide_tile(layers[j]) for j in prev)):
+        prev = runs[-1] if runs else None
+        if (not decode and prev is not None and len(prev) < 4
+                and (layers[prev[0]].M, layers[prev[0]].n_in, layers[prev[0]].n_out, layers[prev[0]].r)
+                == (L.M, L.n_in, L.n_out, L.r)):
             prev.append(li)
         else:
-            units.append([li])
-    # keep a group only where it changes the tile
-    out = []
-    for u in units:
-        if len(u) > 1 and not wide_tile(layers[u[0]], len(u)):
-            out.extend([j] for j in u)
+            runs.append([li])
+    units = []
+    for u in runs:
+        L = layers[u[0]]
+        if len(u) > 1 and tile_rounds(L, len(u)) < len(u) * tile_rounds(L):
+            units.append(u)
         else:
-            out.append(u)
-    return out
+            units.extend([j] for j in u)
+    return units
 
 
 def prefill_kernels(layers, units):
