@@ -12,6 +12,23 @@ namespace {
 
 // ----------------------------------------------------------------------------------- decode
 
+// U's rows tr0 + lane%16, ranks 16 (lane / 16) .. +15 of the first 64-rank block (zeros past n_out
+// or r), as loaded; pair01 / pair23 give the (0,1) and (2,3) halves of every group of four ranks,
+// the A operands of the two structured-sparse MFMAs that make one dense product
+struct URow {
+  u32x4_t d0, d1;
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ U, int n_out, int r, int tr0, int lane) {
+    const int n = tr0 + (lane & 15), ju = 16 * (lane >> 4);
+    const bool ok = n < n_out && ju < r;
+    const uint16_t* p = U + (size_t)(ok ? n : 0) * r + (ok ? ju : 0);
+    const u32x4_t zero = {0, 0, 0, 0};
+    d0 = ok ? *(const u32x4_t*)p : zero;
+    d1 = ok ? *(const u32x4_t*)(p + 8) : zero;
+  }
+  __device__ __forceinline__ bf16x8_t pair01() const { return as_bf16x8(u32x4_t{d0[0], d0[2], d1[0], d1[2]}); }
+  __device__ __forceinline__ bf16x8_t pair23() const { return as_bf16x8(u32x4_t{d0[1], d0[3], d1[1], d1[3]}); }
+};
+
 template <int MB, int P, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
     const uint16_t* __restrict__ X, const u32x4_t* __restrict__ values, const uint32_t* __restrict__ meta,
@@ -73,6 +90,10 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
     tb.init(Tpart, slices, M, r, m0, 0, threadIdx.x);
     tb.issue(0);
   }
+  // U's fragments for wave 0's rank-r term, loaded now: after the loop their memory latency would
+  // be exposed at the end of the call
+  URow uf;
+  if (t_pre && r > 0 && wave == 0) uf.load(U, n_out, r, tr * 16, lane);
   static_for<P>([&](auto uu) {  // issued in slot order (fenced), as the loop refills them
     constexpr int u = decltype(uu)::value;
     load(u, sa[u], sw[u], xr[u]);
@@ -118,10 +139,19 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
   // rank-r term, 64 ranks at a time: wave 0 adds U T^T, with T's pair from before the loop or, for
   // larger r, built block by block by all waves
   if (t_pre) {
-    if (wave == 0) {
+    static_assert(kPreRankBlocks == 1, "one block of U fragments loaded ahead");
+    if (wave == 0 && r > 0) {
+      const bf16x8_t u01 = uf.pair01(), u23 = uf.pair23();
 #pragma unroll
-      for (int b = 0; b < kPreRankBlocks; ++b)
-        if (64 * b < r) lowrank_block<1, MB>(acc, U, tpair[2 * b], tpair[2 * b + 1], n_out, r, 64 * b, tr * 16, lane);
+      for (int j = 0; j < MB; ++j) {
+        const int row = (16 * j + sub) * kXPitchU4;
+        const bf16x16_t th = cat16(as_bf16x8(tpair[0][row + quad]), as_bf16x8(tpair[0][row + 4 + quad]));
+        const bf16x16_t tl = cat16(as_bf16x8(tpair[1][row + quad]), as_bf16x8(tpair[1][row + 4 + quad]));
+        acc[0][j] = smfmac16x16x64(u01, th, acc[0][j], 0x4444);
+        acc[0][j] = smfmac16x16x64(u23, th, acc[0][j], 0xEEEE);
+        acc[0][j] = smfmac16x16x64(u01, tl, acc[0][j], 0x4444);
+        acc[0][j] = smfmac16x16x64(u23, tl, acc[0][j], 0xEEEE);
+      }
     }
   } else {
     for (int j0 = 0; j0 < r; j0 += 64) {
