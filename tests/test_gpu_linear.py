@@ -58,6 +58,8 @@ SHAPES = [
     # first stage with 128 ranks per workgroup (r > 64) at its three token blocks (16 / 32 / 64 by
     # M), partial rank blocks, the largest rank on both paths
     (1100, 2080, 300, 128), (4100, 320, 72, 144), (96, 512, 80, 1024), (16, 256, 64, 1024),
+    # decode-sized inputs at longer K: one and a few tokens, ragged rows, no low-rank part
+    (1, 2048, 48, 16), (5, 3584, 100, 64), (16, 2560, 33, 0), (11, 4096, 130, 48),
 ]
 
 
@@ -164,11 +166,12 @@ def test_identity_input(dtype):
     assert rel_err(Y, W.T) <= 1e-5
 
 
-@pytest.mark.parametrize("M", [16, 48, 256])
-def test_integer_exact_bitwise(M):
+@pytest.mark.parametrize("M,n_in", [(16, 512), (48, 512), (256, 512), (16, 2048), (3, 4096)])
+def test_integer_exact_bitwise(M, n_in):
     """Small integers make every product and partial sum exact in float32 (all < 2^24): the GPU
-    result must equal the oracle exactly, for both kernels (decode M <= 64, prefill above)."""
-    dtype, n_in, n_out, r = "bf16", 512, 160, 16
+    result must equal the oracle exactly, for both kernels (decode M <= 64, prefill above) and
+    K up to 4096."""
+    dtype, n_out, r = "bf16", 160, 16
     X = inputs.small_integers((M, n_in), -4, 4, dtype, seed=M, tensor_id=0)
     U = inputs.small_integers((n_out, r), -2, 2, dtype, seed=M, tensor_id=2)
     V = inputs.small_integers((r, n_in), -2, 2, dtype, seed=M, tensor_id=3)
