@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void linear_decode_kernel(
   // T's pair: its loads go out first, the ring's next, and the pair is written to LDS while the
   // ring's loads are in flight (published by the barrier after the loop)
   const bool t_pre = r <= 64 * kPreRankBlocks;
-  TPairBuilder<16 * MB, 64 * WAVES> tb;
+  TPairBuilder<16 * MB, 64 * WAVES, MB == 1 ? 8 : 0> tb;  // 16 tokens: at most 8 K slices, all in one round
   if (t_pre && r > 0) {
     tb.init(Tpart, slices, M, r, m0, 0, threadIdx.x);
     tb.issue(0);
