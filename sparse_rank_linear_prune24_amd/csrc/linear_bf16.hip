@@ -582,12 +582,15 @@ hipError_t launch_linear_bf16_group(int layers, const void* const* X, int64_t M,
   const int per_xcd = (int)grid.x / 8;
   const int group_m = 4;
   const LayerGroup lg = make_group(layers, X, values, meta, U, Tpart, Y);
-  // A Y larger than three quarters of the 256 MB Infinity Cache is stored non-temporally (kept in the
-  // cache it evicts the S and X rows that later tile groups re-read), and as whole token rows through
-  // LDS: non-temporal 16-byte fragment pieces would leave partial cache lines (a 470 MB Y counted as
-  // 727 MB of writes). Measured against fragment stores: -5.5 % at 4096/8192 tokens x 14336 outputs.
-  // Smaller Y: row stores for the 256-row tiles, whose one or two rounds leave the final stores
-  // exposed (-1 to -3 %); fragment stores for the 512-row tiles (the row transpose measured +1-2 %).
+  // A Y above 96 MiB is stored non-temporally (kept in the 256 MB Infinity Cache it evicts the S and
+  // X rows that later tile groups re-read, and leaves dirty lines for the next kernels to write
+  // back), and as whole token rows through LDS: non-temporal 16-byte fragment pieces would leave
+  // partial cache lines (a 470 MB Y counted as 727 MB of writes). Measured against fragment stores:
+  // -5.5 % at 4096/8192 tokens x 14336 outputs; for the 128 MiB Y of an 8192-token 4096-output layer
+  // the layer alone is 1-5 % slower but the block's step 0.8 % faster (the following pack and first
+  // stage gain). Smaller Y: row stores for the 256-row tiles, whose one or two rounds leave the final
+  // stores exposed (-1 to -3 %); fragment stores for the 512-row tiles (the row transpose measured
+  // +1-2 %).
   const bool y_nt = (double)M * n_out * (y_bf16 ? 2 : 4) > kNonTemporalYBytes;
   // eight waves, two per SIMD, each owning 16 NI rows x 128 tokens: NI = 4 for the 512-row tile, 2 for
   // the 256-row one (measured against one wave per SIMD with twice the rows: 3-6 % faster on the

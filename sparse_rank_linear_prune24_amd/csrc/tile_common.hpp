@@ -223,8 +223,8 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[NI][NJ], void* _
   }
 }
 
-// Y bytes above which the prefill kernels store Y non-temporally
-constexpr double kNonTemporalYBytes = 192.0 * (1 << 20);
+// Y bytes above which the prefill kernels store Y non-temporally (whole token rows through LDS)
+constexpr double kNonTemporalYBytes = 96.0 * (1 << 20);
 
 }  // namespace
 }  // namespace splr

@@ -118,7 +118,8 @@ def test_named_sampled_rows(cfg):
 # main loop (16, 80, 128) and further blocks after it (144: a partial one; 192), both Y epilogues
 WIDE = [(4100, 2080, 4100, 80), (8192, 96, 4104, 16), (4096, 448, 8192, 0), (4224, 4096, 4096, 128),
         (4096, 1056, 4100, 192), (4160, 544, 4096, 144),
-        # Y above 192 MiB: non-temporal token-row stores through LDS; a 4-row last tile, and rows
+        # Y above 96 MiB (also the second and third shape): non-temporal token-row stores through LDS;
+        # a 4-row last tile, and rows
         # not a multiple of 4 (every store per element)
         (8192, 96, 6148, 16), (8200, 96, 6150, 16)]
 

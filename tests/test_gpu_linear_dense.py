@@ -58,7 +58,7 @@ def test_dense_shapes(M, n_in, n_out, r):
     check_dense(L, f"{M}x{n_in}->{n_out} r{r}")
 
 
-# the last: Y above 192 MiB (non-temporal token-row stores), ragged tokens and outputs
+# the second and the last: Y above 96 MiB (non-temporal token-row stores); the last with ragged tokens and outputs
 WIDE = [(4100, 2080, 4100, 80), (4096, 448, 8192, 0), (4160, 544, 4096, 144), (8200, 96, 6150, 16)]
 
 
