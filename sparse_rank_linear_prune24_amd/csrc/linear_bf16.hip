@@ -191,12 +191,16 @@ struct UFragments {
 // acc[i][j] (rows nrow0 + 16 i + ..., tokens 16 j + ...) += U[n][j0 .. j0+63] . T[token][j0 .. j0+63]
 // with the accumulators in the accumulator registers (smfmac_acc): the rank-r term of
 // lowrank_block, for the kernels that keep their accumulators there. U comes as loaded fragments,
-// T's bfloat16 pair from the LDS planes hi / lo one token fragment at a time. The MFMAs of a token
-// fragment run over the row fragments innermost, so consecutive MFMAs write different accumulators.
+// T's bfloat16 pair from the LDS planes hi / lo one token fragment at a time, the next fragment's
+// read in flight during the current one's MFMAs. The MFMAs of a token fragment run over the row
+// fragments innermost, so consecutive MFMAs write different accumulators.
 template <int NI, int NJ>
 __device__ __forceinline__ void lowrank_block_acc(f32x4_t (&acc)[NI][NJ], const UFragments<NI>& uf,
-                                                  const u32x4_t* hi, const u32x4_t* lo, int lane) {
+                                                  const u32x4_t* hi, const u32x4_t* lo) {
   static_assert(NI % 2 == 0, "U fragments fenced two rows at a time");
+  // the lane index recomputed here (two instructions) rather than kept from the kernel's start: a
+  // kept value may be spilled, and its reload would wait for every load in flight
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int sub = lane & 15, quad = lane >> 4;
   bf16x8_t u01[NI], u23[NI];
 #pragma unroll
@@ -208,20 +212,26 @@ __device__ __forceinline__ void lowrank_block_acc(f32x4_t (&acc)[NI][NJ], const 
   for (int i = 0; i < NI; i += 2) operand_fence(u01[i], u23[i], u01[i + 1], u23[i + 1]);
   uint32_t i01 = 0x4444u, i23 = 0xEEEEu;
   operand_fence(i01, i23);
+  // T's pair of token fragment j + 1 is read from LDS while the MFMAs of fragment j run
+  bf16x16_t th[2], tl[2];
+  auto read_t = [&](int j, int b) {
+    const int row = (16 * j + sub) * kXPitchU4;
+    th[b] = cat16(as_bf16x8(hi[row + quad]), as_bf16x8(hi[row + 4 + quad]));
+    tl[b] = cat16(as_bf16x8(lo[row + quad]), as_bf16x8(lo[row + 4 + quad]));
+  };
+  read_t(0, 0);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int row = (16 * j + sub) * kXPitchU4;
-    bf16x16_t th = cat16(as_bf16x8(hi[row + quad]), as_bf16x8(hi[row + 4 + quad]));
-    bf16x16_t tl = cat16(as_bf16x8(lo[row + quad]), as_bf16x8(lo[row + 4 + quad]));
-    operand_fence(th, tl);
+    if (j + 1 < NJ) read_t(j + 1, (j + 1) & 1);
+    operand_fence(th[j & 1], tl[j & 1]);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u01[i], th, i01);
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u01[i], th[j & 1], i01);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u23[i], th, i23);
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u23[i], th[j & 1], i23);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u01[i], tl, i01);
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u01[i], tl[j & 1], i01);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u23[i], tl, i23);
+    for (int i = 0; i < NI; ++i) smfmac_acc<0>(acc[i][j], u23[i], tl[j & 1], i23);
   }
   operand_fence(i01, i23);  // the index registers outlive the last MFMA that reads them
 }
@@ -470,8 +480,8 @@ linear_prefill_wide_kernel(const LayerGroup lg, int layers, int slices, int y_bf
     if (two) tb1.finish(tp + 2 * kSlot, tp + 3 * kSlot);
     lds_barrier();
     if (r_pre > 64) uf1.load(U, n_out, r, 64, nrow0, lane);
-    lowrank_block_acc<NI, NJ>(acc, uf0, tp, tp + kSlot, lane);
-    if (r_pre > 64) lowrank_block_acc<NI, NJ>(acc, uf1, tp + 2 * kSlot, tp + 3 * kSlot, lane);
+    lowrank_block_acc<NI, NJ>(acc, uf0, tp, tp + kSlot);
+    if (r_pre > 64) lowrank_block_acc<NI, NJ>(acc, uf1, tp + 2 * kSlot, tp + 3 * kSlot);
     lds_barrier();  // every wave's reads of the T planes are done before the ring overwrites them
   }
 
@@ -514,7 +524,7 @@ linear_prefill_wide_kernel(const LayerGroup lg, int layers, int slices, int y_bf
     uf.load(U, n_out, r, j0, nrow0, lane);
     build_t_pair<BM, 64 * WAVES>(Tpart, slices, M, r, m0, j0, xs, xs + kSlot, threadIdx.x);
     lds_barrier();
-    lowrank_block_acc<NI, NJ>(acc, uf, xs, xs + kSlot, lane);
+    lowrank_block_acc<NI, NJ>(acc, uf, xs, xs + kSlot);
     lds_barrier();
   }
   accumulator_fence(acc);  // the last smfmac_acc results, before the stores
