@@ -32,6 +32,7 @@ torch, a plain device copy moving as many bytes as its weight side).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -621,26 +622,43 @@ def cpu_baseline(cfg, layers, dtype, flop_step, wbytes_step, decode, rows_arg):
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     oracle.build(force=False)
-    t_pack = 0.0
-    t_lin = 0.0
-    frac_rows = []
-    for L in layers:
-        t0 = time.perf_counter()
-        v, m = oracle.prune24_pack(L.R, dtype)
-        t_pack += time.perf_counter() - t0
-        rows = rows_arg or max(1, min(L.M, int(4e9 / (L.n_out * L.n_in / 2) // 1)))
-        rows = min(rows, L.M)
-        sel = np.linspace(0, L.M - 1, rows).astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.linear(L.X, v, m, L.n_out, L.U, L.V, dtype, rows=sel)
-        dt = time.perf_counter() - t0
-        t_lin += dt * (L.M / rows)
-        frac_rows.append(f"{L.name}: {rows}/{L.M} rows")
+
+    def run(row_div):
+        """Pack of every layer, layer product on evenly spaced rows; seconds scaled to one step."""
+        t_pack = t_lin = 0.0
+        frac_rows = []
+        for L in layers:
+            t0 = time.perf_counter()
+            v, m = oracle.prune24_pack(L.R, dtype)
+            t_pack += time.perf_counter() - t0
+            rows = rows_arg or max(1, min(L.M, int(4e9 / (L.n_out * L.n_in / 2) // 1)))
+            rows = max(1, min(rows, L.M) // row_div)
+            sel = np.linspace(0, L.M - 1, rows).astype(np.int64)
+            t0 = time.perf_counter()
+            oracle.linear(L.X, v, m, L.n_out, L.U, L.V, dtype, rows=sel)
+            t_lin += (time.perf_counter() - t0) * (L.M / rows)
+            frac_rows.append(f"{L.name}: {rows}/{L.M} rows")
+        return t_pack, t_lin, frac_rows
+
+    def rate(t_step):
+        return (wbytes_step / t_step / 1e9, "GB/s") if decode else (flop_step / t_step / 1e12, "TFLOP/s")
+
+    t_pack, t_lin, frac_rows = run(1)
     t_step = t_pack + t_lin
-    if decode:
-        value, unit = wbytes_step / t_step / 1e9, "GB/s"
-    else:
-        value, unit = flop_step / t_step / 1e12, "TFLOP/s"
+    value, unit = rate(t_step)
+    # the small workloads also on one thread (the same OpenMP runtime as the oracle's), with a
+    # sixteenth of the rows
+    one_thread = None
+    if cfg.name in ("C1", "C2", "C3"):
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        try:
+            p1, l1, rows1 = run(16)
+        finally:
+            gomp.omp_set_num_threads(int(os.environ["OMP_NUM_THREADS"]))
+        v1, _ = rate(p1 + l1)
+        one_thread = dict(value=round(v1, 6), unit=unit, cores=1, step_s_equiv=round(p1 + l1, 3),
+                          sample=f"full pack of every layer; layer product on {'; '.join(rows1)}")
     cpu = platform.processor() or ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -653,7 +671,8 @@ def cpu_baseline(cfg, layers, dtype, flop_step, wbytes_step, decode, rows_arg):
     return dict(value=round(value, 6), unit=unit, cores=int(os.environ["OMP_NUM_THREADS"]), kind="oracle",
                 sample=f"full pack of every layer; layer product on evenly spaced token rows ({'; '.join(frac_rows)}), "
                        f"time scaled to all rows; float64, OpenMP",
-                step_s_equiv=round(t_step, 3), pack_s=round(t_pack, 3), cpu=cpu)
+                step_s_equiv=round(t_step, 3), pack_s=round(t_pack, 3), cpu=cpu,
+                **({"one_thread": one_thread} if one_thread else {}))
 
 
 if __name__ == "__main__":
